@@ -1,0 +1,199 @@
+/*
+ * isattn -- sparse attention backward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libisattn.so.  Every pointer argument that names tensor data is a
+ * device pointer (HIP global memory) unless stated otherwise; every entry
+ * point only enqueues work on the given HIP stream and never synchronises the
+ * host.  The library allocates no device memory and holds no state: the
+ * caller owns inputs, outputs, CSR arrays and workspaces.  All argument
+ * checks run before the first launch -- on any error nothing is enqueued and a
+ * status code is returned.  No C++ exception crosses this interface.
+ *
+ * Sources (web pages, by title and section):
+ *  [P1] MagiAttention PR #334 "BWD LoopK with warp-specialized pipeline +
+ *       IndexSparse/BlockSparse support": Summary, Core changes 1-3.
+ *  [P3] xtuner PR #2096 "Add optional TileLang Top-K selector": Main Changes 1.
+ *  [P4] MagiAttention PR #331 "support 192/128 and 256/256 ffa_fa4": Summary,
+ *       CSR Tile Mapping.
+ */
+#ifndef ISATTN_H
+#define ISATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum isattn_status {
+    ISATTN_OK = 0,
+    ISATTN_ERR_NULL = 1,          /* a required pointer is NULL                          */
+    ISATTN_ERR_SHAPE = 2,         /* a size is negative or sizes are inconsistent       */
+    ISATTN_ERR_STRIDE_ALIGN = 3,  /* a tensor view's stride or alignment is unsupported */
+    ISATTN_ERR_UNSUPPORTED = 4,   /* outside the supported set (head dims, block, algo) */
+    ISATTN_ERR_MASK = 5,          /* malformed mask descriptor                          */
+    ISATTN_ERR_WORKSPACE = 6,     /* workspace missing, too small or misaligned         */
+    ISATTN_ERR_CAPACITY = 7,      /* CSR column capacity below the worst case           */
+    ISATTN_ERR_HIP = 8            /* a HIP runtime call or kernel launch failed         */
+} isattn_status_t;
+
+/* Problem sizes.  Token-major layout (row = token), as the (total_q, NHK, topk)
+ * index tensor of [P1] Core changes 2 implies.  heads_q % heads_k == 0; query
+ * head h reads KV head h / (heads_q / heads_k). */
+typedef struct isattn_shape {
+    int32_t batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v;
+} isattn_shape_t;
+
+/* A 4-D bf16 device tensor [batch, seq, heads, dim] with the last dimension
+ * contiguous.  Strides are in elements.  ptr and every stride * 2 bytes must
+ * be multiples of 16 bytes. */
+typedef struct isattn_tensor {
+    void*   ptr;
+    int64_t stride_b, stride_s, stride_h;
+} isattn_tensor_t;
+
+enum { ISATTN_MASK_DENSE = 0, ISATTN_MASK_BLOCK_CSR = 1 };
+
+/* Mask descriptor.  kind == ISATTN_MASK_DENSE: every pair is kept (before the
+ * causal term).  kind == ISATTN_MASK_BLOCK_CSR: a pair (i, j) of query head h
+ * is kept iff key block j / block_k is listed in the Q->K CSR row of
+ * (batch b, mask head h * heads / heads_q, query block i / block_q) -- the
+ * per-M-block N-block lists of [P1] Core changes 2; k2q_* holds the same
+ * pairs transposed (per key block, its query blocks: the K2Q metadata of [P4]
+ * CSR Tile Mapping).  Rows are flattened as ((b * heads + hm) * n_blocks +
+ * block); columns ascend within a row; row_ptr[0] == 0.  LoopK reads only
+ * q2k_*, LoopQ only k2q_*; the other pair may be NULL.  Inside a kept block
+ * every pair is attended.  block_q = block_k = 128; heads is 1, heads_k or
+ * heads_q. */
+typedef struct isattn_mask {
+    int32_t kind;
+    int32_t block_q, block_k;
+    int32_t heads;
+    const int32_t* q2k_row_ptr;   /* [batch*heads*n_qb + 1] device */
+    const int32_t* q2k_col;       /* [nnz] device                   */
+    const int32_t* k2q_row_ptr;   /* [batch*heads*n_kb + 1] device */
+    const int32_t* k2q_col;       /* [nnz] device                   */
+} isattn_mask_t;
+
+/* Loop orders of [P1] Summary.  LOOPK: outer loop over 128-row query tiles,
+ * inner loop streams the kept K/V tiles; dQ stays on chip and is stored once,
+ * dK/dV are reduced as fp32 atomics into the workspace and converted by a
+ * postprocess.  LOOPQ: outer loop over 128-key tiles, inner loop over the
+ * query tiles of every head of the GQA group; dK/dV stay on chip and are
+ * stored directly, dQ is reduced as fp32 atomics and converted afterwards. */
+enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1 };
+
+/* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
+ * (fp32 delta [B,Hq,Sq] plus fp32 accumulators: dK,dV [B,Sk,Hk,D] for LOOPK,
+ * dQ [B,Sq,Hq,Dqk] for LOOPQ; each part 256-byte aligned).  Returns 0 for a
+ * NULL shape or unknown algo. */
+size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
+
+/* Attention backward ([P1] Summary and Core changes 1-3): recompute
+ * P = exp(softmax_scale * Q K^T - LSE) on the kept pairs, then
+ *   D  = rowsum(dO * O),  dS = P * (dO V^T - D),
+ *   dV = P^T dO,  dK = softmax_scale * dS^T Q,  dQ = softmax_scale * dS K
+ * (dK/dV summed over the query heads of a GQA group).
+ *
+ * q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv], o and dO [B,Sq,Hq,Dv]:
+ *   bf16 inputs.  lse: fp32 [B,Hq,Sq] contiguous, natural-log log-sum-exp of
+ *   the scaled scores over the kept keys (+inf for a row with none).
+ * mask_desc: see isattn_mask_t; NULL means dense.
+ * causal: nonzero adds the bottom-right causal term j <= i + Sk - Sq.
+ * dq, dk, dv: bf16 outputs with q/k/v's shapes; overwritten, not accumulated.
+ * algo: ISATTN_ALGO_LOOPK or ISATTN_ALGO_LOOPQ.
+ * workspace: device buffer of at least isattn_attn_bwd_workspace_bytes bytes,
+ *   256-byte aligned; its contents on entry do not matter.
+ * stream: hipStream_t (NULL = default stream).
+ * Supported: (dim_qk, dim_v) in {(64,64), (128,128), (192,128)}. */
+isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape,
+                                const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                const isattn_tensor_t* v, const isattn_tensor_t* o,
+                                const isattn_tensor_t* dO, const float* lse,
+                                const isattn_mask_t* mask_desc, int32_t causal,
+                                float softmax_scale,
+                                const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                                const isattn_tensor_t* dv,
+                                int32_t algo, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Bytes of device workspace isattn_index_to_block_sparse needs (presence
+ * matrix plus row/column counts, 256-byte aligned parts). */
+size_t isattn_index_to_block_sparse_workspace_bytes(int32_t batch, int32_t seqlen_q,
+                                                    int32_t seqlen_k, int32_t nhk,
+                                                    int32_t block_q, int32_t block_k);
+
+/* Token top-k indices -> block sparsity ([P1] Core changes 2; [P4] CSR Tile
+ * Mapping; index format of [P3] Main Changes 1).
+ * indices: int32 device [batch*seqlen_q, nhk, topk], contiguous; row r is
+ *   query r % seqlen_q of sequence r / seqlen_q; a value is a key position in
+ *   that sequence.  -1 and any value outside [0, seqlen_k) select nothing;
+ *   duplicates select once; entry order is irrelevant.
+ * Builds presence[b, hk, qb, kb] = 1 iff a row of query block qb selects a key
+ * of key block kb, then writes both CSR forms (rows flattened over (b, hk),
+ * columns ascending, row_ptr[0] = 0):
+ *   q2k_row_ptr [batch*nhk*n_qb + 1], q2k_col [nnz];
+ *   k2q_row_ptr [batch*nhk*n_kb + 1], k2q_col [nnz].
+ * nnz is left on the device as row_ptr[last] (no host synchronisation).
+ * col_capacity (elements of each col array) must be at least
+ * batch*nhk*n_qb*n_kb.  block_q, block_k >= 1 (128 for isattn_attn_bwd). */
+isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t batch,
+                                             int32_t seqlen_q, int32_t seqlen_k, int32_t nhk,
+                                             int32_t topk, int32_t block_q, int32_t block_k,
+                                             int32_t* q2k_row_ptr, int32_t* q2k_col,
+                                             int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                             int64_t col_capacity, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace isattn_block_mask_to_csr needs. */
+size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,
+                                                int32_t n_kb);
+
+/* Block presence matrix -> Q->K and K->Q CSR (the normalisation step of [P1]
+ * Core changes 2 and the transposed lists of [P4]).  presence: uint8 device
+ * [batch, heads, n_qb, n_kb], nonzero = kept.  Outputs and col_capacity as for
+ * isattn_index_to_block_sparse (capacity >= batch*heads*n_qb*n_kb). */
+isattn_status_t isattn_block_mask_to_csr(const uint8_t* presence, int32_t batch, int32_t heads,
+                                         int32_t n_qb, int32_t n_kb,
+                                         int32_t* q2k_row_ptr, int32_t* q2k_col,
+                                         int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                         int64_t col_capacity, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* Static string for a status code (never NULL). */
+const char* isattn_status_string(isattn_status_t status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* isattn_version(void);
+
+/* ---- Stage timing (measurement support) -----------------------------------
+ * A timer records HIP events on the call's stream around the three launches
+ * of isattn_attn_bwd_timed: [0] preprocess, [1] main loop kernel,
+ * [2] postprocess.  isattn_timer_read synchronises on the recorded events and
+ * returns the number of timed calls and the summed milliseconds per stage.
+ * A timer holds `capacity` calls; further calls wrap and overwrite. */
+typedef struct isattn_timer isattn_timer_t;
+
+isattn_status_t isattn_timer_create(int32_t capacity, isattn_timer_t** out);
+isattn_status_t isattn_timer_destroy(isattn_timer_t* timer);
+isattn_status_t isattn_timer_reset(isattn_timer_t* timer);
+isattn_status_t isattn_timer_read(isattn_timer_t* timer, int32_t* n_calls, float* stage_ms);
+
+/* isattn_attn_bwd with stage events recorded into `timer` (may be NULL). */
+isattn_status_t isattn_attn_bwd_timed(const isattn_shape_t* shape,
+                                      const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                      const isattn_tensor_t* v, const isattn_tensor_t* o,
+                                      const isattn_tensor_t* dO, const float* lse,
+                                      const isattn_mask_t* mask_desc, int32_t causal,
+                                      float softmax_scale,
+                                      const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                                      const isattn_tensor_t* dv,
+                                      int32_t algo, void* workspace, size_t workspace_bytes,
+                                      void* stream, isattn_timer_t* timer);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISATTN_H */

@@ -1,0 +1,20 @@
+"""isattn: sparse attention backward for AMD Instinct MI355X (gfx950).
+
+Entry points (thin wrappers over the C ABI in include/isattn.h):
+
+* ``attn_bwd``              -- dQ, dK, dV of masked attention (dense, causal,
+                               GQA, 128x128 block-sparse); LoopK or LoopQ.
+* ``index_to_block_sparse`` -- int32 top-k token indices -> BlockMask (CSR).
+* ``block_mask_to_csr``     -- uint8 block presence -> BlockMask (CSR).
+"""
+from ._abi import LibraryMissing, IsattnError, load as load_library  # noqa: F401
+from .api import (  # noqa: F401
+    BlockMask,
+    Timer,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    block_mask_to_csr,
+    index_to_block_sparse,
+)
+
+__version__ = "0.1.0"

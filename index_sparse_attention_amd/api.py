@@ -1,0 +1,187 @@
+"""Python binding over libisattn.so: argument marshalling only.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or the tensors are not on a GPU, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+
+ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ}
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _view(t: torch.Tensor, name: str) -> _abi.Tensor:
+    if t.dim() != 4:
+        raise ValueError(f"{name}: expected [batch, seq, heads, dim], got shape {tuple(t.shape)}")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: expected bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+    return _abi.Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+@dataclass
+class BlockMask:
+    """Block-sparse mask as device CSR arrays (int32), 128x128 blocks.
+
+    q2k: per (batch, mask head, query block) the ascending key blocks;
+    k2q: per (batch, mask head, key block) the ascending query blocks."""
+    heads: int
+    n_qb: int
+    n_kb: int
+    q2k_row_ptr: torch.Tensor
+    q2k_col: torch.Tensor
+    k2q_row_ptr: torch.Tensor
+    k2q_col: torch.Tensor
+    block_q: int = 128
+    block_k: int = 128
+
+    def nnz(self) -> int:
+        """Number of kept blocks (reads the last row pointer: synchronises)."""
+        return int(self.q2k_row_ptr[-1].item())
+
+    def _abi(self) -> _abi.Mask:
+        return _abi.Mask(_abi.MASK_BLOCK_CSR, self.block_q, self.block_k, self.heads,
+                         self.q2k_row_ptr.data_ptr(), self.q2k_col.data_ptr(),
+                         self.k2q_row_ptr.data_ptr(), self.k2q_col.data_ptr())
+
+
+class Timer:
+    """Stage timer of isattn_attn_bwd_timed (preprocess, main, postprocess)."""
+
+    def __init__(self, capacity: int = 256):
+        lib = _abi.load()
+        h = ctypes.c_void_p()
+        _abi.check(lib.isattn_timer_create(capacity, ctypes.byref(h)), "isattn_timer_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def reset(self):
+        _abi.check(_abi.load().isattn_timer_reset(self._h), "isattn_timer_reset")
+
+    def read(self):
+        """(n_calls, [pre_ms, main_ms, post_ms] summed over the calls)."""
+        n = ctypes.c_int32()
+        ms = (ctypes.c_float * 3)()
+        _abi.check(_abi.load().isattn_timer_read(self._h, ctypes.byref(n), ms), "isattn_timer_read")
+        return n.value, [ms[0], ms[1], ms[2]]
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            _abi.load().isattn_timer_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def attn_bwd_workspace_bytes(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v,
+                             algo="loopk") -> int:
+    shape = _abi.Shape(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v)
+    return int(_abi.load().isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), ALGOS[algo]))
+
+
+def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = False,
+             softmax_scale: float | None = None, algo: str = "loopk", dq=None, dk=None, dv=None,
+             workspace: torch.Tensor | None = None, stream=None, timer: Timer | None = None):
+    """Attention backward on the GPU.  Returns (dq, dk, dv) as bf16 tensors.
+
+    q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv], o/do [B,Sq,Hq,Dv] bf16;
+    lse fp32 [B,Hq,Sq] (natural log).  ``mask`` None = dense.  ``causal``
+    adds the bottom-right causal term.  Outputs are allocated when not given.
+    """
+    lib = _abi.load()
+    B, Sq, Hq, Dqk = q.shape
+    Sk, Hk, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
+    a = ALGOS[algo]
+    need = int(lib.isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    views = [_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
+                                      (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
+    args = [ctypes.byref(shape)] + [ctypes.byref(x) for x in views[:5]] + [
+        lse.data_ptr(), ctypes.byref(m), int(bool(causal)), float(softmax_scale)] + [
+        ctypes.byref(x) for x in views[5:]] + [a, workspace.data_ptr(), workspace.numel(),
+                                               _stream_ptr(stream)]
+    if timer is None:
+        _abi.check(lib.isattn_attn_bwd(*args), "isattn_attn_bwd")
+    else:
+        _abi.check(lib.isattn_attn_bwd_timed(*args, timer.handle), "isattn_attn_bwd_timed")
+    return dq, dk, dv
+
+
+def _csr_buffers(rows_q, rows_k, nnz_max, device):
+    i32 = dict(dtype=torch.int32, device=device)
+    return (torch.empty(rows_q + 1, **i32), torch.empty(max(nnz_max, 1), **i32),
+            torch.empty(rows_k + 1, **i32), torch.empty(max(nnz_max, 1), **i32))
+
+
+def index_to_block_sparse(indices: torch.Tensor, batch: int, seqlen_q: int, seqlen_k: int,
+                          block_q: int = 128, block_k: int = 128, stream=None) -> BlockMask:
+    """int32 indices [batch*seqlen_q, nhk, topk] -> BlockMask with heads = nhk."""
+    lib = _abi.load()
+    if indices.dtype != torch.int32 or indices.dim() != 3 or not indices.is_contiguous():
+        raise ValueError("indices must be contiguous int32 [batch*seqlen_q, nhk, topk]")
+    if not indices.is_cuda:
+        raise ValueError("indices must be a GPU tensor")
+    nhk, topk = indices.shape[1], indices.shape[2]
+    n_qb, n_kb = -(-seqlen_q // block_q), -(-seqlen_k // block_k)
+    nnz_max = batch * nhk * n_qb * n_kb
+    qp, qc, kp, kc = _csr_buffers(batch * nhk * n_qb, batch * nhk * n_kb, nnz_max, indices.device)
+    ws_bytes = int(lib.isattn_index_to_block_sparse_workspace_bytes(batch, seqlen_q, seqlen_k, nhk,
+                                                                    block_q, block_k))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=indices.device)
+    _abi.check(lib.isattn_index_to_block_sparse(
+        indices.data_ptr(), batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k,
+        qp.data_ptr(), qc.data_ptr(), kp.data_ptr(), kc.data_ptr(), qc.numel(),
+        ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "isattn_index_to_block_sparse")
+    return BlockMask(nhk, n_qb, n_kb, qp, qc, kp, kc, block_q, block_k)
+
+
+def block_mask_to_csr(presence: torch.Tensor, block_q: int = 128, block_k: int = 128,
+                      stream=None) -> BlockMask:
+    """uint8 presence [batch, heads, n_qb, n_kb] (nonzero = kept) -> BlockMask."""
+    lib = _abi.load()
+    if presence.dtype != torch.uint8 or presence.dim() != 4 or not presence.is_contiguous():
+        raise ValueError("presence must be contiguous uint8 [batch, heads, n_qb, n_kb]")
+    if not presence.is_cuda:
+        raise ValueError("presence must be a GPU tensor")
+    B, H, n_qb, n_kb = presence.shape
+    nnz_max = B * H * n_qb * n_kb
+    qp, qc, kp, kc = _csr_buffers(B * H * n_qb, B * H * n_kb, nnz_max, presence.device)
+    ws_bytes = int(lib.isattn_block_mask_to_csr_workspace_bytes(B, H, n_qb, n_kb))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=presence.device)
+    _abi.check(lib.isattn_block_mask_to_csr(
+        presence.data_ptr(), B, H, n_qb, n_kb, qp.data_ptr(), qc.data_ptr(), kp.data_ptr(),
+        kc.data_ptr(), qc.numel(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)),
+        "isattn_block_mask_to_csr")
+    return BlockMask(H, n_qb, n_kb, qp, qc, kp, kc, block_q, block_k)

@@ -1,0 +1,224 @@
+// extern "C" entry points of libisattn.so (declared in include/isattn.h).
+// Validation is in validate.cpp (HIP-free); this file carves workspaces and
+// enqueues the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/isattn.h"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+struct isattn_timer {
+    int32_t capacity = 0;
+    int32_t recorded = 0;      // calls recorded since the last reset (may exceed capacity)
+    std::vector<hipEvent_t> ev;  // 4 per slot
+};
+
+namespace {
+
+using namespace isattn;
+
+inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+isattn_status_t record(isattn_timer_t* t, int slot, int k, hipStream_t s) {
+    if (t == nullptr) return ISATTN_OK;
+    return hipEventRecord(t->ev[size_t(slot) * 4 + k], s) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
+}
+
+isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                              const isattn_tensor_t* k, const isattn_tensor_t* v,
+                              const isattn_tensor_t* o, const isattn_tensor_t* dO, const float* lse,
+                              const isattn_mask_t* mask, int32_t causal, float softmax_scale,
+                              const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                              const isattn_tensor_t* dv, int32_t algo, void* workspace,
+                              size_t workspace_bytes, void* stream, isattn_timer_t* timer) {
+    BwdArgs a{};
+    BwdPlan plan{};
+    isattn_status_t st = validate_bwd(shape, q, k, v, o, dO, lse, mask, causal, softmax_scale, dq, dk,
+                                      dv, algo, workspace, workspace_bytes, &a, &plan);
+    if (st != ISATTN_OK) return st;
+    if (a.B == 0) return ISATTN_OK;
+    a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
+    a.acc0 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc0));
+    a.acc1 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc1));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int slot = 0;
+    if (timer != nullptr) slot = timer->recorded % timer->capacity;
+
+    if ((st = record(timer, slot, 0, s)) != ISATTN_OK) return st;
+    if (launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
+    const hipError_t e = algo == ISATTN_ALGO_LOOPK ? launch_loopk(a, s) : launch_loopq(a, s);
+    if (e != hipSuccess) return ISATTN_ERR_HIP;
+    if ((st = record(timer, slot, 2, s)) != ISATTN_OK) return st;
+    if (launch_postprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if ((st = record(timer, slot, 3, s)) != ISATTN_OK) return st;
+    if (timer != nullptr) timer->recorded++;
+    return ISATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo) {
+    if (shape == nullptr) return 0;
+    BwdPlan p{};
+    if (!plan_bwd_workspace(*shape, algo, &p)) return 0;
+    return p.total;
+}
+
+isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                                const isattn_tensor_t* k, const isattn_tensor_t* v,
+                                const isattn_tensor_t* o, const isattn_tensor_t* dO, const float* lse,
+                                const isattn_mask_t* mask_desc, int32_t causal, float softmax_scale,
+                                const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                                const isattn_tensor_t* dv, int32_t algo, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return attn_bwd_impl(shape, q, k, v, o, dO, lse, mask_desc, causal, softmax_scale, dq, dk, dv, algo,
+                         workspace, workspace_bytes, stream, nullptr);
+}
+
+isattn_status_t isattn_attn_bwd_timed(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                                      const isattn_tensor_t* k, const isattn_tensor_t* v,
+                                      const isattn_tensor_t* o, const isattn_tensor_t* dO,
+                                      const float* lse, const isattn_mask_t* mask_desc, int32_t causal,
+                                      float softmax_scale, const isattn_tensor_t* dq,
+                                      const isattn_tensor_t* dk, const isattn_tensor_t* dv,
+                                      int32_t algo, void* workspace, size_t workspace_bytes,
+                                      void* stream, isattn_timer_t* timer) {
+    return attn_bwd_impl(shape, q, k, v, o, dO, lse, mask_desc, causal, softmax_scale, dq, dk, dv, algo,
+                         workspace, workspace_bytes, stream, timer);
+}
+
+size_t isattn_index_to_block_sparse_workspace_bytes(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                                                    int32_t nhk, int32_t block_q, int32_t block_k) {
+    if (block_q < 1 || block_k < 1 || seqlen_q < 0 || seqlen_k < 0) return 0;
+    CsrPlan p{};
+    if (!plan_csr_workspace(batch, nhk, cdiv(seqlen_q, block_q), cdiv(seqlen_k, block_k), true, &p))
+        return 0;
+    return p.total;
+}
+
+isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t batch, int32_t seqlen_q,
+                                             int32_t seqlen_k, int32_t nhk, int32_t topk,
+                                             int32_t block_q, int32_t block_k, int32_t* q2k_row_ptr,
+                                             int32_t* q2k_col, int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                             int64_t col_capacity, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+    CsrPlan p{};
+    isattn_status_t st = validate_index(indices, batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k,
+                                        q2k_row_ptr, q2k_col, k2q_row_ptr, k2q_col, col_capacity,
+                                        workspace, workspace_bytes, &p);
+    if (st != ISATTN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t n_qb = cdiv(seqlen_q, block_q);
+    const int32_t n_kb = cdiv(seqlen_k, block_k);
+    uint8_t* presence = reinterpret_cast<uint8_t*>(ws_at(workspace, p.off_presence));
+    int32_t* qcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_qcnt));
+    int32_t* kcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_kcnt));
+    if (launch_index_presence(indices, batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k, n_qb, n_kb,
+                              presence, qcnt, s) != hipSuccess)
+        return ISATTN_ERR_HIP;
+    if (launch_presence_to_csr(presence, batch * nhk, n_qb, n_kb, true, qcnt, kcnt, q2k_row_ptr, q2k_col,
+                               k2q_row_ptr, k2q_col, s) != hipSuccess)
+        return ISATTN_ERR_HIP;
+    return ISATTN_OK;
+}
+
+size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,
+                                                int32_t n_kb) {
+    CsrPlan p{};
+    if (!plan_csr_workspace(batch, heads, n_qb, n_kb, false, &p)) return 0;
+    return p.total;
+}
+
+isattn_status_t isattn_block_mask_to_csr(const uint8_t* presence, int32_t batch, int32_t heads,
+                                         int32_t n_qb, int32_t n_kb, int32_t* q2k_row_ptr,
+                                         int32_t* q2k_col, int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                         int64_t col_capacity, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    CsrPlan p{};
+    isattn_status_t st = validate_blockmask(presence, batch, heads, n_qb, n_kb, q2k_row_ptr, q2k_col,
+                                            k2q_row_ptr, k2q_col, col_capacity, workspace,
+                                            workspace_bytes, &p);
+    if (st != ISATTN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* qcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_qcnt));
+    int32_t* kcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_kcnt));
+    if (launch_presence_to_csr(presence, batch * heads, n_qb, n_kb, false, qcnt, kcnt, q2k_row_ptr,
+                               q2k_col, k2q_row_ptr, k2q_col, s) != hipSuccess)
+        return ISATTN_ERR_HIP;
+    return ISATTN_OK;
+}
+
+const char* isattn_status_string(isattn_status_t status) {
+    switch (status) {
+        case ISATTN_OK: return "ok";
+        case ISATTN_ERR_NULL: return "required pointer is NULL";
+        case ISATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case ISATTN_ERR_STRIDE_ALIGN: return "unsupported stride or alignment";
+        case ISATTN_ERR_UNSUPPORTED: return "outside the supported set";
+        case ISATTN_ERR_MASK: return "malformed mask descriptor";
+        case ISATTN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+        case ISATTN_ERR_CAPACITY: return "CSR column capacity too small";
+        case ISATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* isattn_version(void) { return "0.1.0"; }
+
+isattn_status_t isattn_timer_create(int32_t capacity, isattn_timer_t** out) {
+    if (out == nullptr) return ISATTN_ERR_NULL;
+    *out = nullptr;
+    if (capacity < 1) return ISATTN_ERR_SHAPE;
+    isattn_timer_t* t = new (std::nothrow) isattn_timer_t();
+    if (t == nullptr) return ISATTN_ERR_HIP;
+    t->capacity = capacity;
+    t->ev.assign(size_t(capacity) * 4, nullptr);
+    for (auto& e : t->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            isattn_timer_destroy(t);
+            return ISATTN_ERR_HIP;
+        }
+    }
+    *out = t;
+    return ISATTN_OK;
+}
+
+isattn_status_t isattn_timer_destroy(isattn_timer_t* timer) {
+    if (timer == nullptr) return ISATTN_OK;
+    for (auto& e : timer->ev)
+        if (e != nullptr) (void)hipEventDestroy(e);
+    delete timer;
+    return ISATTN_OK;
+}
+
+isattn_status_t isattn_timer_reset(isattn_timer_t* timer) {
+    if (timer == nullptr) return ISATTN_ERR_NULL;
+    timer->recorded = 0;
+    return ISATTN_OK;
+}
+
+isattn_status_t isattn_timer_read(isattn_timer_t* timer, int32_t* n_calls, float* stage_ms) {
+    if (timer == nullptr || n_calls == nullptr || stage_ms == nullptr) return ISATTN_ERR_NULL;
+    const int32_t n = timer->recorded < timer->capacity ? timer->recorded : timer->capacity;
+    stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.f;
+    *n_calls = n;
+    for (int32_t i = 0; i < n; ++i) {
+        hipEvent_t* ev = &timer->ev[size_t(i) * 4];
+        if (hipEventSynchronize(ev[3]) != hipSuccess) return ISATTN_ERR_HIP;
+        for (int k = 0; k < 3; ++k) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) return ISATTN_ERR_HIP;
+            stage_ms[k] += ms;
+        }
+    }
+    return ISATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Launch arguments shared by the host dispatcher and the attention-backward
+// kernels.  Plain data only: device pointers, element strides and sizes.
+#pragma once
+#include <stdint.h>
+
+namespace isattn {
+
+constexpr int kBlock = 128;   // mask block (query rows x keys) of the block-sparse path
+
+struct BwdArgs {
+    // bf16 tensors [batch, seq, heads, dim], last dim contiguous, strides in elements
+    const uint16_t* q;  int64_t q_sb, q_ss, q_sh;
+    const uint16_t* k;  int64_t k_sb, k_ss, k_sh;
+    const uint16_t* v;  int64_t v_sb, v_ss, v_sh;
+    const uint16_t* o;  int64_t o_sb, o_ss, o_sh;
+    const uint16_t* dO; int64_t do_sb, do_ss, do_sh;
+    uint16_t* dq; int64_t dq_sb, dq_ss, dq_sh;
+    uint16_t* dk; int64_t dk_sb, dk_ss, dk_sh;
+    uint16_t* dv; int64_t dv_sb, dv_ss, dv_sh;
+    const float* lse;     // [B, Hq, Sq] natural-log LSE
+    float* delta;         // [B, Hq, Sq] workspace: rowsum(dO * O)
+    float* acc0;          // LoopK: dK accumulator [B,Sk,Hk,Dqk]; LoopQ: dQ accumulator [B,Sq,Hq,Dqk]
+    float* acc1;          // LoopK: dV accumulator [B,Sk,Hk,Dv]; LoopQ: unused
+    int64_t acc0_elems, acc1_elems;
+    // block CSR (mask_kind == 1)
+    const int32_t* q2k_ptr; const int32_t* q2k_col;
+    const int32_t* k2q_ptr; const int32_t* k2q_col;
+    int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
+    int32_t Hm, n_qb, n_kb;
+    int32_t mask_kind, causal;
+    float scale;          // softmax_scale
+    float scale_log2;     // softmax_scale * log2(e)
+};
+
+}  // namespace isattn

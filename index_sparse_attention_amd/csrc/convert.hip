@@ -1,0 +1,280 @@
+// Token top-k indices -> block presence -> Q->K and K->Q CSR, on the GPU.
+//
+// Index tensor (total_q, NHK, topk) scattered into a per-(query block, KV
+// head) presence row, then compacted to per-query-block key-block lists --
+// MagiAttention PR #334, Core changes item 2 -- and to the transposed
+// per-key-block lists (K2Q metadata) of MagiAttention PR #331, "CSR Tile
+// Mapping".  -1 marks an unused slot (xtuner PR #2096, Main Changes item 1);
+// any value outside [0, Sk) is treated the same way.
+//
+// Kernels:
+//   k_index_presence : one workgroup per (qb, hk, b); streams the block's
+//                      block_q x topk indices with 16-byte loads, sets bits of
+//                      an LDS bitmap (test-then-set keeps LDS atomics rare once
+//                      a block is marked), writes the uint8 presence row and
+//                      its popcount.  HBM-bound on the index read.
+//   k_row_counts     : popcount of presence rows (block-mask path only).
+//   k_col_counts     : per-(b, h, kb) column counts, coalesced across kb.
+//   k_scan2          : two exclusive scans (rows, columns) -> row_ptr arrays.
+//   k_fill_q2k/k2q   : one wave per CSR row, ballot + prefix popcount writes
+//                      the ascending column list.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace isattn {
+namespace {
+
+constexpr int kPresThreads = 512;
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 4;
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ void mark_key(uint32_t* bits, int x, int Sk, int bk, int bk_shift) {
+    if (static_cast<unsigned>(x) < static_cast<unsigned>(Sk)) {
+        const int kb = bk_shift >= 0 ? (x >> bk_shift) : (x / bk);
+        const uint32_t bit = 1u << (kb & 31);
+        uint32_t* w = bits + (kb >> 5);
+        if ((__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & bit) == 0)
+            __hip_atomic_fetch_or(w, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+__global__ __launch_bounds__(kPresThreads) void k_index_presence(
+    const int32_t* __restrict__ idx, int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq,
+    int32_t bk, int32_t bk_shift, int32_t n_qb, int32_t n_kb, int32_t vec4,
+    uint8_t* __restrict__ presence, int32_t* __restrict__ qcnt) {
+    extern __shared__ uint32_t bits[];
+    __shared__ int red[kPresThreads / 64];
+    const int qb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int nwords = (n_kb + 31) >> 5;
+    for (int w = tid; w < nwords; w += kPresThreads) bits[w] = 0;
+    __syncthreads();
+
+    const int r0 = qb * bq;
+    const int rows = min(bq, Sq - r0);
+    const int64_t row_stride = int64_t(nhk) * topk;
+    const int32_t* base = idx + (int64_t(b) * Sq + r0) * row_stride + int64_t(hk) * topk;
+    if (vec4) {
+        const int per_row = topk >> 2;
+        const int total = rows * per_row;
+        int u = tid;
+        for (; u + 3 * kPresThreads < total; u += 4 * kPresThreads) {
+            int4 x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int uu = u + j * kPresThreads;
+                const int rr = uu / per_row;
+                const int c = uu - rr * per_row;
+                x[j] = *reinterpret_cast<const int4*>(base + rr * row_stride + 4 * c);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mark_key(bits, x[j].x, Sk, bk, bk_shift);
+                mark_key(bits, x[j].y, Sk, bk, bk_shift);
+                mark_key(bits, x[j].z, Sk, bk, bk_shift);
+                mark_key(bits, x[j].w, Sk, bk, bk_shift);
+            }
+        }
+        for (; u < total; u += kPresThreads) {
+            const int rr = u / per_row;
+            const int c = u - rr * per_row;
+            const int4 x = *reinterpret_cast<const int4*>(base + rr * row_stride + 4 * c);
+            mark_key(bits, x.x, Sk, bk, bk_shift);
+            mark_key(bits, x.y, Sk, bk, bk_shift);
+            mark_key(bits, x.z, Sk, bk, bk_shift);
+            mark_key(bits, x.w, Sk, bk, bk_shift);
+        }
+    } else {
+        const int total = rows * topk;
+        for (int u = tid; u < total; u += kPresThreads) {
+            const int rr = u / topk;
+            const int c = u - rr * topk;
+            mark_key(bits, base[rr * row_stride + c], Sk, bk, bk_shift);
+        }
+    }
+    __syncthreads();
+
+    uint8_t* out = presence + ((int64_t(b) * nhk + hk) * n_qb + qb) * int64_t(n_kb);
+    for (int kb = tid; kb < n_kb; kb += kPresThreads) out[kb] = (bits[kb >> 5] >> (kb & 31)) & 1u;
+    int cnt = 0;
+    for (int w = tid; w < nwords; w += kPresThreads) cnt += __popc(bits[w]);
+    cnt = wave_sum(cnt);
+    if ((tid & 63) == 0) red[tid >> 6] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < kPresThreads / 64; ++i) t += red[i];
+        qcnt[(int64_t(b) * nhk + hk) * n_qb + qb] = t;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ presence,
+                                                     int32_t rows, int32_t n_kb,
+                                                     int32_t* __restrict__ qcnt) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const uint8_t* p = presence + int64_t(row) * n_kb;
+    int c = 0;
+    for (int kb = lane; kb < n_kb; kb += 64) c += p[kb] != 0;
+    c = wave_sum(c);
+    if (lane == 0) qcnt[row] = c;
+}
+
+__global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ presence,
+                                                     int32_t n_qb, int32_t n_kb, int32_t tiles,
+                                                     int32_t* __restrict__ kcnt) {
+    const int bh = blockIdx.x / tiles;
+    const int kb = (blockIdx.x - bh * tiles) * 256 + threadIdx.x;
+    if (kb >= n_kb) return;
+    const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
+    int c = 0;
+    for (int qb = 0; qb < n_qb; ++qb) c += p[int64_t(qb) * n_kb] != 0;
+    kcnt[int64_t(bh) * n_kb + kb] = c;
+}
+
+// Block 0 scans cnt0 -> ptr0, block 1 scans cnt1 -> ptr1 (exclusive, with
+// ptr[0] = 0 and ptr[n] = total).
+__global__ __launch_bounds__(kScanThreads) void k_scan2(const int32_t* __restrict__ cnt0, int32_t n0,
+                                                        int32_t* __restrict__ ptr0,
+                                                        const int32_t* __restrict__ cnt1, int32_t n1,
+                                                        int32_t* __restrict__ ptr1) {
+    const int32_t* cnt = blockIdx.x == 0 ? cnt0 : cnt1;
+    const int n = blockIdx.x == 0 ? n0 : n1;
+    int32_t* ptr = blockIdx.x == 0 ? ptr0 : ptr1;
+    __shared__ int wsum[kScanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    if (tid == 0) ptr[0] = 0;
+    int carry = 0;
+    for (int base = 0; base < n; base += kScanThreads * kScanItems) {
+        int v[kScanItems];
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            const int i = base + tid * kScanItems + j;
+            v[j] = i < n ? cnt[i] : 0;
+            s += v[j];
+        }
+        int x = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wsum[wid] = x;
+        __syncthreads();
+        if (wid == 0) {
+            int t = lane < kScanThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+            for (int o = 1; o < kScanThreads / 64; o <<= 1) {
+                const int y = __shfl_up(t, o, 64);
+                if (lane >= o) t += y;
+            }
+            if (lane < kScanThreads / 64) wsum[lane] = t;
+        }
+        __syncthreads();
+        int run = carry + (wid > 0 ? wsum[wid - 1] : 0) + (x - s);
+#pragma unroll
+        for (int j = 0; j < kScanItems; ++j) {
+            const int i = base + tid * kScanItems + j;
+            run += v[j];
+            if (i < n) ptr[i + 1] = run;
+        }
+        carry += wsum[kScanThreads / 64 - 1];
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_q2k(const uint8_t* __restrict__ presence, int32_t rows,
+                                                   int32_t n_kb, const int32_t* __restrict__ q2k_ptr,
+                                                   int32_t* __restrict__ q2k_col) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const uint8_t* p = presence + int64_t(row) * n_kb;
+    int base = q2k_ptr[row];
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    for (int c0 = 0; c0 < n_kb; c0 += 64) {
+        const int kb = c0 + lane;
+        const bool on = kb < n_kb && p[kb] != 0;
+        const uint64_t m = __ballot(on);
+        if (on) q2k_col[base + __popcll(m & below)] = kb;
+        base += __popcll(m);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_k2q(const uint8_t* __restrict__ presence, int32_t cols,
+                                                   int32_t n_qb, int32_t n_kb,
+                                                   const int32_t* __restrict__ k2q_ptr,
+                                                   int32_t* __restrict__ k2q_col) {
+    const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (col >= cols) return;
+    const int bh = col / n_kb;
+    const int kb = col - bh * n_kb;
+    const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
+    int base = k2q_ptr[col];
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    for (int q0 = 0; q0 < n_qb; q0 += 64) {
+        const int qb = q0 + lane;
+        const bool on = qb < n_qb && p[int64_t(qb) * n_kb] != 0;
+        const uint64_t m = __ballot(on);
+        if (on) k2q_col[base + __popcll(m & below)] = qb;
+        base += __popcll(m);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,
+                                 int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
+                                 int32_t n_qb, int32_t n_kb, uint8_t* presence, int32_t* qcnt,
+                                 hipStream_t s) {
+    if (B == 0 || nhk == 0 || n_qb == 0) return hipSuccess;
+    const int bk_shift = (bk & (bk - 1)) == 0 ? __builtin_ctz(unsigned(bk)) : -1;
+    const int vec4 = (topk % 4 == 0) && ((reinterpret_cast<uintptr_t>(idx) & 15u) == 0);
+    const size_t lds = size_t((n_kb + 31) / 32) * sizeof(uint32_t);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_index_presence),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid(n_qb, nhk, B);
+    hipLaunchKernelGGL(k_index_presence, grid, dim3(kPresThreads), lds, s, idx, Sq, Sk, nhk, topk, bq,
+                       bk, bk_shift, n_qb, n_kb, vec4, presence, qcnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n_qb,
+                                  int32_t n_kb, bool have_row_counts, int32_t* qcnt,
+                                  int32_t* kcnt, int32_t* q2k_ptr, int32_t* q2k_col,
+                                  int32_t* k2q_ptr, int32_t* k2q_col, hipStream_t s) {
+    const int32_t rows = BH * n_qb;
+    const int32_t cols = BH * n_kb;
+    if (rows > 0 && !have_row_counts)
+        hipLaunchKernelGGL(k_row_counts, dim3((rows + 3) / 4), dim3(256), 0, s, presence, rows, n_kb,
+                           qcnt);
+    if (cols > 0) {
+        const int tiles = (n_kb + 255) / 256;
+        hipLaunchKernelGGL(k_col_counts, dim3(BH * tiles), dim3(256), 0, s, presence, n_qb, n_kb, tiles,
+                           kcnt);
+    }
+    hipLaunchKernelGGL(k_scan2, dim3(2), dim3(kScanThreads), 0, s, qcnt, rows, q2k_ptr, kcnt, cols,
+                       k2q_ptr);
+    if (rows > 0 && n_kb > 0)
+        hipLaunchKernelGGL(k_fill_q2k, dim3((rows + 3) / 4), dim3(256), 0, s, presence, rows, n_kb,
+                           q2k_ptr, q2k_col);
+    if (cols > 0 && n_qb > 0)
+        hipLaunchKernelGGL(k_fill_k2q, dim3((cols + 3) / 4), dim3(256), 0, s, presence, cols, n_qb,
+                           n_kb, k2q_ptr, k2q_col);
+    return hipGetLastError();
+}
+
+}  // namespace isattn

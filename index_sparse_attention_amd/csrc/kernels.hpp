@@ -1,0 +1,30 @@
+// Host-side launchers of the HIP kernels (one translation unit each).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bwd_args.hpp"
+
+namespace isattn {
+
+// delta = rowsum(dO * O) and zeroing of the fp32 accumulators of `algo`.
+hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s);
+// fp32 accumulators -> bf16 outputs (x softmax_scale for dK / dQ).
+hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s);
+// Main loops.
+hipError_t launch_loopk(const BwdArgs& a, hipStream_t s);
+hipError_t launch_loopq(const BwdArgs& a, hipStream_t s);
+
+// Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
+hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,
+                                 int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
+                                 int32_t n_qb, int32_t n_kb, uint8_t* presence, int32_t* qcnt,
+                                 hipStream_t s);
+// Presence -> Q->K and K->Q CSR.  Row counts are computed here unless
+// `have_row_counts` (the index path produces them with the presence rows).
+hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n_qb,
+                                  int32_t n_kb, bool have_row_counts, int32_t* qcnt,
+                                  int32_t* kcnt, int32_t* q2k_ptr, int32_t* q2k_col,
+                                  int32_t* k2q_ptr, int32_t* k2q_col, hipStream_t s);
+
+}  // namespace isattn

@@ -1,0 +1,338 @@
+// LoopQ attention backward: outer loop over key tiles, inner loop over the
+// kept query tiles of every query head of the GQA group (the default
+// direction that MagiAttention PR #334 compares LoopK against: dK/dV stay on
+// chip, dQ is reduced by fp32 atomics; the key-block -> query-block lists are
+// the K2Q CSR metadata of MagiAttention PR #331, "CSR Tile Mapping").  dK/dV
+// are written directly as bf16 once the group is done (no postprocess for
+// them, as the flash-attention "switch mha to no postprocess" commit does).
+//
+// One workgroup = 4 waves = one 128-key tile of one (batch, KV head); wave w
+// owns keys 32w..32w+31.  Each inner step stages 64 query rows of Q and dO
+// (row-major and transposed), their LSE*log2e and delta.  Per step and wave:
+//
+//   S  = Q K^T        [64 q x 32 keys]  32x32x16 MFMA, A = Q (LDS), B = K (regs)
+//   dP = dO V^T       [64 q x 32 keys]  B = V (regs)
+//   P  = exp2(S*scale*log2e - LSE*log2e),  dS = P * (dP - delta)
+//   dV += P^T dO      [32 keys x Dv]    A = P^T from the S accumulator registers
+//   dK += dS^T Q      [32 keys x Dqk]   A = dS^T from registers, B = Q^T (LDS)
+//   dS -> LDS, then dQ_part = dS K [64 q x Dqk/4] per wave (16x16x32 MFMA,
+//   B = K (regs)), fp32 atomic add into the dQ accumulator.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace isattn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DQK, int DV>
+struct LoopQCfg {
+    static constexpr int BN = 128;                 // keys per workgroup
+    static constexpr int BM = 64;                  // query rows per inner step
+    static constexpr int NT = 256;
+    static constexpr int PQ = DQK + 8;
+    static constexpr int PQT = BM + 4;
+    static constexpr int PDO = DV + 8;
+    static constexpr int PDOT = BM + 4;
+    static constexpr int PDS = BN + 8;             // sdS[m][key]
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_QT = OFF_Q + BM * PQ;
+    static constexpr int OFF_DO = OFF_QT + DQK * PQT;
+    static constexpr int OFF_DOT = OFF_DO + BM * PDO;
+    static constexpr int OFF_DS = OFF_DOT + DV * PDOT;
+    static constexpr int OFF_STAT = OFF_DS + BM * PDS;  // float lse2[BM], delta[BM]
+    static constexpr int END_LOOP = OFF_STAT + 4 * BM;
+    static constexpr int PK = DQK + 8;             // prologue staging
+    static constexpr int PV = DV + 8;
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_V = BN * PK;
+    static constexpr int END_PRO = OFF_V + BN * PV;
+    static constexpr int LDS_ELEMS = END_LOOP > END_PRO ? END_LOOP : END_PRO;
+    static constexpr int LDS_BYTES = LDS_ELEMS * 2;
+    static constexpr int NCQ = DQK / 16;
+    static constexpr int NCV = DV / 16;
+    static constexpr int NDK = DQK / 32;           // dK accumulator tiles
+    static constexpr int NDV = DV / 32;            // dV accumulator tiles
+    static constexpr int WQ = DQK / 4;             // dQ d-slice per wave
+    static constexpr int NTQ = WQ / 16;
+    static_assert(WQ % 16 == 0, "Dqk must split into 16-wide tiles per wave");
+    static_assert((OFF_STAT * 2) % 16 == 0, "stat block alignment");
+};
+
+template <int D, int PITCH, int ROWS, int NT>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t row_stride,
+                                           int row0, int limit, int tid) {
+    constexpr int CH = D / 8;
+    for (int u = tid; u < ROWS * CH; u += NT) {
+        const int r = u / CH;
+        const int c = u - r * CH;
+        const int gr = row0 + r;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
+        *reinterpret_cast<u32x4_t*>(dst + r * PITCH + 8 * c) = v;
+    }
+}
+
+// ROWS rows: row-major copy (pitch P) and transposed copy (pitch PT).
+template <int D, int P, int PT, int ROWS, int NT>
+__device__ __forceinline__ void stage_both(uint16_t* dst, uint16_t* dstT, const uint16_t* src,
+                                           int64_t row_stride, int row0, int limit, int tid) {
+    constexpr int CH = D / 8;
+    for (int u = tid; u < ROWS * CH; u += NT) {
+        const int r = u / CH;
+        const int c = u - r * CH;
+        const int gr = row0 + r;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
+        *reinterpret_cast<u32x4_t*>(dst + r * P + 8 * c) = v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dstT[(8 * c + 2 * j) * PT + r] = uint16_t(v[j] & 0xffffu);
+            dstT[(8 * c + 2 * j + 1) * PT + r] = uint16_t(v[j] >> 16);
+        }
+    }
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
+    using C = LoopQCfg<DQK, DV>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // ---- work item: longest key columns first under a causal mask
+    const int BH = a.B * a.Hk;
+    const int id = blockIdx.x;
+    const int kb = id / BH;
+    const int bh = id - kb * BH;
+    const int b = bh / a.Hk;
+    const int hk = bh - b * a.Hk;
+    const int n_base = kb * C::BN;
+    const int shift = a.Sk - a.Sq;
+
+    // ---- prologue: K and V tiles -> registers
+    stage_rows<DQK, C::PK, C::BN, C::NT>(lds + C::OFF_K, a.k + b * a.k_sb + hk * a.k_sh, a.k_ss, n_base,
+                                         a.Sk, tid);
+    stage_rows<DV, C::PV, C::BN, C::NT>(lds + C::OFF_V, a.v + b * a.v_sb + hk * a.v_sh, a.v_ss, n_base,
+                                        a.Sk, tid);
+    __syncthreads();
+    const int nk = 32 * w + l32;                 // this lane's key within the tile (32x32 column)
+    bf16x8_t kS[C::NCQ], vS[C::NCV];             // B operands of S / dP
+    bf16x8_t kQ[C::NTQ][4];                      // B operand of dQ_part (k = key)
+    {
+        const uint16_t* sK = lds + C::OFF_K;
+        const uint16_t* sV = lds + C::OFF_V;
+#pragma unroll
+        for (int c = 0; c < C::NCQ; ++c) kS[c] = as_bf16x8(lds_read128(sK + nk * C::PK + 16 * c + 8 * h2));
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) vS[c] = as_bf16x8(lds_read128(sV + nk * C::PV + 16 * c + 8 * h2));
+#pragma unroll
+        for (int t = 0; t < C::NTQ; ++t) {
+            const int d = w * C::WQ + 16 * t + l16;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                u32x4_t v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = 32 * c + 8 * g4 + 2 * j;
+                    v[j] = uint32_t(sK[n * C::PK + d]) | (uint32_t(sK[(n + 1) * C::PK + d]) << 16);
+                }
+                kQ[t][c] = as_bf16x8(v);
+            }
+        }
+    }
+    __syncthreads();
+
+    f32x16_t dk[C::NDK], dv[C::NDV];
+#pragma unroll
+    for (int t = 0; t < C::NDK; ++t) dk[t] = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < C::NDV; ++t) dv[t] = f32x16_t{};
+
+    uint16_t* sQ = lds + C::OFF_Q;
+    uint16_t* sQt = lds + C::OFF_QT;
+    uint16_t* sdO = lds + C::OFF_DO;
+    uint16_t* sdOt = lds + C::OFF_DOT;
+    uint16_t* sdS = lds + C::OFF_DS;
+    float* sL = reinterpret_cast<float*>(lds + C::OFF_STAT);
+    float* sD = sL + C::BM;
+    const int key = n_base + nk;
+    const bool key_in = key < a.Sk;
+    const bool tile_ragged = n_base + C::BN > a.Sk;
+
+    for (int gi = 0; gi < a.G; ++gi) {
+        const int h = hk * a.G + gi;
+        int qb_count, qb_first = 0;
+        const int32_t* qb_list = nullptr;
+        if (a.mask_kind == 1) {
+            const int hm = h * a.Hm / a.Hq;
+            const int r = (b * a.Hm + hm) * a.n_kb + kb;
+            const int beg = a.k2q_ptr[r];
+            qb_count = a.k2q_ptr[r + 1] - beg;
+            qb_list = a.k2q_col + beg;
+        } else {
+            qb_first = 0;
+            if (a.causal) {
+                const int first_row = n_base - shift;           // first row that sees key n_base
+                qb_first = first_row <= 0 ? 0 : first_row / kBlock;
+            }
+            qb_count = a.n_qb - qb_first;
+        }
+        const uint16_t* gq = a.q + b * a.q_sb + h * a.q_sh;
+        const uint16_t* gdo = a.dO + b * a.do_sb + h * a.do_sh;
+        const int64_t srow = (int64_t(b) * a.Hq + h) * a.Sq;
+        float* gdq = a.acc0 + (int64_t(b) * a.Sq * a.Hq + h) * DQK;   // + row * Hq * DQK + d
+
+        for (int it = 0; it < qb_count; ++it) {
+            const int qb = qb_list ? qb_list[it] : qb_first + it;
+            if (qb < 0 || qb >= a.n_qb) continue;   // ignore malformed CSR entries
+#pragma unroll 1
+            for (int half = 0; half < kBlock / C::BM; ++half) {
+                const int m0 = qb * kBlock + half * C::BM;
+                if (m0 >= a.Sq) break;
+                const int mlast = min(m0 + C::BM - 1, a.Sq - 1);
+                if (a.causal && mlast + shift < n_base) continue;  // every row of the step precedes the tile
+                stage_both<DQK, C::PQ, C::PQT, C::BM, C::NT>(sQ, sQt, gq, a.q_ss, m0, a.Sq, tid);
+                stage_both<DV, C::PDO, C::PDOT, C::BM, C::NT>(sdO, sdOt, gdo, a.do_ss, m0, a.Sq, tid);
+                if (tid < C::BM) {
+                    const int row = m0 + tid;
+                    sL[tid] = row < a.Sq ? a.lse[srow + row] * kLog2e : __builtin_inff();
+                    sD[tid] = row < a.Sq ? a.delta[srow + row] : 0.f;
+                }
+                __syncthreads();
+
+                f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+                f32x16_t dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+                for (int c = 0; c < C::NCQ; ++c) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const bf16x8_t qa = as_bf16x8(lds_read128(sQ + (32 * mt + l32) * C::PQ + 16 * c + 8 * h2));
+                        s[mt] = mfma32(qa, kS[c], s[mt]);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < C::NCV; ++c) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const bf16x8_t oa = as_bf16x8(lds_read128(sdO + (32 * mt + l32) * C::PDO + 16 * c + 8 * h2));
+                        dp[mt] = mfma32(oa, vS[c], dp[mt]);
+                    }
+                }
+
+                const bool need_mask = tile_ragged || (a.causal && n_base + C::BN - 1 > m0 + shift);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int ml = 32 * mt + 8 * (i >> 2) + 4 * h2 + (i & 3);
+                        float p = fast_exp2(s[mt][i] * a.scale_log2 - sL[ml]);
+                        if (need_mask) {
+                            const bool ok = key_in && (!a.causal || key <= m0 + ml + shift);
+                            p = ok ? p : 0.f;
+                        }
+                        const float ds = p * (dp[mt][i] - sD[ml]);
+                        s[mt][i] = p;
+                        dp[mt][i] = ds;
+                        sdS[ml * C::PDS + nk] = to_bf16(ds);
+                    }
+                }
+
+                // dV += P^T dO, dK += dS^T Q  (A operands straight from registers)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        u32x4_t pp, pd;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            pp[j] = pack_bf16x2(s[mt][8 * c + 2 * j], s[mt][8 * c + 2 * j + 1]);
+                            pd[j] = pack_bf16x2(dp[mt][8 * c + 2 * j], dp[mt][8 * c + 2 * j + 1]);
+                        }
+                        const int moff = 32 * mt + 16 * c + 4 * h2;
+#pragma unroll
+                        for (int dt = 0; dt < C::NDV; ++dt) {
+                            const uint16_t* src = sdOt + (32 * dt + l32) * C::PDOT + moff;
+                            const u32x2_t lo = lds_read64(src);
+                            const u32x2_t hi = lds_read64(src + 8);
+                            const u32x4_t bv = {lo[0], lo[1], hi[0], hi[1]};
+                            dv[dt] = mfma32(as_bf16x8(pp), as_bf16x8(bv), dv[dt]);
+                        }
+#pragma unroll
+                        for (int dt = 0; dt < C::NDK; ++dt) {
+                            const uint16_t* src = sQt + (32 * dt + l32) * C::PQT + moff;
+                            const u32x2_t lo = lds_read64(src);
+                            const u32x2_t hi = lds_read64(src + 8);
+                            const u32x4_t bq = {lo[0], lo[1], hi[0], hi[1]};
+                            dk[dt] = mfma32(as_bf16x8(pd), as_bf16x8(bq), dk[dt]);
+                        }
+                    }
+                }
+                __syncthreads();
+
+                // dQ_part = dS K on this wave's d-slice; atomics into the dQ accumulator
+#pragma unroll
+                for (int mt = 0; mt < C::BM / 16; ++mt) {
+                    bf16x8_t sa[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        sa[c] = as_bf16x8(lds_read128(sdS + (16 * mt + l16) * C::PDS + 32 * c + 8 * g4));
+                    const int row0 = m0 + 16 * mt + 4 * g4;
+#pragma unroll
+                    for (int t = 0; t < C::NTQ; ++t) {
+                        f32x4_t acc = f32x4_t{};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) acc = mfma16(sa[c], kQ[t][c], acc);
+                        const int d = w * C::WQ + 16 * t + l16;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (row0 + i < a.Sq)
+                                atomic_add_f32(gdq + int64_t(row0 + i) * a.Hq * DQK + d, acc[i]);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- epilogue: dK = scale * acc, dV = acc -> bf16, stored directly
+    uint16_t* gdk = a.dk + b * a.dk_sb + hk * a.dk_sh;
+    uint16_t* gdv = a.dv + b * a.dv_sb + hk * a.dv_sh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int n = n_base + 32 * w + 8 * (i >> 2) + 4 * h2 + (i & 3);
+        if (n < a.Sk) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDK; ++dt) gdk[n * a.dk_ss + 32 * dt + l32] = to_bf16(dk[dt][i] * a.scale);
+#pragma unroll
+            for (int dt = 0; dt < C::NDV; ++dt) gdv[n * a.dv_ss + 32 * dt + l32] = to_bf16(dv[dt][i]);
+        }
+    }
+}
+
+template <int DQK, int DV>
+hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
+    using C = LoopQCfg<DQK, DV>;
+    const int64_t grid = int64_t(a.n_kb) * a.B * a.Hk;
+    if (grid == 0) return hipSuccess;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_loopq<DQK, DV>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       C::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((k_bwd_loopq<DQK, DV>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_loopq(const BwdArgs& a, hipStream_t s) {
+    if (a.Dqk == 64 && a.Dv == 64) return launch_t<64, 64>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_t<128, 128>(a, s);
+    if (a.Dqk == 192 && a.Dv == 128) return launch_t<192, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace isattn

@@ -110,8 +110,13 @@ def tile_grads(qr, dor, lser, dr, kc, vc, em, s):
     return P, dS
 
 
-def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, order: str = "K"):
+def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, order: str = "K",
+             heads=None):
     """Backward of masked attention in float64.  Returns (dQ, dK, dV).
+
+    ``heads``: optional iterable of query heads whose pairs are evaluated; the
+    result equals the full backward when every other head's LSE is +inf
+    (their P is zero, so they contribute nothing and get dQ = 0).
 
     order="K": for each (batch, query head, query block), for each kept key
     block of its Q->K CSR row -- accumulate dQ locally, add dK/dV per block.
@@ -135,9 +140,10 @@ def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, or
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
+    hset = set(range(Hq)) if heads is None else set(int(x) for x in heads)
     if order == "K":
         for b in range(B):
-            for h in range(Hq):
+            for h in sorted(hset):
                 hk = _m.kv_head(h, Hq, Hk)
                 hm = _m.mask_head(h, Hq, mask) if mask.kind == "block" else 0
                 for qb in range(n_qb):
@@ -158,7 +164,7 @@ def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, or
                 for kb in range(n_kb):
                     cols = np.arange(kb * bk, min((kb + 1) * bk, Sk))
                     hrow, qrow = [], []
-                    for h in [h for h in range(Hq) if _m.kv_head(h, Hq, Hk) == hk]:
+                    for h in [h for h in range(Hq) if _m.kv_head(h, Hq, Hk) == hk and h in hset]:
                         hm = _m.mask_head(h, Hq, mask) if mask.kind == "block" else 0
                         for qb in _m.k2q_row(mask, b, hm, kb, n_qb, n_kb):
                             r = np.arange(qb * bq, min((qb + 1) * bq, Sq))

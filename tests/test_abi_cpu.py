@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/isattn.h declares, sizes workspaces as documented, and rejects bad
+arguments with the documented status before any kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from index_sparse_attention_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isattn.h")
+
+OK, NULL, SHAPE, STRIDE, UNSUP, MASK, WS, CAP = 0, 1, 2, 3, 4, 5, 6, 7
+FAKE = 0x7F0000000000          # aligned dummy device address: never dereferenced on a failed check
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(isattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
+    assert set(_abi.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.isattn_version().decode().count(".") == 2
+    for code in range(9):
+        assert lib.isattn_status_string(code)
+    assert lib.isattn_status_string(99) == b"unknown status"
+
+
+def shape(B=1, Sq=256, Sk=256, Hq=2, Hk=2, Dqk=128, Dv=128):
+    return _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
+
+
+def ws_bytes(lib, s, algo):
+    return lib.isattn_attn_bwd_workspace_bytes(ctypes.byref(s), algo)
+
+
+def test_workspace_sizes(lib):
+    s = shape(B=2, Sq=300, Sk=200, Hq=4, Hk=2, Dqk=128, Dv=128)
+    al = lambda x: (x + 255) // 256 * 256
+    delta = al(2 * 300 * 4 * 4)
+    assert ws_bytes(lib, s, 0) == delta + al(2 * 200 * 2 * 128 * 4) * 2
+    assert ws_bytes(lib, s, 1) == delta + al(2 * 300 * 4 * 128 * 4)
+    assert ws_bytes(lib, s, 7) == 0
+    assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
+    # converter: presence B*H*nQB*nKB bytes + row and column counts
+    assert lib.isattn_index_to_block_sparse_workspace_bytes(1, 16384, 16384, 2, 128, 128) == \
+        al(2 * 128 * 128) + al(2 * 128 * 4) + al(2 * 128 * 4)
+    assert lib.isattn_block_mask_to_csr_workspace_bytes(2, 16, 64, 64) == al(2 * 16 * 64 * 4) * 2
+
+
+class Call:
+    """Builds a valid-looking isattn_attn_bwd argument set; tests break one part."""
+
+    def __init__(self, lib, algo=0, **kw):
+        self.lib = lib
+        self.shape = shape(**kw)
+        s = self.shape
+        self.views = {}
+        for name, (S, H, D) in {"q": (s.seqlen_q, s.heads_q, s.dim_qk), "k": (s.seqlen_k, s.heads_k, s.dim_qk),
+                                "v": (s.seqlen_k, s.heads_k, s.dim_v), "o": (s.seqlen_q, s.heads_q, s.dim_v),
+                                "do": (s.seqlen_q, s.heads_q, s.dim_v), "dq": (s.seqlen_q, s.heads_q, s.dim_qk),
+                                "dk": (s.seqlen_k, s.heads_k, s.dim_qk), "dv": (s.seqlen_k, s.heads_k, s.dim_v)}.items():
+            self.views[name] = _abi.Tensor(FAKE, S * H * D, H * D, D)
+        self.lse = FAKE
+        self.mask = None
+        self.causal = 0
+        self.scale = 0.125
+        self.algo = algo
+        self.ws = FAKE
+        self.ws_bytes = ws_bytes(lib, self.shape, algo) if algo in (0, 1) else 0
+
+    def __call__(self, shape_ptr=True):
+        v = self.views
+        sp = ctypes.byref(self.shape) if shape_ptr else None
+        mp = ctypes.byref(self.mask) if self.mask is not None else None
+        ref = lambda t: ctypes.byref(t) if t is not None else None
+        return self.lib.isattn_attn_bwd(sp, ref(v["q"]), ref(v["k"]), ref(v["v"]), ref(v["o"]), ref(v["do"]),
+                                        self.lse, mp, self.causal, self.scale, ref(v["dq"]), ref(v["dk"]),
+                                        ref(v["dv"]), self.algo, self.ws, self.ws_bytes, None)
+
+
+def test_bwd_validation_errors(lib):
+    assert Call(lib)(shape_ptr=False) == NULL
+    c = Call(lib); c.views["q"] = None; assert c() == NULL
+    c = Call(lib); c.views["dk"].ptr = None; assert c() == NULL
+    c = Call(lib); c.lse = None; assert c() == NULL
+    assert Call(lib, Hq=3, Hk=2)() == SHAPE
+    assert Call(lib, B=-1)() == SHAPE
+    assert Call(lib, Dqk=96, Dv=96)() == UNSUP
+    assert Call(lib, Dqk=128, Dv=64)() == UNSUP
+    assert Call(lib, Dqk=256, Dv=256)() == UNSUP
+    assert Call(lib, algo=5)() == UNSUP
+    c = Call(lib); c.scale = float("nan"); assert c() == UNSUP
+    c = Call(lib); c.views["v"].ptr = FAKE + 8; assert c() == STRIDE
+    c = Call(lib); c.views["o"].stride_s = 130; assert c() == STRIDE
+    c = Call(lib); c.views["dq"].stride_h = -128; assert c() == STRIDE
+    c = Call(lib); c.ws_bytes -= 1; assert c() == WS
+    c = Call(lib); c.ws = None; assert c() == WS
+    c = Call(lib); c.ws = FAKE + 16; assert c() == WS
+    c = Call(lib); c.mask = _abi.Mask(7, 128, 128, 2, FAKE, FAKE, FAKE, FAKE); assert c() == MASK
+    c = Call(lib); c.mask = _abi.Mask(1, 64, 64, 2, FAKE, FAKE, FAKE, FAKE); assert c() == UNSUP
+    c = Call(lib, Hq=4, Hk=2); c.mask = _abi.Mask(1, 128, 128, 3, FAKE, FAKE, FAKE, FAKE); assert c() == MASK
+    c = Call(lib); c.mask = _abi.Mask(1, 128, 128, 2, None, None, FAKE, FAKE); assert c() == NULL
+    c = Call(lib, algo=1); c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, None, None); assert c() == NULL
+
+
+def test_index_converter_validation_errors(lib):
+    def call(indices=FAKE, B=1, Sq=256, Sk=256, nhk=2, topk=64, bq=128, bk=128, cap=None, ws=FAKE,
+             wsb=None, outs=(FAKE, FAKE, FAKE, FAKE)):
+        n_qb, n_kb = -(-Sq // max(bq, 1)), -(-Sk // max(bk, 1))
+        cap = B * nhk * n_qb * n_kb if cap is None else cap
+        if wsb is None:
+            wsb = lib.isattn_index_to_block_sparse_workspace_bytes(B, Sq, Sk, nhk, max(bq, 1), max(bk, 1))
+        return lib.isattn_index_to_block_sparse(indices, B, Sq, Sk, nhk, topk, bq, bk, *outs, cap, ws, wsb,
+                                                None)
+    assert call(indices=None) == NULL
+    assert call(outs=(None, FAKE, FAKE, FAKE)) == NULL
+    assert call(outs=(FAKE, FAKE, FAKE, None)) == NULL
+    assert call(B=-1) == SHAPE
+    assert call(bq=0) == SHAPE
+    assert call(cap=7) == CAP
+    assert call(wsb=16) == WS
+    assert call(ws=FAKE + 64) == WS
+    assert call(Sk=(1 << 19) * 128 + 1, bk=128) == UNSUP
+
+
+def test_block_mask_validation_errors(lib):
+    def call(presence=FAKE, B=2, H=4, nq=8, nk=8, cap=None, wsb=None, ws=FAKE):
+        cap = B * H * nq * nk if cap is None else cap
+        wsb = lib.isattn_block_mask_to_csr_workspace_bytes(B, H, nq, nk) if wsb is None else wsb
+        return lib.isattn_block_mask_to_csr(presence, B, H, nq, nk, FAKE, FAKE, FAKE, FAKE, cap, ws, wsb, None)
+    assert call(presence=None) == NULL
+    assert call(H=-2) == SHAPE
+    assert call(cap=10) == CAP
+    assert call(wsb=0) == WS

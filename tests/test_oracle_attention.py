@@ -398,3 +398,19 @@ def test_flop_and_block_counts():
     assert oracle.kept_block_count(m, 1, 4, 256, 256, False) == 12
     # 192/128 dims
     assert oracle.flop_count(d, 1, 1, 128, 128, 192, 128, True) == 128 * 128 * 2 * (3 * 192 + 2 * 128)
+
+
+def test_heads_subset_backward_matches_infinite_lse():
+    """attn_bwd(heads=...) equals the full backward when every other head has
+    LSE = +inf (such heads contribute nothing and get dQ = 0)."""
+    B, Hq, Hk, Sq, Sk = 1, 4, 2, 9, 11
+    q, k, v, do = rand(B, Sq, Hq, 4), rand(B, Sk, Hk, 4), rand(B, Sk, Hk, 3), rand(B, Sq, Hq, 3)
+    m = oracle.dense_mask()
+    O, L = oracle.attn_fwd(q, k, v, m, True, 0.5, heads=[1, 2])
+    full = oracle.attn_bwd(q, k, v, O, do, L, m, True, 0.5)
+    sub = oracle.attn_bwd(q, k, v, O, do, L, m, True, 0.5, heads=[1, 2])
+    subq = oracle.attn_bwd(q, k, v, O, do, L, m, True, 0.5, order="Q", heads=[1, 2])
+    for a, b, c in zip(full, sub, subq):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+        np.testing.assert_allclose(a, c, atol=1e-12)
+    assert np.all(full[0][:, :, [0, 3]] == 0)
