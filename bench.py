@@ -1,0 +1,322 @@
+"""Benchmark: attention-backward TFLOP/s on kept blocks, 8K block-sparse (keep 0.25).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--algo split|loopk|loopq] [--no-cpu-baseline] [--no-compare]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+block presence -> Q->K / K->Q CSR on the GPU, then the backward call (delta
+preprocess, the main kernel(s), and for LoopK/LoopQ the fp32 -> bf16
+postprocess).  Inputs are resident in HBM before the timed region.  FLOP are
+counted over computed blocks only: 2 * (3*Dqk + 2*Dv) per (query, key) pair of
+every kept block, whatever the algorithm executes.
+
+Printed on stdout: one JSON line.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "blocksparse_mha_s8k_d128"
+METRIC = "attn-bwd TFLOP/s on kept blocks, 8K block-sparse 0.75; % bf16 MFMA peak"
+BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+# kernels of each algorithm: (name, timer stage, algorithmic FLOP per pair, executed FLOP per pair)
+def main_kernels(algo, dqk, dv):
+    full = 2 * (3 * dqk + 2 * dv)
+    if algo == "loopk":
+        return [("k_bwd_loopk", 1, full, full)]
+    if algo == "loopq":
+        return [("k_bwd_loopq", 1, full, full)]
+    # split: the dK/dV pass does S, dP, dV, dK; the dQ pass does dQ plus a recompute of S and dP
+    return [("k_bwd_dkdv", 1, 2 * (2 * dqk + 2 * dv), 2 * (2 * dqk + 2 * dv)),
+            ("k_bwd_dq", 2, 2 * dqk, 2 * (2 * dqk + dv))]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_blocks(w, presence=None, indices_presence=None):
+    """Computed (b, head, qb, kb) blocks: mask blocks with at least one visible pair."""
+    n_qb, n_kb = w.n_qb, w.n_kb
+    if w.mask in ("block", "index"):
+        p = presence if presence is not None else indices_presence
+        Hm = p.shape[1]
+        cnt = 0
+        if w.causal:
+            qb = np.arange(n_qb)[:, None]
+            kb = np.arange(n_kb)[None, :]
+            last = np.minimum((qb + 1) * 128, w.seqlen_q) - 1
+            vis = kb * 128 <= last + w.seqlen_k - w.seqlen_q
+            cnt = int(((p != 0) & vis[None, None]).sum())
+        else:
+            cnt = int((p != 0).sum())
+        return cnt * (w.heads_q // Hm)
+    per_head = 0
+    for qb in range(n_qb):
+        if w.causal:
+            last = min((qb + 1) * 128, w.seqlen_q) - 1
+            lim = last + w.seqlen_k - w.seqlen_q
+            per_head += 0 if lim < 0 else min(n_kb, lim // 128 + 1)
+        else:
+            per_head += n_kb
+    return per_head * w.batch * w.heads_q
+
+
+def flop_per_step(w, kept):
+    return kept * 128 * 128 * 2 * (3 * w.dim_qk + 2 * w.dim_v)
+
+
+def file_sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            t = json.load(f).get(kernel_key)
+        if not t or t.get("source_sha256") != file_sha(t["source"]):
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, data, budget_s=15.0, max_heads=16):
+    """The fp64 oracle backward (K order) on a bounded sample of the workload:
+    whole (batch 0, head h) slices, added until about budget_s of CPU time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    b = 0
+    q = oracle.bf16_to_f64(data["q"][b:b + 1])
+    k = oracle.bf16_to_f64(data["k"][b:b + 1])
+    v = oracle.bf16_to_f64(data["v"][b:b + 1])
+    do = oracle.bf16_to_f64(data["do"][b:b + 1])
+    if w.mask == "block":
+        pres = data["presence"][b:b + 1]
+        omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
+    elif w.mask == "index":
+        pres = oracle.indices_to_presence(data["indices"][:w.seqlen_q], 1, w.seqlen_q, w.seqlen_k)
+        omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
+    else:
+        omask = oracle.dense_mask()
+    total_flop, total_s, heads = 0, 0.0, []
+    for h in range(min(w.heads_q, max_heads)):
+        O, L = oracle.attn_fwd(q, k, v, omask, w.causal, w.scale, heads=[h])
+        O = oracle.bf16_to_f64(oracle.round_to_bf16(O))
+        L = oracle.round_to_f32(L).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.attn_bwd(q, k, v, O, do, L, omask, w.causal, w.scale, order="K", heads=[h])
+        total_s += time.perf_counter() - t0
+        total_flop += oracle.flop_count(omask, 1, w.heads_q, w.seqlen_q, w.seqlen_k, w.dim_qk, w.dim_v,
+                                        w.causal) // w.heads_q if w.mask == "dense" else \
+            _head_flop(oracle, omask, w, h)
+        heads.append(h)
+        log(f"  cpu baseline: head {h}: {total_s:.1f} s so far")
+        if total_s >= budget_s:
+            break
+    return {
+        "value": total_flop / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle backward (K order) of batch 0, query heads {heads} of "
+                   f"{w.name}: {total_flop / 1e9:.1f} GFLOP in {total_s:.1f} s"),
+    }
+
+
+def _head_flop(oracle, omask, w, h):
+    per_pair = 2 * (3 * w.dim_qk + 2 * w.dim_v)
+    hm = h * omask.heads // w.heads_q
+    n_qb, n_kb = w.n_qb, w.n_kb
+    tot = 0
+    for qb in range(n_qb):
+        r = hm * n_qb + qb
+        kbs = omask.q2k_col[omask.q2k_row_ptr[r]:omask.q2k_row_ptr[r + 1]]
+        last = min((qb + 1) * 128, w.seqlen_q) - 1
+        for kb in kbs:
+            if w.causal and kb * 128 > last + w.seqlen_k - w.seqlen_q:
+                continue
+            tot += (last + 1 - qb * 128) * (min((kb + 1) * 128, w.seqlen_k) - kb * 128) * per_pair
+    return tot
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--algo", default="split", choices=["split", "loopk", "loopq"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the other loop order")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by batch/head with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import index_sparse_attention_amd as isa
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    isa.load_library()
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w.name}: generating inputs")
+    data = synth.make_workload_inputs(w)
+    presence = data.get("presence")
+    idx_presence = None
+    if w.mask == "index":
+        # kept-block count for the FLOP figure comes from the GPU-built CSR below
+        pass
+    dev = torch.device("cuda:0")
+    t = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, do = t(data["q"]), t(data["k"]), t(data["v"]), t(data["do"])
+
+    # mask on the device (once, to size things and count kept blocks)
+    if w.mask == "block":
+        pres_dev = torch.from_numpy(presence).to(dev)
+        mk = lambda: isa.block_mask_to_csr(pres_dev)
+    elif w.mask == "index":
+        idx_dev = torch.from_numpy(data["indices"]).to(dev)
+        mk = lambda: isa.index_to_block_sparse(idx_dev, w.batch, w.seqlen_q, w.seqlen_k)
+    else:
+        mk = lambda: None
+    m0 = mk()
+    if w.mask == "index":
+        qp = m0.q2k_row_ptr.cpu().numpy()
+        qc = m0.q2k_col[:int(qp[-1])].cpu().numpy()
+        idx_presence = np.zeros((w.batch, w.heads_k, w.n_qb, w.n_kb), dtype=np.uint8)
+        rows = np.repeat(np.arange(len(qp) - 1), np.diff(qp))
+        idx_presence.reshape(-1, w.n_kb)[rows, qc] = 1
+    kept = kept_blocks(w, presence, idx_presence)
+    flop = flop_per_step(w, kept)
+    mean_keys = kept * 128.0 / (w.batch * w.heads_q * w.seqlen_q)
+    o_bits, lse_np = synth.stand_in_forward_stats(w, mean_keys)
+    o = t(o_bits)
+    lse = torch.from_numpy(lse_np).to(dev)
+    log(f"kept blocks {kept}, {flop / 1e9:.1f} GFLOP per step")
+
+    def run(algo, steps, warmup):
+        ws = torch.empty(isa.attn_bwd_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_k,
+                                                      w.dim_qk, w.dim_v, algo), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        timer = isa.Timer(capacity=max(steps, 1))
+
+        def step(tm):
+            m = mk()
+            isa.attn_bwd(q, k, v, o, do, lse, mask=m, causal=w.causal, softmax_scale=w.scale, algo=algo,
+                         dq=dq, dk=dk, dv=dv, workspace=ws, timer=tm)
+
+        for _ in range(warmup):
+            step(None)
+        torch.cuda.synchronize()
+        timer.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            step(timer)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = e0.elapsed_time(e1)
+        n, stage = timer.read()
+        timer.close()
+        return {"ms_per_step": ev_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+                "stage_ms": [s / max(n, 1) for s in stage], "n_timed": n}
+
+    log(f"timing {args.algo}: {args.warmup} warmup + {args.steps} steps")
+    r = run(args.algo, args.steps, args.warmup)
+    pairs = kept * 128 * 128
+    value = flop / (r["ms_per_step"] * 1e-3) / 1e12
+    kern = []
+    for name, stage, alg_pp, exe_pp in main_kernels(args.algo, w.dim_qk, w.dim_v):
+        ms = r["stage_ms"][stage]
+        kern.append({"kernel": name, "avg_launch_ms": round(ms, 4),
+                     "algorithmic_tflops": round(pairs * alg_pp / (ms * 1e-3) / 1e12, 3),
+                     "executed_mfma_tflops": round(pairs * exe_pp / (ms * 1e-3) / 1e12, 3)})
+    dom = max(kern, key=lambda k: k["avg_launch_ms"])
+    traffic = load_traffic(f"{dom['kernel']}:{w.name}")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_k": w.heads_k,
+                   "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k, "dim_qk": w.dim_qk, "dim_v": w.dim_v,
+                   "causal": w.causal, "mask": w.mask, "block": 128, "keep_prob": w.keep_prob,
+                   "topk": w.topk, "kept_blocks": kept, "algo": args.algo, "seed": w.seed},
+        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": dom["algorithmic_tflops"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom["algorithmic_tflops"] / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": dom["kernel"], "avg_launch_ms": dom["avg_launch_ms"],
+                     "executed_mfma_tflops": dom["executed_mfma_tflops"]},
+        "kernels": kern,
+        "stages_ms": {"pre": round(r["stage_ms"][0], 4), "main_a": round(r["stage_ms"][1], 4),
+                      "main_b": round(r["stage_ms"][2], 4), "post": round(r["stage_ms"][3], 4)},
+    }
+    rows_q = w.batch * w.seqlen_q * w.heads_q
+    rows_k = w.batch * w.seqlen_k * w.heads_k
+    pre_bytes = rows_q * w.dim_v * 2 * 2 + rows_q * 4
+    post_bytes = 0
+    if args.algo == "loopk":
+        pre_bytes += rows_k * (w.dim_qk + w.dim_v) * 4
+        post_bytes = rows_k * (w.dim_qk + w.dim_v) * (4 + 2)
+    elif args.algo == "loopq":
+        pre_bytes += rows_q * w.dim_qk * 4
+        post_bytes = rows_q * w.dim_qk * (4 + 2)
+    out["prepost_gbs"] = {"pre": round(pre_bytes / (r["stage_ms"][0] * 1e-3) / 1e9, 1),
+                          "post": (round(post_bytes / (r["stage_ms"][3] * 1e-3) / 1e9, 1)
+                                   if post_bytes else None),
+                          "peak": HBM_PEAK_GBS}
+    if not args.no_compare:
+        out["compare"] = []
+        for other in [a for a in ("split", "loopk", "loopq") if a != args.algo]:
+            log(f"timing {other} for comparison")
+            r2 = run(other, max(10, args.steps // 2), 3)
+            out["compare"].append({"algo": other, "ms_per_step": round(r2["ms_per_step"], 4),
+                                   "value": round(flop / (r2["ms_per_step"] * 1e-3) / 1e12, 3),
+                                   "stages_ms": [round(x, 4) for x in r2["stage_ms"]]})
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, data)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

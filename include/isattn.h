@@ -63,7 +63,7 @@ enum { ISATTN_MASK_DENSE = 0, ISATTN_MASK_BLOCK_CSR = 1 };
  * pairs transposed (per key block, its query blocks: the K2Q metadata of [P4]
  * CSR Tile Mapping).  Rows are flattened as ((b * heads + hm) * n_blocks +
  * block); columns ascend within a row; row_ptr[0] == 0.  LoopK reads only
- * q2k_*, LoopQ only k2q_*; the other pair may be NULL.  Inside a kept block
+ * q2k_*, LoopQ only k2q_*, SPLIT both; a pair not read may be NULL.  Inside a kept block
  * every pair is attended.  block_q = block_k = 128; heads is 1, heads_k or
  * heads_q. */
 typedef struct isattn_mask {
@@ -81,13 +81,17 @@ typedef struct isattn_mask {
  * dK/dV are reduced as fp32 atomics into the workspace and converted by a
  * postprocess.  LOOPQ: outer loop over 128-key tiles, inner loop over the
  * query tiles of every head of the GQA group; dK/dV stay on chip and are
- * stored directly, dQ is reduced as fp32 atomics and converted afterwards. */
-enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1 };
+ * stored directly, dQ is reduced as fp32 atomics and converted afterwards.
+ * SPLIT: both loop orders, each restricted to the outputs it keeps on chip --
+ * a LOOPQ pass for dK/dV and a LOOPK pass for dQ -- recomputing P and dS in
+ * each; no atomics and no fp32 accumulators (1.4x the MFMA work at
+ * Dqk = Dv). */
+enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
 
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
- * (fp32 delta [B,Hq,Sq] plus fp32 accumulators: dK,dV [B,Sk,Hk,D] for LOOPK,
- * dQ [B,Sq,Hq,Dqk] for LOOPQ; each part 256-byte aligned).  Returns 0 for a
- * NULL shape or unknown algo. */
+ * (fp32 delta [B,Hq,Sq] plus head-major fp32 accumulators: dK,dV [B,Hk,Sk,D]
+ * for LOOPK, dQ [B,Hq,Sq,Dqk] for LOOPQ, none for SPLIT; each part 256-byte
+ * aligned).  Returns 0 for a NULL shape or unknown algo. */
 size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
 
 /* Attention backward ([P1] Summary and Core changes 1-3): recompute
@@ -102,7 +106,7 @@ size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo
  * mask_desc: see isattn_mask_t; NULL means dense.
  * causal: nonzero adds the bottom-right causal term j <= i + Sk - Sq.
  * dq, dk, dv: bf16 outputs with q/k/v's shapes; overwritten, not accumulated.
- * algo: ISATTN_ALGO_LOOPK or ISATTN_ALGO_LOOPQ.
+ * algo: ISATTN_ALGO_LOOPK, ISATTN_ALGO_LOOPQ or ISATTN_ALGO_SPLIT.
  * workspace: device buffer of at least isattn_attn_bwd_workspace_bytes bytes,
  *   256-byte aligned; its contents on entry do not matter.
  * stream: hipStream_t (NULL = default stream).
@@ -168,11 +172,13 @@ const char* isattn_status_string(isattn_status_t status);
 const char* isattn_version(void);
 
 /* ---- Stage timing (measurement support) -----------------------------------
- * A timer records HIP events on the call's stream around the three launches
- * of isattn_attn_bwd_timed: [0] preprocess, [1] main loop kernel,
- * [2] postprocess.  isattn_timer_read synchronises on the recorded events and
- * returns the number of timed calls and the summed milliseconds per stage.
- * A timer holds `capacity` calls; further calls wrap and overwrite. */
+ * A timer records HIP events on the call's stream around the launches of
+ * isattn_attn_bwd_timed: stage [0] preprocess, [1] first main kernel (LOOPK /
+ * LOOPQ main loop, or the SPLIT dK/dV pass), [2] second main kernel (the SPLIT
+ * dQ pass; empty otherwise), [3] postprocess (empty for SPLIT).
+ * isattn_timer_read synchronises on the recorded events and returns the number
+ * of timed calls and the summed milliseconds per stage (stage_ms[4]).  A timer
+ * holds `capacity` calls; further calls wrap and overwrite. */
 typedef struct isattn_timer isattn_timer_t;
 
 isattn_status_t isattn_timer_create(int32_t capacity, isattn_timer_t** out);

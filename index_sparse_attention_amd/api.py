@@ -14,7 +14,7 @@ import torch
 
 from . import _abi
 
-ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ}
+ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ, "split": _abi.ALGO_SPLIT}
 
 
 def _stream_ptr(stream) -> int:
@@ -61,7 +61,7 @@ class BlockMask:
 
 
 class Timer:
-    """Stage timer of isattn_attn_bwd_timed (preprocess, main, postprocess)."""
+    """Stage timer of isattn_attn_bwd_timed (preprocess, two main kernels, postprocess)."""
 
     def __init__(self, capacity: int = 256):
         lib = _abi.load()
@@ -77,11 +77,11 @@ class Timer:
         _abi.check(_abi.load().isattn_timer_reset(self._h), "isattn_timer_reset")
 
     def read(self):
-        """(n_calls, [pre_ms, main_ms, post_ms] summed over the calls)."""
+        """(n_calls, [pre, main_a, main_b, post] milliseconds summed over the calls)."""
         n = ctypes.c_int32()
-        ms = (ctypes.c_float * 3)()
+        ms = (ctypes.c_float * 4)()
         _abi.check(_abi.load().isattn_timer_read(self._h, ctypes.byref(n), ms), "isattn_timer_read")
-        return n.value, [ms[0], ms[1], ms[2]]
+        return n.value, [ms[0], ms[1], ms[2], ms[3]]
 
     def close(self):
         if getattr(self, "_h", None) is not None:

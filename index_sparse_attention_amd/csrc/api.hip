@@ -13,18 +13,20 @@
 struct isattn_timer {
     int32_t capacity = 0;
     int32_t recorded = 0;      // calls recorded since the last reset (may exceed capacity)
-    std::vector<hipEvent_t> ev;  // 4 per slot
+    std::vector<hipEvent_t> ev;  // kTimerEvents per slot
 };
 
 namespace {
 
 using namespace isattn;
 
+constexpr int kTimerEvents = 5;   // boundaries of the 4 stages
+
 inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 isattn_status_t record(isattn_timer_t* t, int slot, int k, hipStream_t s) {
     if (t == nullptr) return ISATTN_OK;
-    return hipEventRecord(t->ev[size_t(slot) * 4 + k], s) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
+    return hipEventRecord(t->ev[size_t(slot) * kTimerEvents + k], s) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
 }
 
 isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t* q,
@@ -50,11 +52,16 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if ((st = record(timer, slot, 0, s)) != ISATTN_OK) return st;
     if (launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
-    const hipError_t e = algo == ISATTN_ALGO_LOOPK ? launch_loopk(a, s) : launch_loopq(a, s);
+    hipError_t e;
+    if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);
+    else if (algo == ISATTN_ALGO_LOOPQ) e = launch_loopq(a, s);
+    else e = launch_split_dkdv(a, s);
     if (e != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 2, s)) != ISATTN_OK) return st;
-    if (launch_postprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (algo == ISATTN_ALGO_SPLIT && launch_split_dq(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 3, s)) != ISATTN_OK) return st;
+    if (launch_postprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if ((st = record(timer, slot, 4, s)) != ISATTN_OK) return st;
     if (timer != nullptr) timer->recorded++;
     return ISATTN_OK;
 }
@@ -178,7 +185,7 @@ isattn_status_t isattn_timer_create(int32_t capacity, isattn_timer_t** out) {
     isattn_timer_t* t = new (std::nothrow) isattn_timer_t();
     if (t == nullptr) return ISATTN_ERR_HIP;
     t->capacity = capacity;
-    t->ev.assign(size_t(capacity) * 4, nullptr);
+    t->ev.assign(size_t(capacity) * kTimerEvents, nullptr);
     for (auto& e : t->ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
@@ -207,12 +214,12 @@ isattn_status_t isattn_timer_reset(isattn_timer_t* timer) {
 isattn_status_t isattn_timer_read(isattn_timer_t* timer, int32_t* n_calls, float* stage_ms) {
     if (timer == nullptr || n_calls == nullptr || stage_ms == nullptr) return ISATTN_ERR_NULL;
     const int32_t n = timer->recorded < timer->capacity ? timer->recorded : timer->capacity;
-    stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.f;
+    for (int k = 0; k < kTimerEvents - 1; ++k) stage_ms[k] = 0.f;
     *n_calls = n;
     for (int32_t i = 0; i < n; ++i) {
-        hipEvent_t* ev = &timer->ev[size_t(i) * 4];
-        if (hipEventSynchronize(ev[3]) != hipSuccess) return ISATTN_ERR_HIP;
-        for (int k = 0; k < 3; ++k) {
+        hipEvent_t* ev = &timer->ev[size_t(i) * kTimerEvents];
+        if (hipEventSynchronize(ev[kTimerEvents - 1]) != hipSuccess) return ISATTN_ERR_HIP;
+        for (int k = 0; k < kTimerEvents - 1; ++k) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) return ISATTN_ERR_HIP;
             stage_ms[k] += ms;

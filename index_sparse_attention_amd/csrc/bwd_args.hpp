@@ -19,8 +19,8 @@ struct BwdArgs {
     uint16_t* dv; int64_t dv_sb, dv_ss, dv_sh;
     const float* lse;     // [B, Hq, Sq] natural-log LSE
     float* delta;         // [B, Hq, Sq] workspace: rowsum(dO * O)
-    float* acc0;          // LoopK: dK accumulator [B,Sk,Hk,Dqk]; LoopQ: dQ accumulator [B,Sq,Hq,Dqk]
-    float* acc1;          // LoopK: dV accumulator [B,Sk,Hk,Dv]; LoopQ: unused
+    float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
+    float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;
     // block CSR (mask_kind == 1)
     const int32_t* q2k_ptr; const int32_t* q2k_col;

@@ -60,3 +60,153 @@ __device__ __forceinline__ u32x4_t gload128(const uint16_t* p) {
 }
 
 }  // namespace isattn
+
+namespace isattn {
+
+// Swap bits 2 and 3 of a row index.  Staging tile row r at LDS row
+// swap23(r) makes the 32x32 MFMA accumulator registers 8c..8c+7 of lane
+// half h hold logical rows 16c + 8h + 0..7 -- eight consecutive rows, so the
+// accumulator can feed the next MFMA as an operand whose partner operand is
+// read as contiguous runs.
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte runs addressed by lanes 4s + i/4, s = 0..3.  Pointing
+// lane L of a group at row (r0 + L/4), column (c0 + 4*(L%4)) of a row-major
+// bf16 tile returns, in lane i, rows r0..r0+3 of column c0 + i: four
+// consecutive k of one MFMA B-operand column.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+}  // namespace isattn
+
+namespace isattn {
+
+// Cooperative copy of ROWS rows x D bf16 of a [seq, D] slice (row stride in
+// elements) into LDS with row pitch PITCH.  All of a thread's 16-byte global
+// loads are issued before any LDS store, so their latencies overlap; load()
+// and store() can be split around other work to prefetch the next tile.
+// Rows at or past `limit` read as zeros.  With PERM, tile row r lands at LDS
+// row swap23(r).
+template <int D, int PITCH, int ROWS, int NT, bool PERM>
+struct TileStager {
+    static constexpr int CH = D / 8;               // 16-byte chunks per row
+    static constexpr int N = ROWS * CH / NT;       // chunks per thread
+    static_assert((ROWS * CH) % NT == 0, "tile must split evenly over the threads");
+    u32x4_t v[N];
+
+    __device__ __forceinline__ void load(const uint16_t* src, int64_t row_stride, int row0, int limit,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            const int r = u / CH;
+            const int c = u - r * CH;
+            const int gr = row0 + r;
+            v[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (gr < limit) v[i] = gload128(src + gr * row_stride + 8 * c);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            const int r = u / CH;
+            const int c = u - r * CH;
+            const int lr = PERM ? swap23(r) : r;
+            *reinterpret_cast<u32x4_t*>(dst + lr * PITCH + 8 * c) = v[i];
+        }
+    }
+    // Transposed copy: element (r, d) to dstT[d * PT + r].
+    template <int PT>
+    __device__ __forceinline__ void store_t(uint16_t* dstT, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            const int r = u / CH;
+            const int c = u - r * CH;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dstT[(8 * c + 2 * j) * PT + r] = uint16_t(v[i][j] & 0xffffu);
+                dstT[(8 * c + 2 * j + 1) * PT + r] = uint16_t(v[i][j] >> 16);
+            }
+        }
+    }
+};
+
+}  // namespace isattn
+
+namespace isattn {
+
+// ---- swizzled LDS tiles filled by direct global->LDS loads -----------------
+// A tile of ROWS x D bf16 is stored unpadded (row r at element r * D); its
+// 16-byte chunk c sits at chunk position c ^ chunk_swz(r).  With this XOR the
+// 8 rows read by one 128-byte ds_read_b128 phase hit 8 different bank groups,
+// and so do the 4 rows x 2 chunks of a 16-lane ds_read_b64_tr_b16 phase that
+// starts at a row multiple of 4.
+__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int elem) {
+    return r * D + ((((elem >> 3) ^ chunk_swz(r)) << 3) | (elem & 7));
+}
+
+// Async copy of tile rows [row0, row0 + ROWS) of a [seq, D] slice into a
+// swizzled LDS tile, tile row t landing at LDS row swap23(t).  Each wave issues
+// 1 KiB direct-to-LDS loads (global_load_lds_dwordx4: lane L's 16 bytes go to
+// the instruction's LDS base + 16 * L).  Rows at or past `limit` are clamped
+// to limit - 1 (in-bounds data that the caller masks out); limit must be > 0.
+// Returns nothing; completion is tracked by vmcnt.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_async(uint16_t* tile, const uint16_t* src, int64_t row_stride,
+                                                int row0, int limit, int wave, int lane) {
+    constexpr int NI = ROWS * D * 2 / 1024;        // 1 KiB instructions per tile
+    static_assert((ROWS * D * 2) % 1024 == 0 && NI % NW == 0, "tile must split into whole wave loads");
+#pragma unroll
+    for (int k = 0; k < NI / NW; ++k) {
+        const int j = wave + k * NW;
+        const int e = 512 * j + 8 * lane;          // element offset this lane fills
+        const int r = e / D;
+        const int p = (e - r * D) >> 3;
+        const int c = p ^ chunk_swz(r);
+        const int gr = min(row0 + swap23(r), limit - 1);
+        __builtin_amdgcn_global_load_lds(src + gr * row_stride + 8 * c,
+                                         (__attribute__((address_space(3))) void*)(tile + 512 * j), 16, 0, 0);
+    }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n outstanding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// B operand of a 32x32x16 MFMA from a swizzled, swap23-staged tile: logical
+// rows 16*cc + 8*h + 0..7 of the 32-row group at `row32`, column col0 + lane%32.
+template <int D>
+__device__ __forceinline__ bf16x8_t b_operand_tr_swz(const uint16_t* tile, int row32, int cc, int col0,
+                                                     int lane) {
+    const int L = lane & 15;
+    const int g = lane >> 4;
+    const int h = g >> 1;
+    const int row = row32 + 16 * cc + 4 * h + (L >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (L & 3);
+    const u32x2_t lo = lds_read_tr16(tile + swz_off<D>(row, col));
+    const u32x2_t hi = lds_read_tr16(tile + swz_off<D>(row + 8, col));
+    const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+    return as_bf16x8(v);
+}
+
+// A operand (or B operand of the non-transposed kind) of a 32x32x16 MFMA:
+// 8 consecutive elements of LDS row `row` starting at a multiple of 8.
+template <int D>
+__device__ __forceinline__ bf16x8_t row_operand_swz(const uint16_t* tile, int row, int col) {
+    return as_bf16x8(lds_read128(tile + swz_off<D>(row, col)));
+}
+
+}  // namespace isattn

@@ -14,6 +14,9 @@ hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s);
 // Main loops.
 hipError_t launch_loopk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_loopq(const BwdArgs& a, hipStream_t s);
+// Atomic-free two-pass backward: dK/dV pass (key-outer), dQ pass (query-outer).
+hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);
+hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
 hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,

@@ -64,38 +64,23 @@ struct LoopKCfg {
 };
 
 // Rows [row0, row0 + ROWS) of a [seq, dim] slice into LDS (pitch PITCH), zeros past `limit`.
+// Rows [row0, row0 + ROWS) of a [seq, D] slice into LDS (pitch PITCH), zeros past `limit`.
 template <int D, int PITCH, int ROWS, int NT>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t row_stride,
                                            int row0, int limit, int tid) {
-    constexpr int CH = D / 8;
-    for (int u = tid; u < ROWS * CH; u += NT) {
-        const int r = u / CH;
-        const int c = u - r * CH;
-        const int gr = row0 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
-        *reinterpret_cast<u32x4_t*>(dst + r * PITCH + 8 * c) = v;
-    }
+    TileStager<D, PITCH, ROWS, NT, false> t;
+    t.load(src, row_stride, row0, limit, tid);
+    t.store(dst, tid);
 }
 
 // 64 keys of K: row-major copy (pitch PK) and transposed copy (pitch PKT).
 template <int D, int PK, int PKT, int NT>
 __device__ __forceinline__ void stage_k(uint16_t* sK, uint16_t* sKt, const uint16_t* src,
                                         int64_t row_stride, int row0, int limit, int tid) {
-    constexpr int CH = D / 8;
-    for (int u = tid; u < 64 * CH; u += NT) {
-        const int r = u / CH;
-        const int c = u - r * CH;
-        const int gr = row0 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
-        *reinterpret_cast<u32x4_t*>(sK + r * PK + 8 * c) = v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sKt[(8 * c + 2 * j) * PKT + r] = uint16_t(v[j] & 0xffffu);
-            sKt[(8 * c + 2 * j + 1) * PKT + r] = uint16_t(v[j] >> 16);
-        }
-    }
+    TileStager<D, PK, 64, NT, false> t;
+    t.load(src, row_stride, row0, limit, tid);
+    t.store(sK, tid);
+    t.template store_t<PKT>(sKt, tid);
 }
 
 template <int DQK, int DV>
@@ -204,9 +189,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopk(BwdArgs a) {
     uint16_t* sdS = lds + C::OFF_DS;
     const uint16_t* gk = a.k + b * a.k_sb + hk * a.k_sh;
     const uint16_t* gv = a.v + b * a.v_sb + hk * a.v_sh;
-    const int64_t acc_row = int64_t(a.Hk);      // accumulators are contiguous [B, Sk, Hk, D]
-    float* gdk = a.acc0 + (int64_t(b) * a.Sk * a.Hk + hk) * DQK;
-    float* gdv = a.acc1 + (int64_t(b) * a.Sk * a.Hk + hk) * DV;
+    // fp32 accumulators are head-major [B, Hk, Sk, D]: the keys of one step are
+    // contiguous, so a step's atomics spread over all L2 channels
+    float* gdk = a.acc0 + (int64_t(b) * a.Hk + hk) * a.Sk * DQK;
+    float* gdv = a.acc1 + (int64_t(b) * a.Hk + hk) * a.Sk * DV;
 
     for (int it = 0; it < kb_count; ++it) {
         const int kb = kb_list ? kb_list[it] : it;
@@ -300,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopk(BwdArgs a) {
                     const int d = w * C::WV + 16 * t + l16;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (key0 + i < a.Sk) atomic_add_f32(gdv + int64_t(key0 + i) * acc_row * DV + d, acc[i]);
+                        if (key0 + i < a.Sk) atomic_add_f32(gdv + int64_t(key0 + i) * DV + d, acc[i]);
                 }
 #pragma unroll
                 for (int t = 0; t < C::NTK; ++t) {
@@ -310,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopk(BwdArgs a) {
                     const int d = w * C::WQK + 16 * t + l16;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (key0 + i < a.Sk) atomic_add_f32(gdk + int64_t(key0 + i) * acc_row * DQK + d, acc[i]);
+                        if (key0 + i < a.Sk) atomic_add_f32(gdk + int64_t(key0 + i) * DQK + d, acc[i]);
                 }
             }
             __syncthreads();

@@ -62,35 +62,19 @@ struct LoopQCfg {
 template <int D, int PITCH, int ROWS, int NT>
 __device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t row_stride,
                                            int row0, int limit, int tid) {
-    constexpr int CH = D / 8;
-    for (int u = tid; u < ROWS * CH; u += NT) {
-        const int r = u / CH;
-        const int c = u - r * CH;
-        const int gr = row0 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
-        *reinterpret_cast<u32x4_t*>(dst + r * PITCH + 8 * c) = v;
-    }
+    TileStager<D, PITCH, ROWS, NT, false> t;
+    t.load(src, row_stride, row0, limit, tid);
+    t.store(dst, tid);
 }
 
 // ROWS rows: row-major copy (pitch P) and transposed copy (pitch PT).
 template <int D, int P, int PT, int ROWS, int NT>
 __device__ __forceinline__ void stage_both(uint16_t* dst, uint16_t* dstT, const uint16_t* src,
                                            int64_t row_stride, int row0, int limit, int tid) {
-    constexpr int CH = D / 8;
-    for (int u = tid; u < ROWS * CH; u += NT) {
-        const int r = u / CH;
-        const int c = u - r * CH;
-        const int gr = row0 + r;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (gr < limit) v = gload128(src + gr * row_stride + 8 * c);
-        *reinterpret_cast<u32x4_t*>(dst + r * P + 8 * c) = v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dstT[(8 * c + 2 * j) * PT + r] = uint16_t(v[j] & 0xffffu);
-            dstT[(8 * c + 2 * j + 1) * PT + r] = uint16_t(v[j] >> 16);
-        }
-    }
+    TileStager<D, P, ROWS, NT, false> t;
+    t.load(src, row_stride, row0, limit, tid);
+    t.store(dst, tid);
+    t.template store_t<PT>(dstT, tid);
 }
 
 template <int DQK, int DV>
@@ -184,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
         const uint16_t* gq = a.q + b * a.q_sb + h * a.q_sh;
         const uint16_t* gdo = a.dO + b * a.do_sb + h * a.do_sh;
         const int64_t srow = (int64_t(b) * a.Hq + h) * a.Sq;
-        float* gdq = a.acc0 + (int64_t(b) * a.Sq * a.Hq + h) * DQK;   // + row * Hq * DQK + d
+        float* gdq = a.acc0 + (int64_t(b) * a.Hq + h) * a.Sq * DQK;   // head-major [B, Hq, Sq, Dqk]
 
         for (int it = 0; it < qb_count; ++it) {
             const int qb = qb_list ? qb_list[it] : qb_first + it;
@@ -290,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (row0 + i < a.Sq)
-                                atomic_add_f32(gdq + int64_t(row0 + i) * a.Hq * DQK + d, acc[i]);
+                                atomic_add_f32(gdq + int64_t(row0 + i) * DQK + d, acc[i]);
                     }
                 }
                 __syncthreads();

@@ -68,10 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_postprocess(const float* __restric
     const int64_t row = u / L;
     const int sub = int(u % L);
     if (row >= rows) return;
-    const int64_t h = row % H;
-    const int64_t t = row / H;
-    const int64_t s = t % S;
-    const int64_t b = t / S;
+    const int64_t s = row % S;          // accumulator rows are head-major (b, h, s)
+    const int64_t t = row / S;
+    const int64_t h = t % H;
+    const int64_t b = t / H;
     const float4* src = reinterpret_cast<const float4*>(acc + row * D + 8 * sub);
     const float4 x = src[0];
     const float4 y = src[1];
@@ -132,6 +132,7 @@ hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s) {
 }
 
 hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s) {
+    if (algo == 2) return hipSuccess;           // SPLIT stores bf16 outputs directly
     if (algo == 0) {
         hipError_t e = post_dispatch(a.Dqk, a.acc0, a.dk, a.dk_sb, a.dk_ss, a.dk_sh, a.B, a.Sk, a.Hk,
                                      a.scale, s);

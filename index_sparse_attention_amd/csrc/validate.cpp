@@ -45,7 +45,7 @@ void copy_view_out(const isattn_tensor_t* t, uint16_t** p, int64_t* sb, int64_t*
 bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
         return false;
-    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ) return false;
+    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT) return false;
     BwdPlan p{};
     p.n_qb = cdiv(s.seqlen_q, kBlock);
     p.n_kb = cdiv(s.seqlen_k, kBlock);
@@ -58,8 +58,11 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     if (algo == ISATTN_ALGO_LOOPK) {
         p.acc0_elems = rows_k * s.dim_qk;
         p.acc1_elems = rows_k * s.dim_v;
-    } else {
+    } else if (algo == ISATTN_ALGO_LOOPQ) {
         p.acc0_elems = rows_q * s.dim_qk;
+        p.acc1_elems = 0;
+    } else {
+        p.acc0_elems = 0;
         p.acc1_elems = 0;
     }
     p.off_acc0 = off;
@@ -89,7 +92,8 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         int64_t(s.batch) * s.heads_k * cdiv(s.seqlen_k, kBlock) >= (int64_t(1) << 31))
         return ISATTN_ERR_SHAPE;
     if (!supported_dims(s.dim_qk, s.dim_v)) return ISATTN_ERR_UNSUPPORTED;
-    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ) return ISATTN_ERR_UNSUPPORTED;
+    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT)
+        return ISATTN_ERR_UNSUPPORTED;
     if (!std::isfinite(softmax_scale)) return ISATTN_ERR_UNSUPPORTED;
 
     const int64_t nq = int64_t(s.batch) * s.seqlen_q * s.heads_q;
@@ -113,9 +117,9 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         if (mask->block_q != kBlock || mask->block_k != kBlock) return ISATTN_ERR_UNSUPPORTED;
         if (mask->heads != 1 && mask->heads != s.heads_k && mask->heads != s.heads_q)
             return ISATTN_ERR_MASK;
-        if (algo == ISATTN_ALGO_LOOPK && (mask->q2k_row_ptr == nullptr || mask->q2k_col == nullptr))
+        if (algo != ISATTN_ALGO_LOOPQ && (mask->q2k_row_ptr == nullptr || mask->q2k_col == nullptr))
             return ISATTN_ERR_NULL;
-        if (algo == ISATTN_ALGO_LOOPQ && (mask->k2q_row_ptr == nullptr || mask->k2q_col == nullptr))
+        if (algo != ISATTN_ALGO_LOOPK && (mask->k2q_row_ptr == nullptr || mask->k2q_col == nullptr))
             return ISATTN_ERR_NULL;
         a.mask_kind = ISATTN_MASK_BLOCK_CSR;
         a.Hm = mask->heads;

@@ -57,6 +57,7 @@ def test_workspace_sizes(lib):
     delta = al(2 * 300 * 4 * 4)
     assert ws_bytes(lib, s, 0) == delta + al(2 * 200 * 2 * 128 * 4) * 2
     assert ws_bytes(lib, s, 1) == delta + al(2 * 300 * 4 * 128 * 4)
+    assert ws_bytes(lib, s, 2) == delta
     assert ws_bytes(lib, s, 7) == 0
     assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
     # converter: presence B*H*nQB*nKB bytes + row and column counts

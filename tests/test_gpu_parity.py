@@ -38,7 +38,7 @@ def get_case(name):
     return _built[name]
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_attn_bwd_parity(name, algo):
     c = get_case(name)
@@ -54,18 +54,20 @@ def test_attn_bwd_parity(name, algo):
 
 
 @pytest.mark.parametrize("name", ["causal_gqa_br_d128", "block_h1_gqa_causal", "index_gqa_d128", "causal_d192"])
-def test_loopk_matches_loopq(name):
-    """The two loop orders agree within the tolerance (fp32 atomic order differs)."""
+def test_loop_orders_agree(name):
+    """LoopK, LoopQ and the split passes agree within the tolerance (fp32
+    accumulation order differs between them)."""
     c = get_case(name)
-    log(f"loopk vs loopq {name}")
+    log(f"loopk vs loopq vs split {name}")
     mask = gpu_mask(c)
     a = run_gpu(c, "loopk", mask)
-    b = run_gpu(c, "loopq", mask)
-    for n, x, y in zip(("dq", "dk", "dv"), a, b):
-        assert_close(n + " loopk-vs-loopq", x, y)
+    for other in ("loopq", "split"):
+        b = run_gpu(c, other, mask)
+        for n, x, y in zip(("dq", "dk", "dv"), a, b):
+            assert_close(f"{n} loopk-vs-{other}", x, y)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
 def test_dense_equals_all_kept_blocks(algo):
     """Dense mask and an all-kept block mask give the same gradients."""
     import torch
@@ -79,7 +81,7 @@ def test_dense_equals_all_kept_blocks(algo):
         assert_close(n + " dense-vs-allkept", x, y)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
 def test_poisoned_workspace(algo):
     """A workspace full of NaN bytes on entry does not leak into the results."""
     c = get_case("causal_gqa_br_d128")
@@ -91,7 +93,7 @@ def test_poisoned_workspace(algo):
     assert_close("dv", dv, rv)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
 def test_empty_sequences(algo):
     """Sq = 0 gives zero dK/dV; Sk = 0 gives zero dQ; B = 0 is a no-op."""
     import torch
