@@ -173,14 +173,19 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
     bf16x8_t dsa[C::QT][2];                        // packed dS of the previous step
     auto dq_update = [&](int stage_i) {
         const uint16_t* sK = lds + stage_i * C::STAGE;
+        constexpr int NF = 2 * C::NDT;             // B fragments, f = cc * NDT + dt
+        constexpr int PF = NF < 3 ? NF : 3;        // prefetch depth
+        bf16x8_t fr[PF + 1];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+        for (int f = 0; f < PF; ++f) fr[f] = b_operand_tr_swz<DQK>(sK, 0, f / C::NDT, 32 * (f % C::NDT), lane);
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
-                const bf16x8_t kbv = b_operand_tr_swz<DQK>(sK, 0, cc, 32 * dt, lane);
+        for (int f = 0; f < NF; ++f) {
+            if (f + PF < NF)
+                fr[(f + PF) % (PF + 1)] = b_operand_tr_swz<DQK>(sK, 0, (f + PF) / C::NDT, 32 * ((f + PF) % C::NDT), lane);
+            const int cc = f / C::NDT, dt = f % C::NDT;
 #pragma unroll
-                for (int qt = 0; qt < C::QT; ++qt) dq[qt][dt] = mfma32(dsa[qt][cc], kbv, dq[qt][dt]);
-            }
+            for (int qt = 0; qt < C::QT; ++qt) dq[qt][dt] = mfma32(dsa[qt][cc], fr[f % (PF + 1)], dq[qt][dt]);
+        }
     };
 
     int n0 = -1;
@@ -206,18 +211,22 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
             dpt[qt] = f32x16_t{};
         }
         {
-            bf16x8_t ka[2], va[2];
-            ka[0] = row_operand_swz<DQK>(sK, l32, 8 * h2);
-            va[0] = row_operand_swz<DV>(sV, l32, 8 * h2);
+            constexpr int PF = 2;                  // prefetch depth (chunks)
+            bf16x8_t ka[PF + 1], va[PF + 1];
+#pragma unroll
+            for (int c = 0; c < PF; ++c) {
+                ka[c] = row_operand_swz<DQK>(sK, l32, 16 * c + 8 * h2);
+                if (c < C::NCV) va[c] = row_operand_swz<DV>(sV, l32, 16 * c + 8 * h2);
+            }
 #pragma unroll
             for (int c = 0; c < C::NCQ; ++c) {
-                if (c + 1 < C::NCQ) ka[(c + 1) & 1] = row_operand_swz<DQK>(sK, l32, 16 * (c + 1) + 8 * h2);
-                if (c + 1 < C::NCV) va[(c + 1) & 1] = row_operand_swz<DV>(sV, l32, 16 * (c + 1) + 8 * h2);
+                if (c + PF < C::NCQ) ka[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sK, l32, 16 * (c + PF) + 8 * h2);
+                if (c + PF < C::NCV) va[(c + PF) % (PF + 1)] = row_operand_swz<DV>(sV, l32, 16 * (c + PF) + 8 * h2);
 #pragma unroll
-                for (int qt = 0; qt < C::QT; ++qt) st[qt] = mfma32(ka[c & 1], qB[qt][c], st[qt]);
+                for (int qt = 0; qt < C::QT; ++qt) st[qt] = mfma32(ka[c % (PF + 1)], qB[qt][c], st[qt]);
                 if (c < C::NCV) {
 #pragma unroll
-                    for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c & 1], doB[qt][c], dpt[qt]);
+                    for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c % (PF + 1)], doB[qt][c], dpt[qt]);
                 }
             }
         }
@@ -406,17 +415,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     auto dkv_update = [&](int stage_i) {
         const uint16_t* sQ = lds + stage_i * C::STAGE;
         const uint16_t* sdO = sQ + C::BM * DQK;
+        // MFMA f: group g = f / (NDV + NDK) = (mt, cc); within it dV tiles first, then dK tiles
+        constexpr int PG = C::NDV + C::NDK;
+        constexpr int NF = 4 * PG;
+        constexpr int PF = 4;                      // prefetch depth (fragments)
+        auto frag = [&](int f) -> bf16x8_t {
+            const int g = f / PG, j = f % PG;
+            const int mt = g >> 1, cc = g & 1;
+            return j < C::NDV ? b_operand_tr_swz<DV>(sdO, 32 * mt, cc, 32 * j, lane)
+                              : b_operand_tr_swz<DQK>(sQ, 32 * mt, cc, 32 * (j - C::NDV), lane);
+        };
+        bf16x8_t fr[PF + 1];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int f = 0; f < PF; ++f) fr[f] = frag(f);
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-                for (int dt = 0; dt < C::NDV; ++dt)
-                    dv[dt] = mfma32(pa[mt][cc], b_operand_tr_swz<DV>(sdO, 32 * mt, cc, 32 * dt, lane), dv[dt]);
-#pragma unroll
-                for (int dt = 0; dt < C::NDK; ++dt)
-                    dk[dt] = mfma32(sa[mt][cc], b_operand_tr_swz<DQK>(sQ, 32 * mt, cc, 32 * dt, lane), dk[dt]);
-            }
+        for (int f = 0; f < NF; ++f) {
+            if (f + PF < NF) fr[(f + PF) % (PF + 1)] = frag(f + PF);
+            const int g = f / PG, j = f % PG;
+            const int mt = g >> 1, cc = g & 1;
+            if (j < C::NDV) dv[j] = mfma32(pa[mt][cc], fr[f % (PF + 1)], dv[j]);
+            else dk[j - C::NDV] = mfma32(sa[mt][cc], fr[f % (PF + 1)], dk[j - C::NDV]);
+        }
     };
 
     load_head();
@@ -448,24 +467,29 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
         f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
         f32x16_t dp[2] = {f32x16_t{}, f32x16_t{}};
         {
-            bf16x8_t qa[2][2], oa[2][2];
+            constexpr int PF = 2;                  // prefetch depth (chunks)
+            bf16x8_t qa[PF + 1][2], oa[PF + 1][2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                qa[0][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 8 * h2);
-                oa[0][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 8 * h2);
-            }
+            for (int c = 0; c < PF; ++c)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    qa[c][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 16 * c + 8 * h2);
+                    if (c < C::NCV) oa[c][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 16 * c + 8 * h2);
+                }
 #pragma unroll
             for (int c = 0; c < C::NCQ; ++c) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    if (c + 1 < C::NCQ) qa[(c + 1) & 1][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 16 * (c + 1) + 8 * h2);
-                    if (c + 1 < C::NCV) oa[(c + 1) & 1][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 16 * (c + 1) + 8 * h2);
+                    if (c + PF < C::NCQ)
+                        qa[(c + PF) % (PF + 1)][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 16 * (c + PF) + 8 * h2);
+                    if (c + PF < C::NCV)
+                        oa[(c + PF) % (PF + 1)][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 16 * (c + PF) + 8 * h2);
                 }
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(qa[c & 1][mt], kB[c], s[mt]);
+                for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(qa[c % (PF + 1)][mt], kB[c], s[mt]);
                 if (c < C::NCV) {
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) dp[mt] = mfma32(oa[c & 1][mt], vB[c], dp[mt]);
+                    for (int mt = 0; mt < 2; ++mt) dp[mt] = mfma32(oa[c % (PF + 1)][mt], vB[c], dp[mt]);
                 }
             }
         }
