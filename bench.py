@@ -100,62 +100,70 @@ def load_traffic(kernel_key):
         return None
 
 
-def cpu_baseline(w, data, budget_s=15.0, max_heads=16):
+def cpu_baseline(w, data, budget_s=20.0, max_slices=64):
     """The fp64 oracle backward (K order) on a bounded sample of the workload:
-    whole (batch 0, head h) slices, added until about budget_s of CPU time."""
+    whole (batch b, query head h) slices, in order, added until about budget_s
+    of CPU time (or max_slices)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    b = 0
-    q = oracle.bf16_to_f64(data["q"][b:b + 1])
-    k = oracle.bf16_to_f64(data["k"][b:b + 1])
-    v = oracle.bf16_to_f64(data["v"][b:b + 1])
-    do = oracle.bf16_to_f64(data["do"][b:b + 1])
-    if w.mask == "block":
-        pres = data["presence"][b:b + 1]
-        omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
-    elif w.mask == "index":
-        pres = oracle.indices_to_presence(data["indices"][:w.seqlen_q], 1, w.seqlen_q, w.seqlen_k)
-        omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
-    else:
-        omask = oracle.dense_mask()
-    total_flop, total_s, heads = 0, 0.0, []
-    for h in range(min(w.heads_q, max_heads)):
-        O, L = oracle.attn_fwd(q, k, v, omask, w.causal, w.scale, heads=[h])
-        O = oracle.bf16_to_f64(oracle.round_to_bf16(O))
-        L = oracle.round_to_f32(L).astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.attn_bwd(q, k, v, O, do, L, omask, w.causal, w.scale, order="K", heads=[h])
-        total_s += time.perf_counter() - t0
-        total_flop += oracle.flop_count(omask, 1, w.heads_q, w.seqlen_q, w.seqlen_k, w.dim_qk, w.dim_v,
-                                        w.causal) // w.heads_q if w.mask == "dense" else \
-            _head_flop(oracle, omask, w, h)
-        heads.append(h)
-        log(f"  cpu baseline: head {h}: {total_s:.1f} s so far")
-        if total_s >= budget_s:
+    total_flop, total_s, slices = 0, 0.0, []
+    for b in range(w.batch):
+        q = oracle.bf16_to_f64(data["q"][b:b + 1])
+        k = oracle.bf16_to_f64(data["k"][b:b + 1])
+        v = oracle.bf16_to_f64(data["v"][b:b + 1])
+        do = oracle.bf16_to_f64(data["do"][b:b + 1])
+        if w.mask == "block":
+            pres = data["presence"][b:b + 1]
+            omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
+        elif w.mask == "index":
+            rows = data["indices"][b * w.seqlen_q:(b + 1) * w.seqlen_q]
+            pres = oracle.indices_to_presence(rows, 1, w.seqlen_q, w.seqlen_k)
+            omask = oracle.block_mask_from_csr(pres.shape[1], *oracle.presence_to_csr(pres))
+        else:
+            omask = oracle.dense_mask()
+        for h in range(w.heads_q):
+            O, L = oracle.attn_fwd(q, k, v, omask, w.causal, w.scale, heads=[h])
+            O = oracle.bf16_to_f64(oracle.round_to_bf16(O))
+            L = oracle.round_to_f32(L).astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.attn_bwd(q, k, v, O, do, L, omask, w.causal, w.scale, order="K", heads=[h])
+            total_s += time.perf_counter() - t0
+            total_flop += _head_flop(omask, w, h)
+            slices.append((b, h))
+            log(f"  cpu baseline: batch {b} head {h}: {total_s:.1f} s so far")
+            if total_s >= budget_s or len(slices) >= max_slices:
+                break
+        if total_s >= budget_s or len(slices) >= max_slices:
             break
     return {
         "value": total_flop / total_s / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle backward (K order) of batch 0, query heads {heads} of "
-                   f"{w.name}: {total_flop / 1e9:.1f} GFLOP in {total_s:.1f} s"),
+        "sample": (f"fp64 NumPy oracle backward (K order) of {len(slices)} whole (batch, query head) "
+                   f"slices of {w.name}, first {slices[0]} .. last {slices[-1]}: "
+                   f"{total_flop / 1e9:.1f} GFLOP in {total_s:.1f} s"),
     }
 
 
-def _head_flop(oracle, omask, w, h):
+def _head_flop(omask, w, h):
+    """FLOP of one (batch, query head) slice over its computed blocks, with the
+    convention of the GPU figure (whole 128x128 blocks, ragged edges cut)."""
     per_pair = 2 * (3 * w.dim_qk + 2 * w.dim_v)
-    hm = h * omask.heads // w.heads_q
     n_qb, n_kb = w.n_qb, w.n_kb
     tot = 0
     for qb in range(n_qb):
-        r = hm * n_qb + qb
-        kbs = omask.q2k_col[omask.q2k_row_ptr[r]:omask.q2k_row_ptr[r + 1]]
         last = min((qb + 1) * 128, w.seqlen_q) - 1
+        if omask.kind == "dense":
+            kbs = range(n_kb)
+        else:
+            hm = h * omask.heads // w.heads_q
+            r = hm * n_qb + qb
+            kbs = omask.q2k_col[omask.q2k_row_ptr[r]:omask.q2k_row_ptr[r + 1]]
         for kb in kbs:
             if w.causal and kb * 128 > last + w.seqlen_k - w.seqlen_q:
                 continue
