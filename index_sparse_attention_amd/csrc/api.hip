@@ -43,6 +43,7 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if (st != ISATTN_OK) return st;
     if (a.B == 0) return ISATTN_OK;
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
+    a.lse2 = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
     a.acc0 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc0));
     a.acc1 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc1));
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -18,7 +18,8 @@ struct BwdArgs {
     uint16_t* dk; int64_t dk_sb, dk_ss, dk_sh;
     uint16_t* dv; int64_t dv_sb, dv_ss, dv_sh;
     const float* lse;     // [B, Hq, Sq] natural-log LSE
-    float* delta;         // [B, Hq, Sq] workspace: rowsum(dO * O)
+    float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O)
+    float* lse2;          // [B, Hq, stat_ld] workspace (SPLIT only): lse * log2(e); else null
     float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
     float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;
@@ -27,6 +28,8 @@ struct BwdArgs {
     const int32_t* k2q_ptr; const int32_t* k2q_col;
     int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
     int32_t Hm, n_qb, n_kb;
+    int32_t stat_ld;      // row stride of delta / lse2 per (b, h): Sq, or n_qb * 128 for SPLIT
+                          // (rows Sq.. hold delta = 0, lse2 = +inf)
     int32_t mask_kind, causal;
     float scale;          // softmax_scale
     float scale_log2;     // softmax_scale * log2(e)

@@ -14,6 +14,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 // D = A(32x16) * B(16x32) + C, fp32 accumulate.  Lane l: A row l%32 and B
 // column l%32, eight k-slots 8*(l/32)..+7; C/D register i holds row
 // 8*(i/4) + 4*(l/32) + i%4 of column l%32.
@@ -177,6 +179,36 @@ __device__ __forceinline__ void load_tile_async(uint16_t* tile, const uint16_t* 
         __builtin_amdgcn_global_load_lds(src + gr * row_stride + 8 * c,
                                          (__attribute__((address_space(3))) void*)(tile + 512 * j), 16, 0, 0);
     }
+}
+
+// Direct global->LDS copies issued as inline assembly: lane L reads the bytes
+// at base + off (base a wave-uniform pointer, off a per-lane byte offset) and
+// they land at LDS byte address lds + 16 * L (dwordx4) or lds + 4 * L (dword).
+// The compiler does not track these loads, so it never delays LDS reads of
+// other buffers behind them; the caller makes a tile visible with
+// wait_vmcnt<0>() and a workgroup barrier before reading it.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return uint32_t(uintptr_t((__attribute__((address_space(3))) const void*)(p)));
+}
+// A wave-uniform value that the compiler may hold in a VGPR, moved to SGPRs
+// (the base address and LDS address operands below must be scalar).
+__device__ __forceinline__ const void* scalar_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base))
+                 : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (<= n outstanding).

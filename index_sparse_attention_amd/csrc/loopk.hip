@@ -29,7 +29,6 @@
 namespace isattn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DQK, int DV>
 struct LoopKCfg {

@@ -1,7 +1,8 @@
 // Preprocess and postprocess of the attention backward.
 //
 // Preprocess: delta[b, h, i] = sum_d dO[b,i,h,d] * O[b,i,h,d] (fp32 sum of
-// exact bf16 products), plus zeroing of the fp32 accumulators the main loop
+// exact bf16 products); for SPLIT also lse2 = lse * log2(e), the form the
+// dK/dV pass copies straight into LDS; plus zeroing of the fp32 accumulators the main loop
 // reduces into (dK/dV for LoopK, dQ for LoopQ).  The zeroing is a plain fill
 // kernel, not a memset node, so the whole call can be graph-captured.
 //
@@ -26,16 +27,17 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
     constexpr int L = DV / 8;          // lanes per row, 8 bf16 each
     constexpr int RPB = kThreads / L;  // rows per block
     if (int32_t(blockIdx.x) < nblk_delta) {
-        const int64_t rows = int64_t(a.B) * a.Sq * a.Hq;
+        // rows (b, h, i) of the statistics arrays, i fastest (memory order);
+        // rows i >= Sq are padding: delta = 0, lse2 = +inf
+        const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
         const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / L;
         const int sub = threadIdx.x % L;
         float acc = 0.f;
-        int64_t b = 0, i = 0, h = 0;
-        if (row < rows) {
-            h = row % a.Hq;
-            const int64_t t = row / a.Hq;
-            i = t % a.Sq;
-            b = t / a.Sq;
+        const int64_t i = row % a.stat_ld;
+        const int64_t bh = row / a.stat_ld;
+        if (row < rows && i < a.Sq) {
+            const int64_t h = bh % a.Hq;
+            const int64_t b = bh / a.Hq;
             const u32x4_t o = gload128(a.o + b * a.o_sb + i * a.o_ss + h * a.o_sh + 8 * sub);
             const u32x4_t g = gload128(a.dO + b * a.do_sb + i * a.do_ss + h * a.do_sh + 8 * sub);
 #pragma unroll
@@ -46,7 +48,10 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
         }
 #pragma unroll
         for (int o = L / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (row < rows && sub == 0) a.delta[(b * a.Hq + h) * a.Sq + i] = acc;
+        if (row < rows && sub == 0) {
+            a.delta[row] = acc;
+            if (a.lse2 != nullptr) a.lse2[row] = i < a.Sq ? a.lse[bh * a.Sq + i] * kLog2e : __builtin_inff();
+        }
     } else {
         const int64_t n4 = n4_0 + n4_1;
         const int64_t stride = int64_t(gridDim.x - nblk_delta) * kThreads;
@@ -109,7 +114,7 @@ hipError_t post_dispatch(int D, const float* acc, uint16_t* out, int64_t sb, int
 
 hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s) {
     (void)algo;
-    const int64_t rows = int64_t(a.B) * a.Sq * a.Hq;
+    const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
     const int L = a.Dv / 8;
     const int rpb = kThreads / L;
     const int32_t nblk_delta = int32_t((rows + rpb - 1) / rpb);

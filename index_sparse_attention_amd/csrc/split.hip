@@ -29,7 +29,6 @@
 namespace isattn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D, int PITCH, int ROWS, int NT, bool PERM>
 __device__ __forceinline__ void stage(uint16_t* dst, const uint16_t* src, int64_t row_stride, int row0,
@@ -148,13 +147,10 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
         for (int c = 0; c < C::NCQ; ++c) qB[qt][c] = in ? gload_operand(qr + 16 * c) : bf16x8_t{};
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) doB[qt][c] = in ? gload_operand(dr + 16 * c) : bf16x8_t{};
-        lse2[qt] = __builtin_inff();
-        dlt[qt] = 0.f;
-        if (in) {
-            const int64_t si = (int64_t(b) * a.Hq + h) * a.Sq + qrow;
-            lse2[qt] = a.lse[si] * kLog2e;
-            dlt[qt] = a.delta[si];
-        }
+        // padded statistics: rows past Sq read lse2 = +inf (P = 0) and delta = 0
+        const int64_t si = (int64_t(b) * a.Hq + h) * a.stat_ld + qrow;
+        lse2[qt] = a.lse2[si];
+        dlt[qt] = a.delta[si];
     }
 
     f32x16_t dq[C::QT][C::NDT];
@@ -286,22 +282,488 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK/dV pass
+//
+// One workgroup per (batch, KV head, 128-key block), four waves in two roles
+// over the same 128 keys:
+//   P waves (0, 1), 64 keys each: K rows resident in registers, dV
+//     accumulators.  Step t: S = Q_t K^T and P_t = exp2(S * scale * log2e -
+//     lse2), handed to the partner through LDS; between those, the MFMAs of
+//     dV += P_{t-1}^T dO_{t-1}.
+//   dS waves (2, 3), the same 64 keys: V rows resident, dK accumulators.
+//     Step t finishes query slice t-1: dP = dO V^T, dS = P (dP - delta) with
+//     P from the partner, dK += dS^T Q; the dS arithmetic of one 32-key tile
+//     runs between the MFMAs of the other.
+// A step is BM query rows of one kept query block of one head of the GQA
+// group.  The Q/dO tiles and the rows' lse2/delta go through a 3-stage LDS
+// ring filled by direct global->LDS loads; step t reads stages t and t-1
+// while stage t+1 lands.  Each 64-key wave feeds every Q/dO operand it reads
+// from LDS to two 32-key MFMA tiles.
 // ---------------------------------------------------------------------------
 template <int DQK, int DV>
 struct DkvCfg {
-    static constexpr int BN = 128;                 // keys per workgroup
-    static constexpr int BM = 64;                  // query rows per step
+    static constexpr int BN = 128;                          // keys per workgroup
+    static constexpr int BM = 32;                           // query rows per step
     static constexpr int NW = 4;
     static constexpr int NT = 256;
-    static constexpr int TILE = BM * (DQK + DV);   // Q and dO tiles of one stage
-    static constexpr int STAGE = TILE + 4 * BM;    // + float lse2[BM], delta[BM]
-    static constexpr int LDS_BYTES = 3 * STAGE * 2;
+    static constexpr int Q_BYTES = BM * DQK * 2;
+    static constexpr int O_BYTES = BM * DV * 2;
+    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[BM], delta[BM]
+    static constexpr int STAGE_BYTES = STAT_OFF + 2 * BM * 4;
+    static constexpr int NU = 4;                            // P fragments (kt, cc) per P wave and step
+    static constexpr int XBUF_BYTES = 2 * NU * 1024;        // P of both P waves for one step
+    static constexpr int X_OFF = 3 * STAGE_BYTES;
+    static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
+    static constexpr int NQI = Q_BYTES / 1024 / NW;         // 1 KiB loads per wave per Q tile
+    static constexpr int NOI = O_BYTES / 1024 / NW;
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDK = DQK / 32;
     static constexpr int NDV = DV / 32;
-    static_assert((STAGE * 2) % 16 == 0 && (TILE * 2) % 16 == 0, "stage alignment");
+    static_assert(Q_BYTES % (1024 * NW) == 0 && O_BYTES % (1024 * NW) == 0, "tiles split into whole wave loads");
+    static_assert(STAGE_BYTES % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Step sequence of one workgroup: (query head of the GQA group, kept query
+// block, BM-row part).  Every wave walks it identically.  The kept query
+// blocks of a head are read 64 at a time into a register (one per lane).
+template <int BM>
+struct DkvSteps {
+    const BwdArgs& a;
+    int b, hk, kb, n_base, shift, lane;
+    int gi = 0, it = 0, part = 0, count = 0, first = 0;
+    const int32_t* list = nullptr;
+    int chunk = 0, chunk_base = -1;
+
+    __device__ DkvSteps(const BwdArgs& a_, int b_, int hk_, int kb_, int lane_)
+        : a(a_), b(b_), hk(hk_), kb(kb_), n_base(kb_ * kBlock), shift(a_.Sk - a_.Sq), lane(lane_) {}
+
+    __device__ int hq() const { return hk * a.G + gi; }
+
+    __device__ void load_head() {
+        list = nullptr;
+        first = 0;
+        chunk_base = -1;
+        if (a.mask_kind == 1) {
+            const int hm = hq() * a.Hm / a.Hq;
+            const int r = (b * a.Hm + hm) * a.n_kb + kb;
+            const int beg = a.k2q_ptr[r];
+            count = a.k2q_ptr[r + 1] - beg;
+            list = a.k2q_col + beg;
+        } else {
+            if (a.causal) {
+                const int first_row = n_base - shift;
+                first = first_row <= 0 ? 0 : first_row / kBlock;
+            }
+            count = a.n_qb - first;
+        }
+    }
+    __device__ int qb_at() {
+        if (list == nullptr) return first + it;
+        const int base = it & ~63;
+        if (base != chunk_base) {
+            chunk_base = base;
+            chunk = base + lane < count ? list[base + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(chunk, it & 63);
+    }
+    // row m of the current step, -1 if no row of it sees the key block
+    __device__ int row0() {
+        const int qb = qb_at();
+        const int m = qb * kBlock + part * BM;
+        if (qb < 0 || qb >= a.n_qb || m >= a.Sq) return -1;
+        const int mlast = min(m + BM - 1, a.Sq - 1);
+        if (a.causal && mlast + shift < n_base) return -1;
+        return m;
+    }
+    __device__ bool start(int* m) {
+        load_head();
+        while (count == 0) {
+            if (++gi >= a.G) return false;
+            load_head();
+        }
+        *m = row0();
+        return *m >= 0 || next(m);
+    }
+    __device__ bool next(int* m) {
+        for (;;) {
+            if (++part == kBlock / BM) {
+                part = 0;
+                ++it;
+            }
+            while (it >= count) {
+                if (++gi >= a.G) return false;
+                it = 0;
+                part = 0;
+                load_head();
+            }
+            *m = row0();
+            if (*m >= 0) return true;
+        }
+    }
+};
+
+template <int DQK, int DV>
+struct DkvShared {
+    using C = DkvCfg<DQK, DV>;
+    const BwdArgs& a;
+    uint16_t* lds;
+    uint32_t lds_base;
+    int w, lane, l32, h2, b, hk, n_base;
+    uint32_t qoff[C::NQI], ooff[C::NOI];            // per-lane byte offsets of the tile loads (no clamping)
+
+    __device__ DkvShared(const BwdArgs& a_, uint16_t* lds_, int w_, int lane_, int b_, int hk_, int n_base_)
+        : a(a_), lds(lds_), lds_base(lds_address(lds_)), w(w_), lane(lane_), l32(lane_ & 31), h2(lane_ >> 5),
+          b(b_), hk(hk_), n_base(n_base_) {
+#pragma unroll
+        for (int k = 0; k < C::NQI; ++k) qoff[k] = tile_off<DQK>(w + C::NW * k, C::BM, a.q_ss);
+#pragma unroll
+        for (int k = 0; k < C::NOI; ++k) ooff[k] = tile_off<DV>(w + C::NW * k, C::BM, a.do_ss);
+    }
+    // byte offset of this lane's 16 bytes in 1 KiB load j of a swizzled tile
+    // (tile row t at LDS row swap23(t)); tile rows past `lim` read row lim
+    template <int D>
+    __device__ uint32_t tile_off(int j, int lim, int64_t ss) const {
+        const int e = 512 * j + 8 * lane;
+        const int r = e / D;
+        const int c = ((e - r * D) >> 3) ^ chunk_swz(r);
+        return uint32_t(min(swap23(r), lim)) * uint32_t(ss * 2) + uint32_t(16 * c);
+    }
+    __device__ const uint16_t* q_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2); }
+    __device__ const uint16_t* do_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2) + C::Q_BYTES / 2; }
+    __device__ const float* stats(int s) const {
+        return reinterpret_cast<const float*>(lds + s * (C::STAGE_BYTES / 2) + C::STAT_OFF / 2);
+    }
+    __device__ char* xbuf(int par, int wr, int u) const {
+        return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + (wr * C::NU + u) * 1024 + lane * 16;
+    }
+
+    // Enqueue the loads of step (hq, m) into stage s.
+    __device__ void issue(int hq, int m, int s) const {
+        const uint32_t sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        const uint16_t* qsrc = a.q + b * a.q_sb + hq * a.q_sh + int64_t(m) * a.q_ss;
+        const uint16_t* osrc = a.dO + b * a.do_sb + hq * a.do_sh + int64_t(m) * a.do_ss;
+        if (m + C::BM <= a.Sq) {
+#pragma unroll
+            for (int k = 0; k < C::NQI; ++k) dma16(qsrc, qoff[k], sb + 1024 * (w + C::NW * k));
+#pragma unroll
+            for (int k = 0; k < C::NOI; ++k) dma16(osrc, ooff[k], sb + C::Q_BYTES + 1024 * (w + C::NW * k));
+        } else {                                    // ragged tail: rows past Sq re-read row Sq - 1
+            const int lim = a.Sq - 1 - m;
+#pragma unroll
+            for (int k = 0; k < C::NQI; ++k)
+                dma16(qsrc, tile_off<DQK>(w + C::NW * k, lim, a.q_ss), sb + 1024 * (w + C::NW * k));
+#pragma unroll
+            for (int k = 0; k < C::NOI; ++k)
+                dma16(osrc, tile_off<DV>(w + C::NW * k, lim, a.do_ss), sb + C::Q_BYTES + 1024 * (w + C::NW * k));
+        }
+        // padded statistics: LDS position L holds row swap23(L) of the step
+        if (w >= 2 && lane < C::BM) {
+            const float* src = (w == 2 ? a.lse2 : a.delta) + (int64_t(b) * a.Hq + hq) * a.stat_ld + m;
+            dma4(src, uint32_t(4 * swap23(lane)), sb + uint32_t(C::STAT_OFF + (w - 2) * C::BM * 4));
+        }
+    }
+};
+
+// P wave: S, P, dV.
+template <int DQK, int DV>
+struct DkvPWave {
+    using C = DkvCfg<DQK, DV>;
+    const DkvShared<DQK, DV>& sh;
+    const BwdArgs& a;
+    int wr;
+    bf16x8_t kB[2][C::NCQ];                         // K rows of the wave's two 32-key tiles
+    f32x16_t dv[2][C::NDV];
+    bf16x8_t pa[2][2];                              // P of the previous step, (kt, cc)
+    int qmin[2];                                    // first query row that sees the lane's key of tile kt
+
+    __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
+        const int shift = a.Sk - a.Sq;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = sh.n_base + 64 * wr + 32 * kt + sh.l32;
+            const bool in = key < a.Sk;
+            const uint16_t* kr = a.k + sh.b * a.k_sb + sh.hk * a.k_sh + int64_t(in ? key : 0) * a.k_ss + 8 * sh.h2;
+#pragma unroll
+            for (int c = 0; c < C::NCQ; ++c) kB[kt][c] = in ? gload_operand(kr + 16 * c) : bf16x8_t{};
+            qmin[kt] = in ? (a.causal ? key - shift : -(1 << 30)) : INT_MAX;   // rows < 2^30: tau cannot overflow
+#pragma unroll
+            for (int j = 0; j < C::NDV; ++j) dv[kt][j] = f32x16_t{};
+        }
+    }
+
+    __device__ bf16x8_t dot_frag(const uint16_t* sdO, int f) const {   // f = (cc, j)
+        return b_operand_tr_swz<DV>(sdO, 0, f / C::NDV, 32 * (f % C::NDV), sh.lane);
+    }
+
+    // One step: S of stage s, P of it (to LDS parity par and to pa), and
+    // with PREV the dV update of the previous step (stage sp) in between.
+    // tau[kt]: rows of the step below offset tau (relative to this lane's first
+    // row, m + 8 * h2) are masked for the lane's key of tile kt
+    template <bool PREV>
+    __device__ void body(int s, int sp, int par, int m, bool mask) {
+        int tau[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) tau[kt] = mask ? qmin[kt] - m - 8 * sh.h2 : INT_MIN;
+        const uint16_t* sQ = sh.q_tile(s);
+        f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+        {
+            constexpr int PF = 3;
+            bf16x8_t qa[PF + 1];
+#pragma unroll
+            for (int c = 0; c < PF; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
+#pragma unroll
+            for (int c = 0; c < C::NCQ; ++c) {
+                if (c + PF < C::NCQ) qa[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sQ, sh.l32, 16 * (c + PF) + 8 * sh.h2);
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(qa[c % (PF + 1)], kB[kt][c], st[kt]);
+                __builtin_amdgcn_sched_barrier(0);   // keep the ring's read-ahead distance (bounds registers)
+            }
+        }
+        const float* sL = sh.stats(s);
+        float4 l4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * sh.h2);
+
+        // dV MFMAs of the previous step: fragments f = (cc, j), two key tiles each;
+        // the new P fragments u = (kt, cc) are formed between them
+        constexpr int NF = 2 * C::NDV;
+        const uint16_t* sdO = sh.do_tile(sp);
+        constexpr int PF = 3;
+        bf16x8_t fr[PF + 1];
+        if (PREV) {
+#pragma unroll
+            for (int f = 0; f < PF; ++f) fr[f] = dot_frag(sdO, f);
+        }
+        bf16x8_t pn[2][2];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (PREV) {
+                if (f + PF < NF) fr[(f + PF) % (PF + 1)] = dot_frag(sdO, f + PF);
+                const int cc = f / C::NDV, j = f % C::NDV;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) dv[kt][j] = mfma32(pa[kt][cc], fr[f % (PF + 1)], dv[kt][j]);
+            }
+#pragma unroll
+            for (int u = f * C::NU / NF; u < (f + 1) * C::NU / NF; ++u) {
+                const int kt = u >> 1, cc = u & 1;
+                u32x4_t pk;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float p2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int i = 8 * cc + 2 * jj + e;
+                        const float4 lv = l4[i >> 2];
+                        const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
+                        const float p = fast_exp2(fmaf(st[kt][i], a.scale_log2, -l));
+                        p2[e] = 16 * cc + 2 * jj + e < tau[kt] ? 0.f : p;
+                    }
+                    pk[jj] = pack_bf16x2(p2[0], p2[1]);
+                }
+                pn[kt][cc] = as_bf16x8(pk);
+                *reinterpret_cast<bf16x8_t*>(sh.xbuf(par, wr, u)) = pn[kt][cc];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) pa[kt][cc] = pn[kt][cc];
+    }
+
+    __device__ void first(int s, int par, int m, bool mask) { body<false>(s, s, par, m, mask); }
+    __device__ void step(int s, int sp, int par, int m, bool mask) { body<true>(s, sp, par, m, mask); }
+    // dV update of the last step (stage sp)
+    __device__ void drain(int sp, int par) {
+        (void)par;
+        const uint16_t* sdO = sh.do_tile(sp);
+#pragma unroll
+        for (int f = 0; f < 2 * C::NDV; ++f) {
+            const bf16x8_t fr = dot_frag(sdO, f);
+            const int cc = f / C::NDV, j = f % C::NDV;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) dv[kt][j] = mfma32(pa[kt][cc], fr, dv[kt][j]);
+        }
+    }
+    __device__ void store() const {
+        uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = sh.n_base + 64 * wr + 32 * kt + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+                if (n < a.Sk) {
+#pragma unroll
+                    for (int j = 0; j < C::NDV; ++j) g[n * a.dv_ss + 32 * j + sh.l32] = to_bf16(dv[kt][j][i]);
+                }
+            }
+    }
+};
+
+// dS wave: dP, dS, dK.
+template <int DQK, int DV>
+struct DkvSWave {
+    using C = DkvCfg<DQK, DV>;
+    const DkvShared<DQK, DV>& sh;
+    const BwdArgs& a;
+    int wr;
+    bf16x8_t vB[2][C::NCV];
+    f32x16_t dk[2][C::NDK];
+
+    __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = sh.n_base + 64 * wr + 32 * kt + sh.l32;
+            const bool in = key < a.Sk;
+            const uint16_t* vr = a.v + sh.b * a.v_sb + sh.hk * a.v_sh + int64_t(in ? key : 0) * a.v_ss + 8 * sh.h2;
+#pragma unroll
+            for (int c = 0; c < C::NCV; ++c) vB[kt][c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
+#pragma unroll
+            for (int j = 0; j < C::NDK; ++j) dk[kt][j] = f32x16_t{};
+        }
+    }
+
+    // dS fragment (kt, cc) from P (LDS) and dP of key tile kt
+    __device__ bf16x8_t ds_frag(const f32x16_t& dpt, const float4 (&d4)[4], const u32x4_t& pw, int cc) const {
+        u32x4_t pk;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            float r[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 8 * cc + 2 * jj + e;
+                const float4 dv4 = d4[i >> 2];
+                const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
+                const float p = e == 0 ? bf16_lo(pw[jj]) : bf16_hi(pw[jj]);
+                r[e] = p * (dpt[i] - dl);
+            }
+            pk[jj] = pack_bf16x2(r[0], r[1]);
+        }
+        return as_bf16x8(pk);
+    }
+
+    // Finish the query slice in stage s whose P is in LDS parity par.
+    __device__ void finish(int s, int par) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));
+        const uint16_t* sdO = sh.do_tile(s);
+        const uint16_t* sQ = sh.q_tile(s);
+        bf16x8_t oa[C::NCV];
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
+        const float* sD = sh.stats(s) + C::BM;
+        float4 d4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
+        u32x4_t pw[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) pw[kt][cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc));
+        constexpr int NQF = 2 * C::NDK;            // Q^T fragments (cc, j)
+        bf16x8_t qf[NQF];
+        f32x16_t dp0 = f32x16_t{}, dp1 = f32x16_t{};
+        bf16x8_t sa[2][2];
+        // dP of key tile 0
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) dp0 = mfma32(oa[c], vB[0][c], dp0);
+        asm volatile("" : "+v"(dp0));              // dP is read by VALU: keep it out of the accumulators' AGPRs
+        // dP of key tile 1, with dS of tile 0 formed in between
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) {
+            dp1 = mfma32(oa[c], vB[1][c], dp1);
+            if (c == C::NCV / 4) sa[0][0] = ds_frag(dp0, d4, pw[0][0], 0);
+            if (c == 3 * C::NCV / 4) sa[0][1] = ds_frag(dp0, d4, pw[0][1], 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("" : "+v"(dp1));
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+        // dK of key tile 0, with dS of tile 1 formed in between
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) {
+            dk[0][f % C::NDK] = mfma32(sa[0][f / C::NDK], qf[f], dk[0][f % C::NDK]);
+            if (f == NQF / 4) sa[1][0] = ds_frag(dp1, d4, pw[1][0], 0);
+            if (f == 3 * NQF / 4) sa[1][1] = ds_frag(dp1, d4, pw[1][1], 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // dK of key tile 1
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) dk[1][f % C::NDK] = mfma32(sa[1][f / C::NDK], qf[f], dk[1][f % C::NDK]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));   // accumulators stay in AGPRs
+    }
+
+    __device__ void first(int s, int par, int m, bool mask) {
+        (void)s;
+        (void)par;
+        (void)m;
+        (void)mask;
+    }
+    __device__ void step(int s, int sp, int par, int m, bool mask) {
+        (void)s;
+        (void)m;
+        (void)mask;
+        finish(sp, par ^ 1);
+    }
+    __device__ void drain(int sp, int par) { finish(sp, par); }
+
+    __device__ void store() const {
+        uint16_t* g = a.dk + sh.b * a.dk_sb + sh.hk * a.dk_sh;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = sh.n_base + 64 * wr + 32 * kt + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+                if (n < a.Sk) {
+#pragma unroll
+                    for (int j = 0; j < C::NDK; ++j) g[n * a.dk_ss + 32 * j + sh.l32] = to_bf16(dk[kt][j][i] * a.scale);
+                }
+            }
+    }
+};
+
+// Steps, barriers and loads, shared by both roles.  Step t (stage t % 3, P
+// parity t % 2) may read stage t - 1; stage t + 1 is enqueued after the
+// barrier that ends step t - 1.  The loop body is one straight-line block per
+// role (masking is a per-element select, not a branch) so that the
+// accumulators stay put in registers across iterations.
+template <int DQK, int DV, class Role>
+__device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
+                                         Role& role) {
+    using C = DkvCfg<DQK, DV>;
+    const BwdArgs& a = sh.a;
+    const bool ragged_keys = sh.n_base + C::BN > a.Sk;
+    const int shift = a.Sk - a.Sq;
+    // some pair of step m is masked (rows past Sq need no mask: their lse2 is +inf)
+    auto need_mask = [&](int m) { return ragged_keys || (a.causal && sh.n_base + C::BN - 1 > m + shift); };
+
+    int m = -1;
+    if (!steps.start(&m)) return;
+    sh.issue(steps.hq(), m, 0);
+    int t = 0;
+    int mn = -1;
+    bool more = steps.next(&mn);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (more) sh.issue(steps.hq(), mn, 1);
+    role.first(0, 0, m, need_mask(m));
+    while (more) {
+        m = mn;
+        ++t;
+        more = steps.next(&mn);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (more) sh.issue(steps.hq(), mn, (t + 1) % 3);
+        role.step(t % 3, (t + 2) % 3, t & 1, m, need_mask(m));
+    }
+    __syncthreads();
+    role.drain(t % 3, t & 1);
+}
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
@@ -309,248 +771,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int l32 = lane & 31, h2 = lane >> 5;
-
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps role and load addresses scalar
     const int BH = a.B * a.Hk;
     const int id = blockIdx.x;
     const int kb = id / BH;                        // longest key columns first under a causal mask
     const int bh = id - kb * BH;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
-    const int n_base = kb * C::BN;
-    const int shift = a.Sk - a.Sq;
-
-    // ---- resident operands: K / V rows of this wave's keys (B operands)
-    const int nk = 32 * w + l32;
-    const int key = n_base + nk;
-    const bool key_in = key < a.Sk;
-    bf16x8_t kB[C::NCQ], vB[C::NCV];
-    {
-        const uint16_t* kr = a.k + b * a.k_sb + hk * a.k_sh + int64_t(key_in ? key : 0) * a.k_ss + 8 * h2;
-        const uint16_t* vr = a.v + b * a.v_sb + hk * a.v_sh + int64_t(key_in ? key : 0) * a.v_ss + 8 * h2;
-#pragma unroll
-        for (int c = 0; c < C::NCQ; ++c) kB[c] = key_in ? gload_operand(kr + 16 * c) : bf16x8_t{};
-#pragma unroll
-        for (int c = 0; c < C::NCV; ++c) vB[c] = key_in ? gload_operand(vr + 16 * c) : bf16x8_t{};
-    }
-
-    f32x16_t dk[C::NDK], dv[C::NDV];
-#pragma unroll
-    for (int t = 0; t < C::NDK; ++t) dk[t] = f32x16_t{};
-#pragma unroll
-    for (int t = 0; t < C::NDV; ++t) dv[t] = f32x16_t{};
-
-    const bool tile_ragged = n_base + C::BN > a.Sk;
-    // query row q sees this lane's key iff the key is in range and (not causal or key <= q + shift)
-    const int qmin = key_in ? (a.causal ? key - shift : INT_MIN) : INT_MAX;
-
-    // ---- step iterator over (query head of the group, kept query block, 64-row half)
-    int gi = 0, it = 0, half = 0, qb_count = 0, qb_first = 0;
-    const int32_t* qb_list = nullptr;
-    auto load_head = [&]() {
-        const int hq = hk * a.G + gi;
-        qb_list = nullptr;
-        qb_first = 0;
-        if (a.mask_kind == 1) {
-            const int hm = hq * a.Hm / a.Hq;
-            const int r = (b * a.Hm + hm) * a.n_kb + kb;
-            const int beg = a.k2q_ptr[r];
-            qb_count = a.k2q_ptr[r + 1] - beg;
-            qb_list = a.k2q_col + beg;
-        } else {
-            if (a.causal) {
-                const int first_row = n_base - shift;
-                qb_first = first_row <= 0 ? 0 : first_row / kBlock;
-            }
-            qb_count = a.n_qb - qb_first;
-        }
-    };
-    auto cur_m0 = [&]() -> int {                   // m0 of (gi, it, half), -1 if no row sees the tile
-        const int qb = qb_list ? qb_list[it] : qb_first + it;
-        const int m0 = qb * kBlock + half * C::BM;
-        if (qb < 0 || qb >= a.n_qb || m0 >= a.Sq) return -1;
-        const int mlast = min(m0 + C::BM - 1, a.Sq - 1);
-        if (a.causal && mlast + shift < n_base) return -1;
-        return m0;
-    };
-    auto advance = [&](int* m0) -> bool {          // to the next valid step; false at the end
-        for (;;) {
-            if (++half == kBlock / C::BM) {
-                half = 0;
-                ++it;
-            }
-            while (it >= qb_count) {
-                if (++gi >= a.G) return false;
-                it = 0;
-                half = 0;
-                load_head();
-            }
-            *m0 = cur_m0();
-            if (*m0 >= 0) return true;
-        }
-    };
-
-    const int64_t srow_g = int64_t(b) * a.Hq;
-    float statv = 0.f;                             // this thread's LSE*log2e or delta of a staged row
-    auto issue = [&](int hq, int m0, int stage_i) {
-        uint16_t* base = lds + stage_i * C::STAGE;
-        load_tile_async<DQK, C::BM, C::NW>(base, a.q + b * a.q_sb + hq * a.q_sh, a.q_ss, m0, a.Sq, w, lane);
-        load_tile_async<DV, C::BM, C::NW>(base + C::BM * DQK, a.dO + b * a.do_sb + hq * a.do_sh, a.do_ss, m0,
-                                          a.Sq, w, lane);
-        if (tid < 2 * C::BM) {
-            const int row = m0 + (tid & (C::BM - 1));
-            const int64_t si = (srow_g + hq) * a.Sq + row;
-            if (tid < C::BM) statv = row < a.Sq ? a.lse[si] * kLog2e : __builtin_inff();
-            else statv = row < a.Sq ? a.delta[si] : 0.f;
-        }
-    };
-    auto store_stats = [&](int stage_i) {
-        if (tid < 2 * C::BM) {
-            float* st = reinterpret_cast<float*>(lds + stage_i * C::STAGE + C::TILE);
-            st[(tid & ~(C::BM - 1)) + swap23(tid & (C::BM - 1))] = statv;
-        }
-    };
-    bf16x8_t pa[2][2], sa[2][2];                   // packed P / dS of the previous step
-    auto dkv_update = [&](int stage_i) {
-        const uint16_t* sQ = lds + stage_i * C::STAGE;
-        const uint16_t* sdO = sQ + C::BM * DQK;
-        // MFMA f: group g = f / (NDV + NDK) = (mt, cc); within it dV tiles first, then dK tiles
-        constexpr int PG = C::NDV + C::NDK;
-        constexpr int NF = 4 * PG;
-        constexpr int PF = 4;                      // prefetch depth (fragments)
-        auto frag = [&](int f) -> bf16x8_t {
-            const int g = f / PG, j = f % PG;
-            const int mt = g >> 1, cc = g & 1;
-            return j < C::NDV ? b_operand_tr_swz<DV>(sdO, 32 * mt, cc, 32 * j, lane)
-                              : b_operand_tr_swz<DQK>(sQ, 32 * mt, cc, 32 * (j - C::NDV), lane);
-        };
-        bf16x8_t fr[PF + 1];
-#pragma unroll
-        for (int f = 0; f < PF; ++f) fr[f] = frag(f);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if (f + PF < NF) fr[(f + PF) % (PF + 1)] = frag(f + PF);
-            const int g = f / PG, j = f % PG;
-            const int mt = g >> 1, cc = g & 1;
-            if (j < C::NDV) dv[j] = mfma32(pa[mt][cc], fr[f % (PF + 1)], dv[j]);
-            else dk[j - C::NDV] = mfma32(sa[mt][cc], fr[f % (PF + 1)], dk[j - C::NDV]);
-        }
-    };
-
-    load_head();
-    int m0 = -1;
-    bool have = qb_count > 0;
-    if (have) {
-        m0 = cur_m0();
-        if (m0 < 0) have = advance(&m0);
-    }
-    if (have) issue(hk * a.G + gi, m0, 0);
-    int sidx = 0;
-    bool has_prev = false;
-    while (have) {
-        int m0n = -1;
-        const bool more = advance(&m0n);
-        const int next_h = hk * a.G + gi;
-        const int cur = sidx % 3;
-        if (has_prev) dkv_update((sidx + 2) % 3);
-        wait_vmcnt<0>();
-        store_stats(cur);
-        __syncthreads();
-        if (more) issue(next_h, m0n, (sidx + 1) % 3);
-
-        const uint16_t* sQ = lds + cur * C::STAGE;
-        const uint16_t* sdO = sQ + C::BM * DQK;
-        const float* sL = reinterpret_cast<const float*>(lds + cur * C::STAGE + C::TILE);
-        const float* sD = sL + C::BM;
-
-        f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-        f32x16_t dp[2] = {f32x16_t{}, f32x16_t{}};
-        {
-            constexpr int PF = 2;                  // prefetch depth (chunks)
-            bf16x8_t qa[PF + 1][2], oa[PF + 1][2];
-#pragma unroll
-            for (int c = 0; c < PF; ++c)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    qa[c][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 16 * c + 8 * h2);
-                    if (c < C::NCV) oa[c][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 16 * c + 8 * h2);
-                }
-#pragma unroll
-            for (int c = 0; c < C::NCQ; ++c) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    if (c + PF < C::NCQ)
-                        qa[(c + PF) % (PF + 1)][mt] = row_operand_swz<DQK>(sQ, 32 * mt + l32, 16 * (c + PF) + 8 * h2);
-                    if (c + PF < C::NCV)
-                        oa[(c + PF) % (PF + 1)][mt] = row_operand_swz<DV>(sdO, 32 * mt + l32, 16 * (c + PF) + 8 * h2);
-                }
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(qa[c % (PF + 1)][mt], kB[c], s[mt]);
-                if (c < C::NCV) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) dp[mt] = mfma32(oa[c % (PF + 1)][mt], vB[c], dp[mt]);
-                }
-            }
-        }
-
-        // LSE / delta of this lane's accumulator rows: LDS rows 32*mt + 8*g + 4*h2 + 0..3
-        float4 l4[2][4], d4[2][4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                l4[mt][g] = *reinterpret_cast<const float4*>(sL + 32 * mt + 8 * g + 4 * h2);
-                d4[mt][g] = *reinterpret_cast<const float4*>(sD + 32 * mt + 8 * g + 4 * h2);
-            }
-        const bool need_mask = tile_ragged || (a.causal && n_base + C::BN - 1 > m0 + shift);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 lv = l4[mt][i >> 2];
-                const float4 dv4 = d4[mt][i >> 2];
-                const float lse = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
-                const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
-                float p = fast_exp2(s[mt][i] * a.scale_log2 - lse);
-                if (need_mask) {
-                    const int qrow = m0 + 32 * mt + 16 * (i >> 3) + 8 * h2 + (i & 7);
-                    p = qrow >= qmin ? p : 0.f;
-                }
-                dp[mt][i] = p * (dp[mt][i] - dl);
-                s[mt][i] = p;
-            }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                u32x4_t pp, pd;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pp[j] = pack_bf16x2(s[mt][8 * cc + 2 * j], s[mt][8 * cc + 2 * j + 1]);
-                    pd[j] = pack_bf16x2(dp[mt][8 * cc + 2 * j], dp[mt][8 * cc + 2 * j + 1]);
-                }
-                pa[mt][cc] = as_bf16x8(pp);
-                sa[mt][cc] = as_bf16x8(pd);
-            }
-        has_prev = true;
-        ++sidx;
-        have = more;
-        m0 = m0n;
-    }
-    if (has_prev) dkv_update((sidx + 2) % 3);
-
-    uint16_t* gdk = a.dk + b * a.dk_sb + hk * a.dk_sh;
-    uint16_t* gdv = a.dv + b * a.dv_sb + hk * a.dv_sh;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int n = n_base + 32 * w + 8 * (i >> 2) + 4 * h2 + (i & 3);
-        if (n < a.Sk) {
-#pragma unroll
-            for (int dt = 0; dt < C::NDK; ++dt) gdk[n * a.dk_ss + 32 * dt + l32] = to_bf16(dk[dt][i] * a.scale);
-#pragma unroll
-            for (int dt = 0; dt < C::NDV; ++dt) gdv[n * a.dv_ss + 32 * dt + l32] = to_bf16(dv[dt][i]);
-        }
+    const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
+    DkvSteps<C::BM> steps(a, b, hk, kb, lane);
+    if (w < 2) {
+        DkvPWave<DQK, DV> role(sh, w);
+        dkdv_run<DQK, DV>(sh, steps, role);
+        role.store();
+    } else {
+        DkvSWave<DQK, DV> role(sh, w - 2);
+        dkdv_run<DQK, DV>(sh, steps, role);
+        role.store();
     }
 }
 

@@ -52,9 +52,14 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     p.G = s.heads_k > 0 ? s.heads_q / s.heads_k : 0;
     const int64_t rows_q = int64_t(s.batch) * s.seqlen_q * s.heads_q;
     const int64_t rows_k = int64_t(s.batch) * s.seqlen_k * s.heads_k;
+    // SPLIT pads the per-row statistics of each (b, h) to whole 128-row blocks
+    p.stat_ld = algo == ISATTN_ALGO_SPLIT ? p.n_qb * kBlock : s.seqlen_q;
+    const int64_t stat_rows = int64_t(s.batch) * s.heads_q * p.stat_ld;
     size_t off = 0;
     p.off_delta = off;
-    off = align_up(off + size_t(rows_q) * sizeof(float), kWsAlign);
+    off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
+    p.off_lse2 = off;
+    if (algo == ISATTN_ALGO_SPLIT) off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
     if (algo == ISATTN_ALGO_LOOPK) {
         p.acc0_elems = rows_k * s.dim_qk;
         p.acc1_elems = rows_k * s.dim_v;
@@ -108,6 +113,9 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     if ((st = check_view(dk, nk)) != ISATTN_OK) return st;
     if ((st = check_view(dv, nk)) != ISATTN_OK) return st;
     if (nq > 0 && lse == nullptr) return ISATTN_ERR_NULL;
+    if (algo == ISATTN_ALGO_SPLIT && nq > 0 &&
+        (q->stride_s >= kMaxSplitRowStride || dO->stride_s >= kMaxSplitRowStride))
+        return ISATTN_ERR_STRIDE_ALIGN;
 
     BwdArgs a{};
     a.mask_kind = ISATTN_MASK_DENSE;
@@ -154,6 +162,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     a.Dv = s.dim_v;
     a.n_qb = p.n_qb;
     a.n_kb = p.n_kb;
+    a.stat_ld = p.stat_ld;
     a.causal = causal != 0;
     a.scale = softmax_scale;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;

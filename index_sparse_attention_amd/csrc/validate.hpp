@@ -12,12 +12,16 @@ namespace isattn {
 
 constexpr size_t kWsAlign = 256;
 
+// Largest sequence stride (elements) of Q and dO the SPLIT dK/dV pass accepts:
+// its direct-to-LDS loads address a tile's rows with 32-bit byte offsets.
+constexpr int64_t kMaxSplitRowStride = int64_t(1) << 22;
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 struct BwdPlan {
-    int32_t n_qb, n_kb, G, Hm;
-    size_t off_delta, off_acc0, off_acc1, total;
+    int32_t n_qb, n_kb, G, Hm, stat_ld;
+    size_t off_delta, off_lse2, off_acc0, off_acc1, total;
     int64_t acc0_elems, acc1_elems;
 };
 

@@ -57,7 +57,9 @@ def test_workspace_sizes(lib):
     delta = al(2 * 300 * 4 * 4)
     assert ws_bytes(lib, s, 0) == delta + al(2 * 200 * 2 * 128 * 4) * 2
     assert ws_bytes(lib, s, 1) == delta + al(2 * 300 * 4 * 128 * 4)
-    assert ws_bytes(lib, s, 2) == delta
+    # SPLIT: delta and lse*log2(e), each padded per (batch, head) to whole 128-row blocks
+    stats = al(2 * 4 * 384 * 4)
+    assert ws_bytes(lib, s, 2) == 2 * stats
     assert ws_bytes(lib, s, 7) == 0
     assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
     # converter: presence B*H*nQB*nKB bytes + row and column counts
@@ -85,7 +87,7 @@ class Call:
         self.scale = 0.125
         self.algo = algo
         self.ws = FAKE
-        self.ws_bytes = ws_bytes(lib, self.shape, algo) if algo in (0, 1) else 0
+        self.ws_bytes = ws_bytes(lib, self.shape, algo) if algo in (0, 1, 2) else 0
 
     def __call__(self, shape_ptr=True):
         v = self.views
@@ -120,6 +122,12 @@ def test_bwd_validation_errors(lib):
     c = Call(lib, Hq=4, Hk=2); c.mask = _abi.Mask(1, 128, 128, 3, FAKE, FAKE, FAKE, FAKE); assert c() == MASK
     c = Call(lib); c.mask = _abi.Mask(1, 128, 128, 2, None, None, FAKE, FAKE); assert c() == NULL
     c = Call(lib, algo=1); c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, None, None); assert c() == NULL
+    # SPLIT addresses Q/dO tile rows with 32-bit offsets: sequence strides from 2^22 elements are rejected
+    c = Call(lib, algo=2); c.views["q"].stride_s = 1 << 22; c.views["q"].stride_b = 256 << 22
+    assert c() == STRIDE
+    c = Call(lib, algo=2); c.views["do"].stride_s = 1 << 22; c.views["do"].stride_b = 256 << 22
+    assert c() == STRIDE
+    c = Call(lib, algo=2); c.ws_bytes -= 1; assert c() == WS
 
 
 def test_index_converter_validation_errors(lib):
