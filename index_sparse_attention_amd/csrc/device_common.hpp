@@ -211,6 +211,19 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
                  : "memory");
 }
 
+// Work item of a workgroup, chosen so each XCD walks a contiguous range of
+// the item list.  Workgroups are dispatched to the 8 XCDs round-robin
+// (workgroup i to XCD i % 8); giving XCD x the items [x * per, (x + 1) * per)
+// in order makes the workgroups an XCD runs at one time neighbours in the
+// list, which share their operand tiles in that XCD's L2.  The grid has
+// 8 * per workgroups; -1 marks the padding ones past the last item.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_items_per(int n_items) { return (n_items + kXcds - 1) / kXcds; }
+__device__ __forceinline__ int xcd_item(int id, int n_items) {
+    const int w = (id % kXcds) * xcd_items_per(n_items) + id / kXcds;
+    return w < n_items ? w : -1;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (<= n outstanding).
 template <int n>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -93,10 +93,12 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
     const int w = tid >> 6;
     const int l32 = lane & 31, h2 = lane >> 5;
 
-    const int BH = a.B * a.Hq;
-    const int id = blockIdx.x;
-    const int qb = a.n_qb - 1 - id / BH;          // longest rows first under a causal mask
-    const int bh = id - (id / BH) * BH;
+    // items (b, h, query block), head-major; within a head the longest rows
+    // (most kept keys under a causal mask) first
+    const int item = xcd_item(blockIdx.x, a.n_qb * a.B * a.Hq);
+    if (item < 0) return;
+    const int bh = item / a.n_qb;
+    const int qb = a.n_qb - 1 - (item - bh * a.n_qb);
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int hk = h / a.G;
@@ -307,14 +309,17 @@ struct DkvCfg {
     static constexpr int NT = 256;
     static constexpr int Q_BYTES = BM * DQK * 2;
     static constexpr int O_BYTES = BM * DV * 2;
-    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[BM], delta[BM]
-    static constexpr int STAGE_BYTES = STAT_OFF + 2 * BM * 4;
+    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[64], delta[64] (BM used)
+    static constexpr int STAGE_BYTES = STAT_OFF + 2 * 64 * 4;
     static constexpr int NU = 4;                            // P fragments (kt, cc) per P wave and step
     static constexpr int XBUF_BYTES = 2 * NU * 1024;        // P of both P waves for one step
-    static constexpr int X_OFF = 3 * STAGE_BYTES;
+    static constexpr int NS = 4;                            // LDS ring stages (loads run two steps ahead)
+    static constexpr int X_OFF = NS * STAGE_BYTES;
     static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
     static constexpr int NQI = Q_BYTES / 1024 / NW;         // 1 KiB loads per wave per Q tile
     static constexpr int NOI = O_BYTES / 1024 / NW;
+    static constexpr int NDMA_P = NQI + NOI;                // loads a P wave issues per step
+    static constexpr int NDMA_S = NQI + NOI + 1;            // a dS wave also loads one statistics row
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDK = DQK / 32;
@@ -328,9 +333,10 @@ struct DkvCfg {
 // blocks of a head are read 64 at a time into a register (one per lane).
 template <int BM>
 struct DkvSteps {
+    static constexpr int PARTS = kBlock / BM;
     const BwdArgs& a;
     int b, hk, kb, n_base, shift, lane;
-    int gi = 0, it = 0, part = 0, count = 0, first = 0;
+    int gi = 0, it = 0, part = 0, count = 0, first = 0, qb = 0;
     const int32_t* list = nullptr;
     int chunk = 0, chunk_base = -1;
 
@@ -366,13 +372,11 @@ struct DkvSteps {
         }
         return __builtin_amdgcn_readlane(chunk, it & 63);
     }
-    // row m of the current step, -1 if no row of it sees the key block
-    __device__ int row0() {
-        const int qb = qb_at();
+    // first row of (qb, part), -1 if out of range or no row of it sees the key block
+    __device__ int row_of() const {
         const int m = qb * kBlock + part * BM;
         if (qb < 0 || qb >= a.n_qb || m >= a.Sq) return -1;
-        const int mlast = min(m + BM - 1, a.Sq - 1);
-        if (a.causal && mlast + shift < n_base) return -1;
+        if (a.causal && min(m + BM - 1, a.Sq - 1) + shift < n_base) return -1;
         return m;
     }
     __device__ bool start(int* m) {
@@ -381,22 +385,31 @@ struct DkvSteps {
             if (++gi >= a.G) return false;
             load_head();
         }
-        *m = row0();
+        it = 0;
+        part = 0;
+        qb = qb_at();
+        *m = row_of();
         return *m >= 0 || next(m);
     }
     __device__ bool next(int* m) {
+        if (part + 1 < PARTS) {                     // common case: next part of the same block
+            ++part;
+            *m = row_of();
+            if (*m >= 0) return true;
+        }
         for (;;) {
-            if (++part == kBlock / BM) {
+            if (++part >= PARTS) {
                 part = 0;
-                ++it;
+                if (++it >= count) {
+                    do {
+                        if (++gi >= a.G) return false;
+                        load_head();
+                    } while (count == 0);
+                    it = 0;
+                }
+                qb = qb_at();
             }
-            while (it >= count) {
-                if (++gi >= a.G) return false;
-                it = 0;
-                part = 0;
-                load_head();
-            }
-            *m = row0();
+            *m = row_of();
             if (*m >= 0) return true;
         }
     }
@@ -410,6 +423,16 @@ struct DkvShared {
     uint32_t lds_base;
     int w, lane, l32, h2, b, hk, n_base;
     uint32_t qoff[C::NQI], ooff[C::NOI];            // per-lane byte offsets of the tile loads (no clamping)
+    uint32_t soff;                                  // per-lane byte offset of the statistics load
+
+    // The loads of one step: wave-uniform source pointers and LDS stage, per-lane offsets.
+    struct Dma {
+        const uint16_t* q;
+        const uint16_t* o;
+        const float* st;
+        uint32_t sb;
+        uint32_t qo[C::NQI], oo[C::NOI];
+    };
 
     __device__ DkvShared(const BwdArgs& a_, uint16_t* lds_, int w_, int lane_, int b_, int hk_, int n_base_)
         : a(a_), lds(lds_), lds_base(lds_address(lds_)), w(w_), lane(lane_), l32(lane_ & 31), h2(lane_ >> 5),
@@ -418,6 +441,7 @@ struct DkvShared {
         for (int k = 0; k < C::NQI; ++k) qoff[k] = tile_off<DQK>(w + C::NW * k, C::BM, a.q_ss);
 #pragma unroll
         for (int k = 0; k < C::NOI; ++k) ooff[k] = tile_off<DV>(w + C::NW * k, C::BM, a.do_ss);
+        soff = uint32_t(4 * (lane < C::BM ? swap23(lane) : 0));   // lanes past BM re-read the first row
     }
     // byte offset of this lane's 16 bytes in 1 KiB load j of a swizzled tile
     // (tile row t at LDS row swap23(t)); tile rows past `lim` read row lim
@@ -437,30 +461,33 @@ struct DkvShared {
         return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + (wr * C::NU + u) * 1024 + lane * 16;
     }
 
-    // Enqueue the loads of step (hq, m) into stage s.
-    __device__ void issue(int hq, int m, int s) const {
-        const uint32_t sb = lds_base + uint32_t(s * C::STAGE_BYTES);
-        const uint16_t* qsrc = a.q + b * a.q_sb + hq * a.q_sh + int64_t(m) * a.q_ss;
-        const uint16_t* osrc = a.dO + b * a.do_sb + hq * a.do_sh + int64_t(m) * a.do_ss;
+    // Plan the loads of step (hq, m) into stage s.
+    __device__ void plan(Dma& d, int hq, int m, int s) const {
+        d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        d.q = a.q + b * a.q_sb + hq * a.q_sh + int64_t(m) * a.q_ss;
+        d.o = a.dO + b * a.do_sb + hq * a.do_sh + int64_t(m) * a.do_ss;
+        d.st = (w == 2 ? a.lse2 : a.delta) + (int64_t(b) * a.Hq + hq) * a.stat_ld + m;
         if (m + C::BM <= a.Sq) {
 #pragma unroll
-            for (int k = 0; k < C::NQI; ++k) dma16(qsrc, qoff[k], sb + 1024 * (w + C::NW * k));
+            for (int k = 0; k < C::NQI; ++k) d.qo[k] = qoff[k];
 #pragma unroll
-            for (int k = 0; k < C::NOI; ++k) dma16(osrc, ooff[k], sb + C::Q_BYTES + 1024 * (w + C::NW * k));
+            for (int k = 0; k < C::NOI; ++k) d.oo[k] = ooff[k];
         } else {                                    // ragged tail: rows past Sq re-read row Sq - 1
             const int lim = a.Sq - 1 - m;
 #pragma unroll
-            for (int k = 0; k < C::NQI; ++k)
-                dma16(qsrc, tile_off<DQK>(w + C::NW * k, lim, a.q_ss), sb + 1024 * (w + C::NW * k));
+            for (int k = 0; k < C::NQI; ++k) d.qo[k] = tile_off<DQK>(w + C::NW * k, lim, a.q_ss);
 #pragma unroll
-            for (int k = 0; k < C::NOI; ++k)
-                dma16(osrc, tile_off<DV>(w + C::NW * k, lim, a.do_ss), sb + C::Q_BYTES + 1024 * (w + C::NW * k));
+            for (int k = 0; k < C::NOI; ++k) d.oo[k] = tile_off<DV>(w + C::NW * k, lim, a.do_ss);
         }
-        // padded statistics: LDS position L holds row swap23(L) of the step
-        if (w >= 2 && lane < C::BM) {
-            const float* src = (w == 2 ? a.lse2 : a.delta) + (int64_t(b) * a.Hq + hq) * a.stat_ld + m;
-            dma4(src, uint32_t(4 * swap23(lane)), sb + uint32_t(C::STAT_OFF + (w - 2) * C::BM * 4));
-        }
+    }
+    // Load j of this wave: Q tile parts, dO tile parts, then (dS waves) the
+    // statistics row: lse2 by wave 2, delta by wave 3, 64 lanes (rows past BM
+    // land in unused slots).  LDS position L holds row swap23(L) of the step.
+    __device__ void fire(const Dma& d, int j) const {
+        if (j < C::NQI) dma16(d.q, d.qo[j], d.sb + 1024 * (w + C::NW * j));
+        else if (j < C::NQI + C::NOI)
+            dma16(d.o, d.oo[j - C::NQI], d.sb + C::Q_BYTES + 1024 * (w + C::NW * (j - C::NQI)));
+        else dma4(d.st, soff, d.sb + uint32_t(C::STAT_OFF + (w - 2) * 256));
     }
 };
 
@@ -468,13 +495,17 @@ struct DkvShared {
 template <int DQK, int DV>
 struct DkvPWave {
     using C = DkvCfg<DQK, DV>;
+    using Dma = typename DkvShared<DQK, DV>::Dma;
+    static constexpr int NF = 2 * C::NDV;           // dO^T fragments (cc, j) of one step
     const DkvShared<DQK, DV>& sh;
     const BwdArgs& a;
     int wr;
     bf16x8_t kB[2][C::NCQ];                         // K rows of the wave's two 32-key tiles
     f32x16_t dv[2][C::NDV];
-    bf16x8_t pa[2][2];                              // P of the previous step, (kt, cc)
     int qmin[2];                                    // first query row that sees the lane's key of tile kt
+    // operands of the dV update of the step just computed, read ahead across the barrier
+    bf16x8_t nfr[NF];                               // its dO^T fragments
+    u32x4_t npp[2][2];                              // its P, (kt, cc)
 
     __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int shift = a.Sk - a.Sq;
@@ -495,94 +526,110 @@ struct DkvPWave {
         return b_operand_tr_swz<DV>(sdO, 0, f / C::NDV, 32 * (f % C::NDV), sh.lane);
     }
 
-    // One step: S of stage s, P of it (to LDS parity par and to pa), and
-    // with PREV the dV update of the previous step (stage sp) in between.
-    // tau[kt]: rows of the step below offset tau (relative to this lane's first
-    // row, m + 8 * h2) are masked for the lane's key of tile kt
+    // One step: S of stage s and P of it (to LDS parity par, read by the
+    // partner); with PREV, the dV MFMAs of the previous step (operands read
+    // ahead into nfr / npp) are issued between the P arithmetic, one bf16
+    // pair of P per MFMA.  Masked steps fix the packed P up afterwards.  At
+    // the end the operands of this step's own dV update are read ahead.
     template <bool PREV>
-    __device__ void body(int s, int sp, int par, int m, bool mask) {
-        int tau[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) tau[kt] = mask ? qmin[kt] - m - 8 * sh.h2 : INT_MIN;
+    __device__ void body(int s, int par, int m, bool mask, const Dma& d) {
         const uint16_t* sQ = sh.q_tile(s);
         f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
         {
-            constexpr int PF = 3;
-            bf16x8_t qa[PF + 1];
+            bf16x8_t qa[C::NCQ];
 #pragma unroll
-            for (int c = 0; c < PF; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
+            for (int c = 0; c < C::NCQ; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
+            __builtin_amdgcn_sched_barrier(0);     // all Q reads in flight before the first MFMA
+            // S MFMAs; this wave's loads for two steps ahead go out between them
 #pragma unroll
             for (int c = 0; c < C::NCQ; ++c) {
-                if (c + PF < C::NCQ) qa[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sQ, sh.l32, 16 * (c + PF) + 8 * sh.h2);
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(qa[c % (PF + 1)], kB[kt][c], st[kt]);
-                __builtin_amdgcn_sched_barrier(0);   // keep the ring's read-ahead distance (bounds registers)
+                for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(qa[c], kB[kt][c], st[kt]);
+                if (c < C::NDMA_P) sh.fire(d, c);
             }
         }
         const float* sL = sh.stats(s);
         float4 l4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * sh.h2);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // dV MFMAs of the previous step: fragments f = (cc, j), two key tiles each;
-        // the new P fragments u = (kt, cc) are formed between them
-        constexpr int NF = 2 * C::NDV;
-        const uint16_t* sdO = sh.do_tile(sp);
-        constexpr int PF = 3;
-        bf16x8_t fr[PF + 1];
-        if (PREV) {
+        // dV MFMAs k = (f, kt) of the previous step, f = (cc, j); P pairs q =
+        // (kt, cc, jj) of this step between them
+        constexpr int NK = 2 * NF;
+        constexpr int NQ = 16;
+        u32x4_t pn[2][2];
 #pragma unroll
-            for (int f = 0; f < PF; ++f) fr[f] = dot_frag(sdO, f);
-        }
-        bf16x8_t pn[2][2];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
+        for (int k = 0; k < NK; ++k) {
             if (PREV) {
-                if (f + PF < NF) fr[(f + PF) % (PF + 1)] = dot_frag(sdO, f + PF);
+                const int f = k >> 1, kt = k & 1;
                 const int cc = f / C::NDV, j = f % C::NDV;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) dv[kt][j] = mfma32(pa[kt][cc], fr[f % (PF + 1)], dv[kt][j]);
+                dv[kt][j] = mfma32(as_bf16x8(npp[kt][cc]), nfr[f], dv[kt][j]);
             }
 #pragma unroll
-            for (int u = f * C::NU / NF; u < (f + 1) * C::NU / NF; ++u) {
-                const int kt = u >> 1, cc = u & 1;
-                u32x4_t pk;
+            for (int q = k * NQ / NK; q < (k + 1) * NQ / NK; ++q) {
+                const int kt = q >> 3, cc = (q >> 2) & 1, jj = q & 3;
+                float p2[2];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float p2[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int i = 8 * cc + 2 * jj + e;
-                        const float4 lv = l4[i >> 2];
-                        const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
-                        const float p = fast_exp2(fmaf(st[kt][i], a.scale_log2, -l));
-                        p2[e] = 16 * cc + 2 * jj + e < tau[kt] ? 0.f : p;
-                    }
-                    pk[jj] = pack_bf16x2(p2[0], p2[1]);
+                for (int e = 0; e < 2; ++e) {
+                    const int i = 8 * cc + 2 * jj + e;
+                    const float4 lv = l4[i >> 2];
+                    const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
+                    p2[e] = fast_exp2(fmaf(st[kt][i], a.scale_log2, -l));
                 }
-                pn[kt][cc] = as_bf16x8(pk);
-                *reinterpret_cast<bf16x8_t*>(sh.xbuf(par, wr, u)) = pn[kt][cc];
+                pn[kt][cc][jj] = pack_bf16x2(p2[0], p2[1]);
+                if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc)) = pn[kt][cc];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (mask) {
+            // pairs whose row is below the lane key's first visible row (causal)
+            // or whose key is past Sk: clear the bf16 halves and rewrite
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int tau = qmin[kt] - m - 8 * sh.h2;   // first visible row offset of this lane
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int o = 16 * cc + 2 * jj;
+                        const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
+                        pn[kt][cc][jj] &= keep;
+                    }
+                    *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc)) = pn[kt][cc];
+                }
+            }
+        }
+        // read ahead the operands of this step's dV update (done next step)
+        const uint16_t* sdO = sh.do_tile(s);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) nfr[f] = dot_frag(sdO, f);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) pa[kt][cc] = pn[kt][cc];
+            for (int cc = 0; cc < 2; ++cc) npp[kt][cc] = pn[kt][cc];
     }
 
-    __device__ void first(int s, int par, int m, bool mask) { body<false>(s, s, par, m, mask); }
-    __device__ void step(int s, int sp, int par, int m, bool mask) { body<true>(s, sp, par, m, mask); }
-    // dV update of the last step (stage sp)
+    __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, par, m, mask, d); }
+    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) {
+        (void)sp;
+        body<true>(s, par, m, mask, d);
+    }
+    __device__ void fire_all(const Dma& d) const {
+#pragma unroll
+        for (int j = 0; j < C::NDMA_P; ++j) sh.fire(d, j);
+    }
+    // this wave's loads of the oldest outstanding step have landed (one newer step in flight)
+    __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_P>(); }
+    // dV update of the last step (operands already read ahead)
     __device__ void drain(int sp, int par) {
+        (void)sp;
         (void)par;
-        const uint16_t* sdO = sh.do_tile(sp);
 #pragma unroll
-        for (int f = 0; f < 2 * C::NDV; ++f) {
-            const bf16x8_t fr = dot_frag(sdO, f);
+        for (int k = 0; k < 2 * NF; ++k) {
+            const int f = k >> 1, kt = k & 1;
             const int cc = f / C::NDV, j = f % C::NDV;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) dv[kt][j] = mfma32(pa[kt][cc], fr, dv[kt][j]);
+            dv[kt][j] = mfma32(as_bf16x8(npp[kt][cc]), nfr[f], dv[kt][j]);
         }
     }
     __device__ void store() const {
@@ -609,6 +656,19 @@ struct DkvSWave {
     int wr;
     bf16x8_t vB[2][C::NCV];
     f32x16_t dk[2][C::NDK];
+    // operands of the next slice to finish, read ahead across the barrier
+    bf16x8_t noa[C::NCV];                           // its dO rows
+    float4 nd4[4];                                  // its delta rows
+
+    // read ahead the dO rows and delta of the slice in stage s
+    __device__ void read_ahead(int s) {
+        const uint16_t* sdO = sh.do_tile(s);
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) noa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
+        const float* sD = sh.stats(s) + 64;         // delta slot follows the 64-float lse2 slot
+#pragma unroll
+        for (int g = 0; g < 4; ++g) nd4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
+    }
 
     __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
 #pragma unroll
@@ -623,40 +683,34 @@ struct DkvSWave {
         }
     }
 
-    // dS fragment (kt, cc) from P (LDS) and dP of key tile kt
-    __device__ bf16x8_t ds_frag(const f32x16_t& dpt, const float4 (&d4)[4], const u32x4_t& pw, int cc) const {
-        u32x4_t pk;
+    // dS pair (cc, jj) of key tile kt: packed bf16 of P * (dP - delta)
+    __device__ uint32_t ds_pair(const f32x16_t& dpt, const float4 (&d4)[4], uint32_t pw, int cc, int jj) const {
+        float r[2];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            float r[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int i = 8 * cc + 2 * jj + e;
-                const float4 dv4 = d4[i >> 2];
-                const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
-                const float p = e == 0 ? bf16_lo(pw[jj]) : bf16_hi(pw[jj]);
-                r[e] = p * (dpt[i] - dl);
-            }
-            pk[jj] = pack_bf16x2(r[0], r[1]);
+        for (int e = 0; e < 2; ++e) {
+            const int i = 8 * cc + 2 * jj + e;
+            const float4 dv4 = d4[i >> 2];
+            const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
+            const float p = e == 0 ? bf16_lo(pw) : bf16_hi(pw);
+            r[e] = p * (dpt[i] - dl);
         }
-        return as_bf16x8(pk);
+        return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the query slice in stage s whose P is in LDS parity par.
-    __device__ void finish(int s, int par) {
+    // Finish the query slice in stage s whose P is in LDS parity par: dP of
+    // key tile 0, dP of tile 1 with dS of tile 0 between its MFMAs, dK of tile
+    // 0 with dS of tile 1 between its MFMAs, dK of tile 1.
+    // (dO rows and delta were read ahead into noa / nd4; with NEXT >= 0 the
+    // next slice's are read ahead at the end)
+    template <bool FIRE>
+    __device__ void finish(int s, int par, const typename DkvShared<DQK, DV>::Dma& d, int next) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));
-        const uint16_t* sdO = sh.do_tile(s);
         const uint16_t* sQ = sh.q_tile(s);
-        bf16x8_t oa[C::NCV];
-#pragma unroll
-        for (int c = 0; c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
-        const float* sD = sh.stats(s) + C::BM;
-        float4 d4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
+        const bf16x8_t (&oa)[C::NCV] = noa;
+        const float4 (&d4)[4] = nd4;
         u32x4_t pw[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -665,52 +719,73 @@ struct DkvSWave {
         constexpr int NQF = 2 * C::NDK;            // Q^T fragments (cc, j)
         bf16x8_t qf[NQF];
         f32x16_t dp0 = f32x16_t{}, dp1 = f32x16_t{};
-        bf16x8_t sa[2][2];
-        // dP of key tile 0
+        u32x4_t sa[2][2];
+        // dP of key tile 0, Q^T fragments read and (FIRE) this wave's loads for two steps ahead issued between
 #pragma unroll
-        for (int c = 0; c < C::NCV; ++c) dp0 = mfma32(oa[c], vB[0][c], dp0);
-        asm volatile("" : "+v"(dp0));              // dP is read by VALU: keep it out of the accumulators' AGPRs
-        // dP of key tile 1, with dS of tile 0 formed in between
+        for (int c = 0; c < C::NCV; ++c) {
+            dp0 = mfma32(oa[c], vB[0][c], dp0);
+            if (FIRE && c < C::NDMA_S) sh.fire(d, c);
+#pragma unroll
+            for (int f = c * NQF / (2 * C::NCV); f < (c + 1) * NQF / (2 * C::NCV); ++f)
+                qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // dP of key tile 1; dS of tile 0 (8 pairs) and the rest of Q^T between
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
             dp1 = mfma32(oa[c], vB[1][c], dp1);
-            if (c == C::NCV / 4) sa[0][0] = ds_frag(dp0, d4, pw[0][0], 0);
-            if (c == 3 * C::NCV / 4) sa[0][1] = ds_frag(dp0, d4, pw[0][1], 1);
+#pragma unroll
+            for (int f = (C::NCV + c) * NQF / (2 * C::NCV); f < (C::NCV + c + 1) * NQF / (2 * C::NCV); ++f)
+                qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+#pragma unroll
+            for (int q = c * 8 / C::NCV; q < (c + 1) * 8 / C::NCV; ++q) {
+                sa[0][q >> 2][q & 3] = ds_pair(dp0, d4, pw[0][q >> 2][q & 3], q >> 2, q & 3);
+                asm volatile("" ::"v"(sa[0][q >> 2][q & 3]));   // pin the pair between these MFMAs
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("" : "+v"(dp1));
-#pragma unroll
-        for (int f = 0; f < NQF; ++f) qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
-        // dK of key tile 0, with dS of tile 1 formed in between
+        // dK of key tile 0; dS of tile 1 between
 #pragma unroll
         for (int f = 0; f < NQF; ++f) {
-            dk[0][f % C::NDK] = mfma32(sa[0][f / C::NDK], qf[f], dk[0][f % C::NDK]);
-            if (f == NQF / 4) sa[1][0] = ds_frag(dp1, d4, pw[1][0], 0);
-            if (f == 3 * NQF / 4) sa[1][1] = ds_frag(dp1, d4, pw[1][1], 1);
+            dk[0][f % C::NDK] = mfma32(as_bf16x8(sa[0][f / C::NDK]), qf[f], dk[0][f % C::NDK]);
+#pragma unroll
+            for (int q = f * 8 / NQF; q < (f + 1) * 8 / NQF; ++q) {
+                sa[1][q >> 2][q & 3] = ds_pair(dp1, d4, pw[1][q >> 2][q & 3], q >> 2, q & 3);
+                asm volatile("" ::"v"(sa[1][q >> 2][q & 3]));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         // dK of key tile 1
 #pragma unroll
-        for (int f = 0; f < NQF; ++f) dk[1][f % C::NDK] = mfma32(sa[1][f / C::NDK], qf[f], dk[1][f % C::NDK]);
+        for (int f = 0; f < NQF; ++f) dk[1][f % C::NDK] = mfma32(as_bf16x8(sa[1][f / C::NDK]), qf[f], dk[1][f % C::NDK]);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));   // accumulators stay in AGPRs
+        if (next >= 0) read_ahead(next);
     }
 
-    __device__ void first(int s, int par, int m, bool mask) {
-        (void)s;
+    __device__ void first(int s, int par, int m, bool mask, const typename DkvShared<DQK, DV>::Dma& d) {
         (void)par;
         (void)m;
         (void)mask;
+        fire_all(d);
+        read_ahead(s);
     }
-    __device__ void step(int s, int sp, int par, int m, bool mask) {
-        (void)s;
+    __device__ void step(int s, int sp, int par, int m, bool mask, const typename DkvShared<DQK, DV>::Dma& d) {
         (void)m;
         (void)mask;
-        finish(sp, par ^ 1);
+        finish<true>(sp, par ^ 1, d, s);
     }
-    __device__ void drain(int sp, int par) { finish(sp, par); }
+    __device__ void drain(int sp, int par) {
+        typename DkvShared<DQK, DV>::Dma d{};
+        finish<false>(sp, par, d, -1);
+    }
+    __device__ void fire_all(const typename DkvShared<DQK, DV>::Dma& d) const {
+#pragma unroll
+        for (int j = 0; j < C::NDMA_S; ++j) sh.fire(d, j);
+    }
+    __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_S>(); }
 
     __device__ void store() const {
         uint16_t* g = a.dk + sh.b * a.dk_sb + sh.hk * a.dk_sh;
@@ -727,15 +802,19 @@ struct DkvSWave {
     }
 };
 
-// Steps, barriers and loads, shared by both roles.  Step t (stage t % 3, P
-// parity t % 2) may read stage t - 1; stage t + 1 is enqueued after the
-// barrier that ends step t - 1.  The loop body is one straight-line block per
-// role (masking is a per-element select, not a branch) so that the
-// accumulators stay put in registers across iterations.
+// Steps, barriers and loads, shared by both roles.  Step t uses ring stage
+// t % NS and may read stage t - 1; its P goes to LDS parity t % 2.  The loads
+// of step t + 2 go out from inside step t's MFMA stream (their stage was last
+// read in step t - 1, before the barrier that opens step t), so each tile has
+// two steps to land; past the last step they re-read the first step's rows
+// into the free stage, which keeps the step bodies free of branches.  The
+// loop body is one straight-line block per role (masking is a fix-up on the
+// packed P, outside the MFMA block) so the accumulators stay put in registers.
 template <int DQK, int DV, class Role>
 __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
                                          Role& role) {
     using C = DkvCfg<DQK, DV>;
+    static_assert(C::NDMA_P <= C::NCQ && C::NDMA_S <= C::NCV, "loads must fit between the first MFMAs");
     const BwdArgs& a = sh.a;
     const bool ragged_keys = sh.n_base + C::BN > a.Sk;
     const int shift = a.Sk - a.Sq;
@@ -744,25 +823,39 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
 
     int m = -1;
     if (!steps.start(&m)) return;
-    sh.issue(steps.hq(), m, 0);
+    const int h0 = steps.hq(), m0 = m;
+    typename DkvShared<DQK, DV>::Dma d;
+    sh.plan(d, h0, m0, 0);
+    role.fire_all(d);
+    int m1 = -1, m2 = -1;
+    bool have1 = steps.next(&m1);                   // step t + 1
+    sh.plan(d, have1 ? steps.hq() : h0, have1 ? m1 : m0, 1);
+    role.fire_all(d);
+    bool have2 = have1 && steps.next(&m2);          // step t + 2
+    const int h2n = have2 ? steps.hq() : h0;
+    role.wait_oldest();
+    __syncthreads();
+    sh.plan(d, h2n, have2 ? m2 : m0, 2);
+    role.first(0, 0, m, need_mask(m), d);
     int t = 0;
-    int mn = -1;
-    bool more = steps.next(&mn);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (more) sh.issue(steps.hq(), mn, 1);
-    role.first(0, 0, m, need_mask(m));
-    while (more) {
-        m = mn;
+    while (have1) {
         ++t;
-        more = steps.next(&mn);
-        wait_vmcnt<0>();
+        m = m1;
+        int m3 = -1;
+        const bool have3 = have2 && steps.next(&m3);
+        const int h3 = have3 ? steps.hq() : h0;
+        role.wait_oldest();
         __syncthreads();
-        if (more) sh.issue(steps.hq(), mn, (t + 1) % 3);
-        role.step(t % 3, (t + 2) % 3, t & 1, m, need_mask(m));
+        sh.plan(d, h3, have3 ? m3 : m0, (t + 2) % C::NS);
+        role.step(t % C::NS, (t + C::NS - 1) % C::NS, t & 1, m, need_mask(m), d);
+        have1 = have2;
+        m1 = m2;
+        have2 = have3;
+        m2 = m3;
     }
+    wait_vmcnt<0>();                                // no load may land in LDS after the workgroup ends
     __syncthreads();
-    role.drain(t % 3, t & 1);
+    role.drain(t % C::NS, t & 1);
 }
 
 template <int DQK, int DV>
@@ -772,10 +865,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps role and load addresses scalar
-    const int BH = a.B * a.Hk;
-    const int id = blockIdx.x;
-    const int kb = id / BH;                        // longest key columns first under a causal mask
-    const int bh = id - kb * BH;
+    // items (b, KV head, key block), head-major; within a head the longest key
+    // columns (most kept query blocks under a causal mask) first
+    const int item = xcd_item(blockIdx.x, a.n_kb * a.B * a.Hk);
+    if (item < 0) return;
+    const int bh = item / a.n_kb;
+    const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
@@ -794,8 +889,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
 template <int DQK, int DV, int WR>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
     using C = DqCfg<DQK, DV, WR>;
-    const int64_t grid = int64_t(a.n_qb) * a.B * a.Hq;
-    if (grid == 0) return hipSuccess;
+    const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
+    if (items == 0) return hipSuccess;
+    const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq<DQK, DV, WR>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
@@ -807,8 +903,9 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
 template <int DQK, int DV>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<DQK, DV>;
-    const int64_t grid = int64_t(a.n_kb) * a.B * a.Hk;
-    if (grid == 0) return hipSuccess;
+    const int64_t items = int64_t(a.n_kb) * a.B * a.Hk;
+    if (items == 0) return hipSuccess;
+    const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);

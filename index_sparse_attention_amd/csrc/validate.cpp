@@ -93,8 +93,9 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         return ISATTN_ERR_SHAPE;
     if (s.heads_q % s.heads_k != 0) return ISATTN_ERR_SHAPE;
     if (s.seqlen_q >= (1 << 30) || s.seqlen_k >= (1 << 30)) return ISATTN_ERR_SHAPE;
-    if (int64_t(s.batch) * s.heads_q * cdiv(s.seqlen_q, kBlock) >= (int64_t(1) << 31) ||
-        int64_t(s.batch) * s.heads_k * cdiv(s.seqlen_k, kBlock) >= (int64_t(1) << 31))
+    // block-level work items (padded to a multiple of 8 workgroups) must fit an int
+    if (int64_t(s.batch) * s.heads_q * cdiv(s.seqlen_q, kBlock) >= (int64_t(1) << 31) - 8 ||
+        int64_t(s.batch) * s.heads_k * cdiv(s.seqlen_k, kBlock) >= (int64_t(1) << 31) - 8)
         return ISATTN_ERR_SHAPE;
     if (!supported_dims(s.dim_qk, s.dim_v)) return ISATTN_ERR_UNSUPPORTED;
     if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT)
