@@ -285,60 +285,70 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK/dV pass
 //
-// One workgroup per (batch, KV head, 128-key block), four waves in two roles
-// over the same 128 keys:
-//   P waves (0, 1), 64 keys each: K rows resident in registers, dV
-//     accumulators.  Step t: S = Q_t K^T and P_t = exp2(S * scale * log2e -
-//     lse2), handed to the partner through LDS; between those, the MFMAs of
-//     dV += P_{t-1}^T dO_{t-1}.
-//   dS waves (2, 3), the same 64 keys: V rows resident, dK accumulators.
-//     Step t finishes query slice t-1: dP = dO V^T, dS = P (dP - delta) with
-//     P from the partner, dK += dS^T Q; the dS arithmetic of one 32-key tile
-//     runs between the MFMAs of the other.
+// One workgroup per (batch, KV head, 128-key block), eight waves in two roles;
+// the SIMD that runs P wave r also runs dS wave r, so each one's arithmetic
+// fills the other's MFMA gaps:
+//   P waves 0-3, 32 keys each: K rows resident in registers, dV accumulators.
+//     Step t: S = Q_t K^T and P_t = exp2(S * scale * log2e - lse2), handed to
+//     the partner through LDS; the dV += P_{t-1}^T dO_{t-1} MFMAs of the
+//     previous step are issued between the P arithmetic.
+//   dS waves 4-7, the same keys: V rows resident, dK accumulators.  Step t
+//     finishes query slice t-1: dP = dO V^T, dS = P (dP - delta) with P from
+//     the partner, dK += dS^T Q.
 // A step is BM query rows of one kept query block of one head of the GQA
-// group.  The Q/dO tiles and the rows' lse2/delta go through a 3-stage LDS
-// ring filled by direct global->LDS loads; step t reads stages t and t-1
-// while stage t+1 lands.  Each 64-key wave feeds every Q/dO operand it reads
-// from LDS to two 32-key MFMA tiles.
+// group.  The Q/dO tiles and the rows' lse2/delta go through a 4-stage LDS
+// ring filled by direct global->LDS loads issued two steps ahead.
 // ---------------------------------------------------------------------------
 template <int DQK, int DV>
 struct DkvCfg {
     static constexpr int BN = 128;                          // keys per workgroup
     static constexpr int BM = 32;                           // query rows per step
-    static constexpr int NW = 4;
-    static constexpr int NT = 256;
+    static constexpr int NW = 8;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NR = NW / 2;                       // waves per role (32 keys each)
     static constexpr int Q_BYTES = BM * DQK * 2;
     static constexpr int O_BYTES = BM * DV * 2;
     static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[64], delta[64] (BM used)
     static constexpr int STAGE_BYTES = STAT_OFF + 2 * 64 * 4;
-    static constexpr int NU = 4;                            // P fragments (kt, cc) per P wave and step
-    static constexpr int XBUF_BYTES = 2 * NU * 1024;        // P of both P waves for one step
+    static constexpr int NU = 2;                            // P fragments (cc) per P wave and step
+    static constexpr int XBUF_BYTES = NR * NU * 1024;       // P of all P waves for one step
     static constexpr int NS = 4;                            // LDS ring stages (loads run two steps ahead)
     static constexpr int X_OFF = NS * STAGE_BYTES;
     static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
-    static constexpr int NQI = Q_BYTES / 1024 / NW;         // 1 KiB loads per wave per Q tile
-    static constexpr int NOI = O_BYTES / 1024 / NW;
-    static constexpr int NDMA_P = NQI + NOI;                // loads a P wave issues per step
-    static constexpr int NDMA_S = NQI + NOI + 1;            // a dS wave also loads one statistics row
+    static constexpr int NQI = Q_BYTES / 1024;              // 1 KiB loads per Q tile
+    static constexpr int NI = (Q_BYTES + O_BYTES) / 1024;   // 1 KiB loads per step
+    static constexpr int KMAX = (NI + NW - 1) / NW;         // tile loads per wave per step
+    static constexpr int NDMA_P = KMAX;                     // loads a P wave issues per step
+    static constexpr int NDMA_S = KMAX + 1;                 // a dS wave also loads one statistics row
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDK = DQK / 32;
     static constexpr int NDV = DV / 32;
-    static_assert(Q_BYTES % (1024 * NW) == 0 && O_BYTES % (1024 * NW) == 0, "tiles split into whole wave loads");
+    static_assert(Q_BYTES % 1024 == 0 && O_BYTES % 1024 == 0, "tiles split into whole wave loads");
     static_assert(STAGE_BYTES % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(NDMA_P <= NCQ && NDMA_S <= NCV, "loads must fit between the first MFMAs");
 };
 
-// Step sequence of one workgroup: (query head of the GQA group, kept query
-// block, BM-row part).  Every wave walks it identically.  The kept query
-// blocks of a head are read 64 at a time into a register (one per lane).
+// Step sequence of one workgroup: every BM-row part of every kept query
+// block of every head of the GQA group.  Every wave walks it identically.
+// Visibility (causal) is decided per block; parts of a visible block that no
+// row of sees, or that lie past Sq, are still stepped through: their P is
+// masked to zero or their rows' lse2 is +inf.  The kept query blocks of a
+// head are read 64 at a time into a register (one per lane).
 template <int BM>
 struct DkvSteps {
     static constexpr int PARTS = kBlock / BM;
     const BwdArgs& a;
     int b, hk, kb, n_base, shift, lane;
-    int gi = 0, it = 0, part = 0, count = 0, first = 0, qb = 0;
+    int gi = 0, it = -1, part = 0, count = 0, first = 0;
+    int m = 0;                                      // first row of the current step
     const int32_t* list = nullptr;
     int chunk = 0, chunk_base = -1;
+    // the current head's Q, dO and statistics rows
+    const uint16_t* qh = nullptr;
+    const uint16_t* oh = nullptr;
+    const float* lh = nullptr;
+    const float* dh = nullptr;
 
     __device__ DkvSteps(const BwdArgs& a_, int b_, int hk_, int kb_, int lane_)
         : a(a_), b(b_), hk(hk_), kb(kb_), n_base(kb_ * kBlock), shift(a_.Sk - a_.Sq), lane(lane_) {}
@@ -346,11 +356,17 @@ struct DkvSteps {
     __device__ int hq() const { return hk * a.G + gi; }
 
     __device__ void load_head() {
+        const int h = hq();
+        qh = a.q + b * a.q_sb + h * a.q_sh;
+        oh = a.dO + b * a.do_sb + h * a.do_sh;
+        const int64_t srow = (int64_t(b) * a.Hq + h) * a.stat_ld;
+        lh = a.lse2 + srow;
+        dh = a.delta + srow;
         list = nullptr;
         first = 0;
         chunk_base = -1;
         if (a.mask_kind == 1) {
-            const int hm = hq() * a.Hm / a.Hq;
+            const int hm = h * a.Hm / a.Hq;
             const int r = (b * a.Hm + hm) * a.n_kb + kb;
             const int beg = a.k2q_ptr[r];
             count = a.k2q_ptr[r + 1] - beg;
@@ -372,46 +388,33 @@ struct DkvSteps {
         }
         return __builtin_amdgcn_readlane(chunk, it & 63);
     }
-    // first row of (qb, part), -1 if out of range or no row of it sees the key block
-    __device__ int row_of() const {
-        const int m = qb * kBlock + part * BM;
-        if (qb < 0 || qb >= a.n_qb || m >= a.Sq) return -1;
-        if (a.causal && min(m + BM - 1, a.Sq - 1) + shift < n_base) return -1;
-        return m;
-    }
-    __device__ bool start(int* m) {
-        load_head();
-        while (count == 0) {
-            if (++gi >= a.G) return false;
-            load_head();
-        }
-        it = 0;
-        part = 0;
-        qb = qb_at();
-        *m = row_of();
-        return *m >= 0 || next(m);
-    }
-    __device__ bool next(int* m) {
-        if (part + 1 < PARTS) {                     // common case: next part of the same block
-            ++part;
-            *m = row_of();
-            if (*m >= 0) return true;
-        }
+    // next kept block some row of which sees the key block; false at the end
+    __device__ bool next_block() {
         for (;;) {
-            if (++part >= PARTS) {
-                part = 0;
-                if (++it >= count) {
-                    do {
-                        if (++gi >= a.G) return false;
-                        load_head();
-                    } while (count == 0);
-                    it = 0;
-                }
-                qb = qb_at();
+            ++it;
+            while (it >= count) {
+                if (++gi >= a.G) return false;
+                load_head();
+                it = 0;
             }
-            *m = row_of();
-            if (*m >= 0) return true;
+            const int qb = qb_at();
+            if (qb < 0 || qb >= a.n_qb) continue;  // malformed entry: nothing to do
+            if (a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base) continue;
+            part = 0;
+            m = qb * kBlock;
+            return true;
         }
+    }
+    __device__ bool start() {
+        load_head();
+        return next_block();
+    }
+    __device__ bool next() {
+        if (++part < PARTS) {
+            m += BM;
+            return true;
+        }
+        return next_block();
     }
 };
 
@@ -422,35 +425,46 @@ struct DkvShared {
     uint16_t* lds;
     uint32_t lds_base;
     int w, lane, l32, h2, b, hk, n_base;
-    uint32_t qoff[C::NQI], ooff[C::NOI];            // per-lane byte offsets of the tile loads (no clamping)
+    uint32_t toff[C::KMAX];                         // per-lane byte offsets of this wave's tile loads (no clamping)
     uint32_t soff;                                  // per-lane byte offset of the statistics load
 
-    // The loads of one step: wave-uniform source pointers and LDS stage, per-lane offsets.
+    // The loads of one step: wave-uniform source pointers (a head's rows) and
+    // LDS stage, per-lane byte offsets (the step's rows included).
     struct Dma {
         const uint16_t* q;
         const uint16_t* o;
         const float* st;
         uint32_t sb;
-        uint32_t qo[C::NQI], oo[C::NOI];
+        uint32_t off[C::KMAX];
+        uint32_t soff;
     };
+
+    // 1 KiB tile load k of this wave: instruction j = w + NW * k of the step's
+    // Q tile (j < NQI) then dO tile; a j past the last re-issues j - NW, which
+    // writes the same bytes again.
+    static __device__ int load_index(int w, int k) {
+        const int j = w + C::NW * k;
+        return j < C::NI ? j : j - C::NW;
+    }
 
     __device__ DkvShared(const BwdArgs& a_, uint16_t* lds_, int w_, int lane_, int b_, int hk_, int n_base_)
         : a(a_), lds(lds_), lds_base(lds_address(lds_)), w(w_), lane(lane_), l32(lane_ & 31), h2(lane_ >> 5),
           b(b_), hk(hk_), n_base(n_base_) {
 #pragma unroll
-        for (int k = 0; k < C::NQI; ++k) qoff[k] = tile_off<DQK>(w + C::NW * k, C::BM, a.q_ss);
-#pragma unroll
-        for (int k = 0; k < C::NOI; ++k) ooff[k] = tile_off<DV>(w + C::NW * k, C::BM, a.do_ss);
+        for (int k = 0; k < C::KMAX; ++k) toff[k] = load_off(load_index(w, k), C::BM);
         soff = uint32_t(4 * (lane < C::BM ? swap23(lane) : 0));   // lanes past BM re-read the first row
     }
-    // byte offset of this lane's 16 bytes in 1 KiB load j of a swizzled tile
-    // (tile row t at LDS row swap23(t)); tile rows past `lim` read row lim
+    // byte offset of this lane's 16 bytes in 1 KiB load j (Q or dO part) of a
+    // swizzled tile (tile row t at LDS row swap23(t)); rows past `lim` read row lim
     template <int D>
-    __device__ uint32_t tile_off(int j, int lim, int64_t ss) const {
-        const int e = 512 * j + 8 * lane;
+    __device__ uint32_t tile_off(int jj, int lim, int64_t ss) const {
+        const int e = 512 * jj + 8 * lane;
         const int r = e / D;
         const int c = ((e - r * D) >> 3) ^ chunk_swz(r);
         return uint32_t(min(swap23(r), lim)) * uint32_t(ss * 2) + uint32_t(16 * c);
+    }
+    __device__ uint32_t load_off(int j, int lim) const {
+        return j < C::NQI ? tile_off<DQK>(j, lim, a.q_ss) : tile_off<DV>(j - C::NQI, lim, a.do_ss);
     }
     __device__ const uint16_t* q_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2); }
     __device__ const uint16_t* do_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2) + C::Q_BYTES / 2; }
@@ -461,37 +475,46 @@ struct DkvShared {
         return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + (wr * C::NU + u) * 1024 + lane * 16;
     }
 
-    // Plan the loads of step (hq, m) into stage s.
-    __device__ void plan(Dma& d, int hq, int m, int s) const {
+    // Plan the loads of the steps' current step into stage s.
+    __device__ void plan(Dma& d, const DkvSteps<C::BM>& st, int s) const {
+        const int m = st.m;
         d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
-        d.q = a.q + b * a.q_sb + hq * a.q_sh + int64_t(m) * a.q_ss;
-        d.o = a.dO + b * a.do_sb + hq * a.do_sh + int64_t(m) * a.do_ss;
-        d.st = (w == 2 ? a.lse2 : a.delta) + (int64_t(b) * a.Hq + hq) * a.stat_ld + m;
+        d.q = st.qh;
+        d.o = st.oh;
+        d.st = (w & 1) == 0 ? st.lh : st.dh;
+        d.soff = soff + uint32_t(4 * m);
         if (m + C::BM <= a.Sq) {
+            const uint32_t mq = uint32_t(m) * uint32_t(a.q_ss * 2), mo = uint32_t(m) * uint32_t(a.do_ss * 2);
 #pragma unroll
-            for (int k = 0; k < C::NQI; ++k) d.qo[k] = qoff[k];
-#pragma unroll
-            for (int k = 0; k < C::NOI; ++k) d.oo[k] = ooff[k];
+            for (int k = 0; k < C::KMAX; ++k) d.off[k] = toff[k] + (load_index(w, k) < C::NQI ? mq : mo);
         } else {                                    // ragged tail: rows past Sq re-read row Sq - 1
-            const int lim = a.Sq - 1 - m;
+            const int mb = min(m, a.Sq - 1);
+            const uint32_t mq = uint32_t(mb) * uint32_t(a.q_ss * 2), mo = uint32_t(mb) * uint32_t(a.do_ss * 2);
 #pragma unroll
-            for (int k = 0; k < C::NQI; ++k) d.qo[k] = tile_off<DQK>(w + C::NW * k, lim, a.q_ss);
-#pragma unroll
-            for (int k = 0; k < C::NOI; ++k) d.oo[k] = tile_off<DV>(w + C::NW * k, lim, a.do_ss);
+            for (int k = 0; k < C::KMAX; ++k) {
+                const int j = load_index(w, k);
+                d.off[k] = load_off(j, a.Sq - 1 - mb) + (j < C::NQI ? mq : mo);
+            }
         }
     }
-    // Load j of this wave: Q tile parts, dO tile parts, then (dS waves) the
-    // statistics row: lse2 by wave 2, delta by wave 3, 64 lanes (rows past BM
-    // land in unused slots).  LDS position L holds row swap23(L) of the step.
-    __device__ void fire(const Dma& d, int j) const {
-        if (j < C::NQI) dma16(d.q, d.qo[j], d.sb + 1024 * (w + C::NW * j));
-        else if (j < C::NQI + C::NOI)
-            dma16(d.o, d.oo[j - C::NQI], d.sb + C::Q_BYTES + 1024 * (w + C::NW * (j - C::NQI)));
-        else dma4(d.st, soff, d.sb + uint32_t(C::STAT_OFF + (w - 2) * 256));
+    // Point a plan at another stage (re-loads its rows there).
+    __device__ void restage(Dma& d, int s) const { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); }
+
+    // Load k of this wave (k < KMAX: tile part; k == KMAX: the statistics row,
+    // dS waves only -- lse2 by even waves, delta by odd ones, 64 lanes, rows
+    // past BM landing in unused slots).  LDS position L holds row swap23(L).
+    __device__ void fire(const Dma& d, int k) const {
+        if (k < C::KMAX) {
+            const int j = load_index(w, k);
+            const bool is_q = j < C::NQI;
+            dma16(is_q ? d.q : d.o, d.off[k], d.sb + uint32_t(is_q ? 1024 * j : C::Q_BYTES + 1024 * (j - C::NQI)));
+        } else {
+            dma4(d.st, d.soff, d.sb + uint32_t(C::STAT_OFF + (w & 1) * 256));
+        }
     }
 };
 
-// P wave: S, P, dV.
+// P wave: S, P, dV for 32 keys.
 template <int DQK, int DV>
 struct DkvPWave {
     using C = DkvCfg<DQK, DV>;
@@ -500,26 +523,22 @@ struct DkvPWave {
     const DkvShared<DQK, DV>& sh;
     const BwdArgs& a;
     int wr;
-    bf16x8_t kB[2][C::NCQ];                         // K rows of the wave's two 32-key tiles
-    f32x16_t dv[2][C::NDV];
-    int qmin[2];                                    // first query row that sees the lane's key of tile kt
+    bf16x8_t kB[C::NCQ];                            // K rows of the wave's 32 keys
+    f32x16_t dv[C::NDV];
+    int qmin;                                       // first query row that sees the lane's key
     // operands of the dV update of the step just computed, read ahead across the barrier
     bf16x8_t nfr[NF];                               // its dO^T fragments
-    u32x4_t npp[2][2];                              // its P, (kt, cc)
+    u32x4_t npp[2];                                 // its P, (cc)
 
     __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
-        const int shift = a.Sk - a.Sq;
+        const int key = sh.n_base + 32 * wr + sh.l32;
+        const bool in = key < a.Sk;
+        const uint16_t* kr = a.k + sh.b * a.k_sb + sh.hk * a.k_sh + int64_t(in ? key : 0) * a.k_ss + 8 * sh.h2;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int key = sh.n_base + 64 * wr + 32 * kt + sh.l32;
-            const bool in = key < a.Sk;
-            const uint16_t* kr = a.k + sh.b * a.k_sb + sh.hk * a.k_sh + int64_t(in ? key : 0) * a.k_ss + 8 * sh.h2;
+        for (int c = 0; c < C::NCQ; ++c) kB[c] = in ? gload_operand(kr + 16 * c) : bf16x8_t{};
+        qmin = in ? (a.causal ? key - (a.Sk - a.Sq) : -(1 << 30)) : INT_MAX;   // rows < 2^30: no overflow below
 #pragma unroll
-            for (int c = 0; c < C::NCQ; ++c) kB[kt][c] = in ? gload_operand(kr + 16 * c) : bf16x8_t{};
-            qmin[kt] = in ? (a.causal ? key - shift : -(1 << 30)) : INT_MAX;   // rows < 2^30: tau cannot overflow
-#pragma unroll
-            for (int j = 0; j < C::NDV; ++j) dv[kt][j] = f32x16_t{};
-        }
+        for (int j = 0; j < C::NDV; ++j) dv[j] = f32x16_t{};
     }
 
     __device__ bf16x8_t dot_frag(const uint16_t* sdO, int f) const {   // f = (cc, j)
@@ -528,23 +547,23 @@ struct DkvPWave {
 
     // One step: S of stage s and P of it (to LDS parity par, read by the
     // partner); with PREV, the dV MFMAs of the previous step (operands read
-    // ahead into nfr / npp) are issued between the P arithmetic, one bf16
-    // pair of P per MFMA.  Masked steps fix the packed P up afterwards.  At
-    // the end the operands of this step's own dV update are read ahead.
+    // ahead into nfr / npp) are issued between the P arithmetic.  Masked
+    // steps fix the packed P up afterwards.  At the end the operands of this
+    // step's own dV update are read ahead.
     template <bool PREV>
     __device__ void body(int s, int par, int m, bool mask, const Dma& d) {
         const uint16_t* sQ = sh.q_tile(s);
-        f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+        f32x16_t st = f32x16_t{};
         {
-            bf16x8_t qa[C::NCQ];
+            constexpr int PF = 4;
+            bf16x8_t qa[PF];
 #pragma unroll
-            for (int c = 0; c < C::NCQ; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
-            __builtin_amdgcn_sched_barrier(0);     // all Q reads in flight before the first MFMA
+            for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
             // S MFMAs; this wave's loads for two steps ahead go out between them
 #pragma unroll
             for (int c = 0; c < C::NCQ; ++c) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(qa[c], kB[kt][c], st[kt]);
+                st = mfma32(qa[c % PF], kB[c], st);
+                if (c + PF < C::NCQ) qa[c % PF] = row_operand_swz<DQK>(sQ, sh.l32, 16 * (c + PF) + 8 * sh.h2);
                 if (c < C::NDMA_P) sh.fire(d, c);
             }
         }
@@ -552,62 +571,50 @@ struct DkvPWave {
         float4 l4[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * sh.h2);
-        __builtin_amdgcn_sched_barrier(0);
 
-        // dV MFMAs k = (f, kt) of the previous step, f = (cc, j); P pairs q =
-        // (kt, cc, jj) of this step between them
-        constexpr int NK = 2 * NF;
-        constexpr int NQ = 16;
-        u32x4_t pn[2][2];
+        // dV MFMAs f = (cc, j) of the previous step; P pairs q = (cc, jj) of
+        // this step between them
+        constexpr int NQ = 8;
+        u32x4_t pn[2];
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            if (PREV) {
-                const int f = k >> 1, kt = k & 1;
-                const int cc = f / C::NDV, j = f % C::NDV;
-                dv[kt][j] = mfma32(as_bf16x8(npp[kt][cc]), nfr[f], dv[kt][j]);
-            }
+        for (int f = 0; f < NF; ++f) {
+            if (PREV) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), nfr[f], dv[f % C::NDV]);
 #pragma unroll
-            for (int q = k * NQ / NK; q < (k + 1) * NQ / NK; ++q) {
-                const int kt = q >> 3, cc = (q >> 2) & 1, jj = q & 3;
+            for (int q = f * NQ / NF; q < (f + 1) * NQ / NF; ++q) {
+                const int cc = q >> 2, jj = q & 3;
                 float p2[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int i = 8 * cc + 2 * jj + e;
                     const float4 lv = l4[i >> 2];
                     const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
-                    p2[e] = fast_exp2(fmaf(st[kt][i], a.scale_log2, -l));
+                    p2[e] = fast_exp2(fmaf(st[i], a.scale_log2, -l));
                 }
-                pn[kt][cc][jj] = pack_bf16x2(p2[0], p2[1]);
-                if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc)) = pn[kt][cc];
+                pn[cc][jj] = pack_bf16x2(p2[0], p2[1]);
+                if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, cc)) = pn[cc];
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         if (mask) {
             // pairs whose row is below the lane key's first visible row (causal)
             // or whose key is past Sk: clear the bf16 halves and rewrite
+            const int tau = qmin - m - 8 * sh.h2;   // first visible row offset of this lane
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int tau = qmin[kt] - m - 8 * sh.h2;   // first visible row offset of this lane
+            for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int o = 16 * cc + 2 * jj;
-                        const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
-                        pn[kt][cc][jj] &= keep;
-                    }
-                    *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc)) = pn[kt][cc];
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int o = 16 * cc + 2 * jj;
+                    const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
+                    pn[cc][jj] &= keep;
                 }
+                *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, cc)) = pn[cc];
             }
         }
         // read ahead the operands of this step's dV update (done next step)
         const uint16_t* sdO = sh.do_tile(s);
 #pragma unroll
         for (int f = 0; f < NF; ++f) nfr[f] = dot_frag(sdO, f);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) npp[kt][cc] = pn[kt][cc];
+        npp[0] = pn[0];
+        npp[1] = pn[1];
     }
 
     __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, par, m, mask, d); }
@@ -617,7 +624,7 @@ struct DkvPWave {
     }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
-        for (int j = 0; j < C::NDMA_P; ++j) sh.fire(d, j);
+        for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
     }
     // this wave's loads of the oldest outstanding step have landed (one newer step in flight)
     __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_P>(); }
@@ -626,39 +633,44 @@ struct DkvPWave {
         (void)sp;
         (void)par;
 #pragma unroll
-        for (int k = 0; k < 2 * NF; ++k) {
-            const int f = k >> 1, kt = k & 1;
-            const int cc = f / C::NDV, j = f % C::NDV;
-            dv[kt][j] = mfma32(as_bf16x8(npp[kt][cc]), nfr[f], dv[kt][j]);
-        }
+        for (int f = 0; f < NF; ++f) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), nfr[f], dv[f % C::NDV]);
     }
     __device__ void store() const {
         uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 16; ++i) {
+            const int n = sh.n_base + 32 * wr + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+            if (n < a.Sk) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int n = sh.n_base + 64 * wr + 32 * kt + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
-                if (n < a.Sk) {
-#pragma unroll
-                    for (int j = 0; j < C::NDV; ++j) g[n * a.dv_ss + 32 * j + sh.l32] = to_bf16(dv[kt][j][i]);
-                }
+                for (int j = 0; j < C::NDV; ++j) g[n * a.dv_ss + 32 * j + sh.l32] = to_bf16(dv[j][i]);
             }
+        }
     }
 };
 
-// dS wave: dP, dS, dK.
+// dS wave: dP, dS, dK for 32 keys.
 template <int DQK, int DV>
 struct DkvSWave {
     using C = DkvCfg<DQK, DV>;
+    using Dma = typename DkvShared<DQK, DV>::Dma;
     const DkvShared<DQK, DV>& sh;
     const BwdArgs& a;
     int wr;
-    bf16x8_t vB[2][C::NCV];
-    f32x16_t dk[2][C::NDK];
+    bf16x8_t vB[C::NCV];
+    f32x16_t dk[C::NDK];
     // operands of the next slice to finish, read ahead across the barrier
     bf16x8_t noa[C::NCV];                           // its dO rows
     float4 nd4[4];                                  // its delta rows
+
+    __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
+        const int key = sh.n_base + 32 * wr + sh.l32;
+        const bool in = key < a.Sk;
+        const uint16_t* vr = a.v + sh.b * a.v_sb + sh.hk * a.v_sh + int64_t(in ? key : 0) * a.v_ss + 8 * sh.h2;
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) vB[c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
+#pragma unroll
+        for (int j = 0; j < C::NDK; ++j) dk[j] = f32x16_t{};
+    }
 
     // read ahead the dO rows and delta of the slice in stage s
     __device__ void read_ahead(int s) {
@@ -670,26 +682,13 @@ struct DkvSWave {
         for (int g = 0; g < 4; ++g) nd4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
     }
 
-    __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const int key = sh.n_base + 64 * wr + 32 * kt + sh.l32;
-            const bool in = key < a.Sk;
-            const uint16_t* vr = a.v + sh.b * a.v_sb + sh.hk * a.v_sh + int64_t(in ? key : 0) * a.v_ss + 8 * sh.h2;
-#pragma unroll
-            for (int c = 0; c < C::NCV; ++c) vB[kt][c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
-#pragma unroll
-            for (int j = 0; j < C::NDK; ++j) dk[kt][j] = f32x16_t{};
-        }
-    }
-
-    // dS pair (cc, jj) of key tile kt: packed bf16 of P * (dP - delta)
-    __device__ uint32_t ds_pair(const f32x16_t& dpt, const float4 (&d4)[4], uint32_t pw, int cc, int jj) const {
+    // dS pair (cc, jj): packed bf16 of P * (dP - delta)
+    __device__ uint32_t ds_pair(const f32x16_t& dpt, uint32_t pw, int cc, int jj) const {
         float r[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int i = 8 * cc + 2 * jj + e;
-            const float4 dv4 = d4[i >> 2];
+            const float4 dv4 = nd4[i >> 2];
             const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
             const float p = e == 0 ? bf16_lo(pw) : bf16_hi(pw);
             r[e] = p * (dpt[i] - dl);
@@ -697,108 +696,71 @@ struct DkvSWave {
         return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the query slice in stage s whose P is in LDS parity par: dP of
-    // key tile 0, dP of tile 1 with dS of tile 0 between its MFMAs, dK of tile
-    // 0 with dS of tile 1 between its MFMAs, dK of tile 1.
-    // (dO rows and delta were read ahead into noa / nd4; with NEXT >= 0 the
-    // next slice's are read ahead at the end)
+    // Finish the query slice in stage s whose P is in LDS parity par (dO rows
+    // and delta were read ahead): dP, dS, dK.  With FIRE this wave's loads for
+    // two steps ahead go out between the dP MFMAs; with next >= 0 the next
+    // slice's dO rows and delta are read ahead at the end.
     template <bool FIRE>
-    __device__ void finish(int s, int par, const typename DkvShared<DQK, DV>::Dma& d, int next) {
+    __device__ void finish(int s, int par, const Dma& d, int next) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));
         const uint16_t* sQ = sh.q_tile(s);
-        const bf16x8_t (&oa)[C::NCV] = noa;
-        const float4 (&d4)[4] = nd4;
-        u32x4_t pw[2][2];
+        u32x4_t pw[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) pw[kt][cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, 2 * kt + cc));
+        for (int cc = 0; cc < 2; ++cc) pw[cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, cc));
         constexpr int NQF = 2 * C::NDK;            // Q^T fragments (cc, j)
         bf16x8_t qf[NQF];
-        f32x16_t dp0 = f32x16_t{}, dp1 = f32x16_t{};
-        u32x4_t sa[2][2];
-        // dP of key tile 0, Q^T fragments read and (FIRE) this wave's loads for two steps ahead issued between
+        f32x16_t dp = f32x16_t{};
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
-            dp0 = mfma32(oa[c], vB[0][c], dp0);
+            dp = mfma32(noa[c], vB[c], dp);
             if (FIRE && c < C::NDMA_S) sh.fire(d, c);
 #pragma unroll
-            for (int f = c * NQF / (2 * C::NCV); f < (c + 1) * NQF / (2 * C::NCV); ++f)
+            for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f)
                 qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
-            __builtin_amdgcn_sched_barrier(0);
         }
-        // dP of key tile 1; dS of tile 0 (8 pairs) and the rest of Q^T between
+        u32x4_t sa[2];
 #pragma unroll
-        for (int c = 0; c < C::NCV; ++c) {
-            dp1 = mfma32(oa[c], vB[1][c], dp1);
+        for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, pw[q >> 2][q & 3], q >> 2, q & 3);
 #pragma unroll
-            for (int f = (C::NCV + c) * NQF / (2 * C::NCV); f < (C::NCV + c + 1) * NQF / (2 * C::NCV); ++f)
-                qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+        for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
 #pragma unroll
-            for (int q = c * 8 / C::NCV; q < (c + 1) * 8 / C::NCV; ++q) {
-                sa[0][q >> 2][q & 3] = ds_pair(dp0, d4, pw[0][q >> 2][q & 3], q >> 2, q & 3);
-                asm volatile("" ::"v"(sa[0][q >> 2][q & 3]));   // pin the pair between these MFMAs
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // dK of key tile 0; dS of tile 1 between
-#pragma unroll
-        for (int f = 0; f < NQF; ++f) {
-            dk[0][f % C::NDK] = mfma32(as_bf16x8(sa[0][f / C::NDK]), qf[f], dk[0][f % C::NDK]);
-#pragma unroll
-            for (int q = f * 8 / NQF; q < (f + 1) * 8 / NQF; ++q) {
-                sa[1][q >> 2][q & 3] = ds_pair(dp1, d4, pw[1][q >> 2][q & 3], q >> 2, q & 3);
-                asm volatile("" ::"v"(sa[1][q >> 2][q & 3]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // dK of key tile 1
-#pragma unroll
-        for (int f = 0; f < NQF; ++f) dk[1][f % C::NDK] = mfma32(as_bf16x8(sa[1][f / C::NDK]), qf[f], dk[1][f % C::NDK]);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[kt][j]));   // accumulators stay in AGPRs
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));   // accumulators stay in AGPRs
         if (next >= 0) read_ahead(next);
     }
 
-    __device__ void first(int s, int par, int m, bool mask, const typename DkvShared<DQK, DV>::Dma& d) {
+    __device__ void first(int s, int par, int m, bool mask, const Dma& d) {
         (void)par;
         (void)m;
         (void)mask;
         fire_all(d);
         read_ahead(s);
     }
-    __device__ void step(int s, int sp, int par, int m, bool mask, const typename DkvShared<DQK, DV>::Dma& d) {
+    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) {
         (void)m;
         (void)mask;
         finish<true>(sp, par ^ 1, d, s);
     }
     __device__ void drain(int sp, int par) {
-        typename DkvShared<DQK, DV>::Dma d{};
+        Dma d{};
         finish<false>(sp, par, d, -1);
     }
-    __device__ void fire_all(const typename DkvShared<DQK, DV>::Dma& d) const {
+    __device__ void fire_all(const Dma& d) const {
 #pragma unroll
-        for (int j = 0; j < C::NDMA_S; ++j) sh.fire(d, j);
+        for (int k = 0; k < C::NDMA_S; ++k) sh.fire(d, k);
     }
     __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_S>(); }
 
     __device__ void store() const {
         uint16_t* g = a.dk + sh.b * a.dk_sb + sh.hk * a.dk_sh;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 16; ++i) {
+            const int n = sh.n_base + 32 * wr + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+            if (n < a.Sk) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int n = sh.n_base + 64 * wr + 32 * kt + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
-                if (n < a.Sk) {
-#pragma unroll
-                    for (int j = 0; j < C::NDK; ++j) g[n * a.dk_ss + 32 * j + sh.l32] = to_bf16(dk[kt][j][i] * a.scale);
-                }
+                for (int j = 0; j < C::NDK; ++j) g[n * a.dk_ss + 32 * j + sh.l32] = to_bf16(dk[j][i] * a.scale);
             }
+        }
     }
 };
 
@@ -806,47 +768,46 @@ struct DkvSWave {
 // t % NS and may read stage t - 1; its P goes to LDS parity t % 2.  The loads
 // of step t + 2 go out from inside step t's MFMA stream (their stage was last
 // read in step t - 1, before the barrier that opens step t), so each tile has
-// two steps to land; past the last step they re-read the first step's rows
-// into the free stage, which keeps the step bodies free of branches.  The
+// two steps to land; past the last step they re-read the last planned step's
+// rows into the free stage, which keeps the step bodies free of branches.  The
 // loop body is one straight-line block per role (masking is a fix-up on the
 // packed P, outside the MFMA block) so the accumulators stay put in registers.
 template <int DQK, int DV, class Role>
 __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
                                          Role& role) {
     using C = DkvCfg<DQK, DV>;
-    static_assert(C::NDMA_P <= C::NCQ && C::NDMA_S <= C::NCV, "loads must fit between the first MFMAs");
     const BwdArgs& a = sh.a;
     const bool ragged_keys = sh.n_base + C::BN > a.Sk;
     const int shift = a.Sk - a.Sq;
     // some pair of step m is masked (rows past Sq need no mask: their lse2 is +inf)
     auto need_mask = [&](int m) { return ragged_keys || (a.causal && sh.n_base + C::BN - 1 > m + shift); };
-
-    int m = -1;
-    if (!steps.start(&m)) return;
-    const int h0 = steps.hq(), m0 = m;
+    if (!steps.start()) return;
     typename DkvShared<DQK, DV>::Dma d;
-    sh.plan(d, h0, m0, 0);
+    int m = steps.m;                                // step t
+    sh.plan(d, steps, 0);
     role.fire_all(d);
-    int m1 = -1, m2 = -1;
-    bool have1 = steps.next(&m1);                   // step t + 1
-    sh.plan(d, have1 ? steps.hq() : h0, have1 ? m1 : m0, 1);
+    bool have1 = steps.next();                      // step t + 1
+    int m1 = steps.m;
+    if (have1) sh.plan(d, steps, 1);
+    else sh.restage(d, 1);
     role.fire_all(d);
-    bool have2 = have1 && steps.next(&m2);          // step t + 2
-    const int h2n = have2 ? steps.hq() : h0;
+    bool have2 = have1 && steps.next();             // step t + 2
+    int m2 = steps.m;
     role.wait_oldest();
     __syncthreads();
-    sh.plan(d, h2n, have2 ? m2 : m0, 2);
+    if (have2) sh.plan(d, steps, 2);
+    else sh.restage(d, 2);
     role.first(0, 0, m, need_mask(m), d);
     int t = 0;
     while (have1) {
         ++t;
         m = m1;
-        int m3 = -1;
-        const bool have3 = have2 && steps.next(&m3);
-        const int h3 = have3 ? steps.hq() : h0;
+        const bool have3 = have2 && steps.next();
+        const int m3 = steps.m;
         role.wait_oldest();
         __syncthreads();
-        sh.plan(d, h3, have3 ? m3 : m0, (t + 2) % C::NS);
+        if (have3) sh.plan(d, steps, (t + 2) % C::NS);
+        else sh.restage(d, (t + 2) % C::NS);
         role.step(t % C::NS, (t + C::NS - 1) % C::NS, t & 1, m, need_mask(m), d);
         have1 = have2;
         m1 = m2;
@@ -859,7 +820,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
 }
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     using C = DkvCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
@@ -875,12 +836,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(BwdArgs a) {
     const int hk = bh - b * a.Hk;
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
     DkvSteps<C::BM> steps(a, b, hk, kb, lane);
-    if (w < 2) {
+    if (w < C::NR) {
         DkvPWave<DQK, DV> role(sh, w);
         dkdv_run<DQK, DV>(sh, steps, role);
         role.store();
     } else {
-        DkvSWave<DQK, DV> role(sh, w - 2);
+        DkvSWave<DQK, DV> role(sh, w - C::NR);
         dkdv_run<DQK, DV>(sh, steps, role);
         role.store();
     }

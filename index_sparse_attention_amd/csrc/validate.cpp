@@ -114,9 +114,11 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     if ((st = check_view(dk, nk)) != ISATTN_OK) return st;
     if ((st = check_view(dv, nk)) != ISATTN_OK) return st;
     if (nq > 0 && lse == nullptr) return ISATTN_ERR_NULL;
-    if (algo == ISATTN_ALGO_SPLIT && nq > 0 &&
-        (q->stride_s >= kMaxSplitRowStride || dO->stride_s >= kMaxSplitRowStride))
-        return ISATTN_ERR_STRIDE_ALIGN;
+    if (algo == ISATTN_ALGO_SPLIT && nq > 0) {
+        const int64_t rows = int64_t(cdiv(s.seqlen_q, kBlock)) * kBlock;
+        if (rows * q->stride_s * 2 >= (int64_t(1) << 31) || rows * dO->stride_s * 2 >= (int64_t(1) << 31))
+            return ISATTN_ERR_STRIDE_ALIGN;
+    }
 
     BwdArgs a{};
     a.mask_kind = ISATTN_MASK_DENSE;

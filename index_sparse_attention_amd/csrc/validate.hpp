@@ -12,9 +12,9 @@ namespace isattn {
 
 constexpr size_t kWsAlign = 256;
 
-// Largest sequence stride (elements) of Q and dO the SPLIT dK/dV pass accepts:
-// its direct-to-LDS loads address a tile's rows with 32-bit byte offsets.
-constexpr int64_t kMaxSplitRowStride = int64_t(1) << 22;
+// The SPLIT dK/dV pass addresses the rows of one (batch, head) slice of Q and
+// dO by 32-bit byte offsets from the slice's first row: n_qb * 128 rows times
+// the sequence stride must stay below 2^31 bytes.
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
