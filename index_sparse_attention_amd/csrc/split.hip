@@ -526,9 +526,7 @@ struct DkvPWave {
     bf16x8_t kB[C::NCQ];                            // K rows of the wave's 32 keys
     f32x16_t dv[C::NDV];
     int qmin;                                       // first query row that sees the lane's key
-    // operands of the dV update of the step just computed, read ahead across the barrier
-    bf16x8_t nfr[NF];                               // its dO^T fragments
-    u32x4_t npp[2];                                 // its P, (cc)
+    u32x4_t npp[2];                                 // P of the step just computed (cc), for its dV update
 
     __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -546,13 +544,19 @@ struct DkvPWave {
     }
 
     // One step: S of stage s and P of it (to LDS parity par, read by the
-    // partner); with PREV, the dV MFMAs of the previous step (operands read
-    // ahead into nfr / npp) are issued between the P arithmetic.  Masked
-    // steps fix the packed P up afterwards.  At the end the operands of this
-    // step's own dV update are read ahead.
+    // partner); with PREV, the dV MFMAs of the previous step (stage sp, its P
+    // kept in npp) are issued between the P arithmetic.  Masked steps fix the
+    // packed P up afterwards.
     template <bool PREV>
-    __device__ void body(int s, int par, int m, bool mask, const Dma& d) {
+    __device__ void body(int s, int sp, int par, int m, bool mask, const Dma& d) {
         const uint16_t* sQ = sh.q_tile(s);
+        const uint16_t* sdO = sh.do_tile(sp);
+        constexpr int PFD = 2;                      // dO^T fragments read this many ahead
+        bf16x8_t fr[PFD + 1];
+        if (PREV) {
+#pragma unroll
+            for (int f = 0; f < PFD; ++f) fr[f] = dot_frag(sdO, f);
+        }
         f32x16_t st = f32x16_t{};
         {
             constexpr int PF = 4;
@@ -578,7 +582,10 @@ struct DkvPWave {
         u32x4_t pn[2];
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            if (PREV) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), nfr[f], dv[f % C::NDV]);
+            if (PREV) {
+                if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(sdO, f + PFD);
+                dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), fr[f % (PFD + 1)], dv[f % C::NDV]);
+            }
 #pragma unroll
             for (int q = f * NQ / NF; q < (f + 1) * NQ / NF; ++q) {
                 const int cc = q >> 2, jj = q & 3;
@@ -609,31 +616,24 @@ struct DkvPWave {
                 *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, cc)) = pn[cc];
             }
         }
-        // read ahead the operands of this step's dV update (done next step)
-        const uint16_t* sdO = sh.do_tile(s);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) nfr[f] = dot_frag(sdO, f);
         npp[0] = pn[0];
         npp[1] = pn[1];
     }
 
-    __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, par, m, mask, d); }
-    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) {
-        (void)sp;
-        body<true>(s, par, m, mask, d);
-    }
+    __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, s, par, m, mask, d); }
+    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) { body<true>(s, sp, par, m, mask, d); }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
         for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
     }
     // this wave's loads of the oldest outstanding step have landed (one newer step in flight)
     __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_P>(); }
-    // dV update of the last step (operands already read ahead)
+    // dV update of the last step (stage sp)
     __device__ void drain(int sp, int par) {
-        (void)sp;
         (void)par;
+        const uint16_t* sdO = sh.do_tile(sp);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), nfr[f], dv[f % C::NDV]);
+        for (int f = 0; f < NF; ++f) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), dot_frag(sdO, f), dv[f % C::NDV]);
     }
     __device__ void store() const {
         uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
@@ -658,9 +658,6 @@ struct DkvSWave {
     int wr;
     bf16x8_t vB[C::NCV];
     f32x16_t dk[C::NDK];
-    // operands of the next slice to finish, read ahead across the barrier
-    bf16x8_t noa[C::NCV];                           // its dO rows
-    float4 nd4[4];                                  // its delta rows
 
     __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -672,23 +669,13 @@ struct DkvSWave {
         for (int j = 0; j < C::NDK; ++j) dk[j] = f32x16_t{};
     }
 
-    // read ahead the dO rows and delta of the slice in stage s
-    __device__ void read_ahead(int s) {
-        const uint16_t* sdO = sh.do_tile(s);
-#pragma unroll
-        for (int c = 0; c < C::NCV; ++c) noa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
-        const float* sD = sh.stats(s) + 64;         // delta slot follows the 64-float lse2 slot
-#pragma unroll
-        for (int g = 0; g < 4; ++g) nd4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
-    }
-
     // dS pair (cc, jj): packed bf16 of P * (dP - delta)
-    __device__ uint32_t ds_pair(const f32x16_t& dpt, uint32_t pw, int cc, int jj) const {
+    __device__ uint32_t ds_pair(const f32x16_t& dpt, const float4 (&d4)[4], uint32_t pw, int cc, int jj) const {
         float r[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int i = 8 * cc + 2 * jj + e;
-            const float4 dv4 = nd4[i >> 2];
+            const float4 dv4 = d4[i >> 2];
             const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
             const float p = e == 0 ? bf16_lo(pw) : bf16_hi(pw);
             r[e] = p * (dpt[i] - dl);
@@ -696,15 +683,23 @@ struct DkvSWave {
         return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the query slice in stage s whose P is in LDS parity par (dO rows
-    // and delta were read ahead): dP, dS, dK.  With FIRE this wave's loads for
-    // two steps ahead go out between the dP MFMAs; with next >= 0 the next
-    // slice's dO rows and delta are read ahead at the end.
+    // Finish the query slice in stage s whose P is in LDS parity par: dP, dS,
+    // dK.  With FIRE this wave's loads for two steps ahead go out between the
+    // dP MFMAs.
     template <bool FIRE>
-    __device__ void finish(int s, int par, const Dma& d, int next) {
+    __device__ void finish(int s, int par, const Dma& d) {
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));
         const uint16_t* sQ = sh.q_tile(s);
+        const uint16_t* sdO = sh.do_tile(s);
+        constexpr int PFO = 4;                      // dO rows read this many ahead
+        bf16x8_t oa[PFO];
+#pragma unroll
+        for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
+        const float* sD = sh.stats(s) + 64;         // delta slot follows the 64-float lse2 slot
+        float4 d4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
         u32x4_t pw[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) pw[cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, cc));
@@ -713,7 +708,8 @@ struct DkvSWave {
         f32x16_t dp = f32x16_t{};
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
-            dp = mfma32(noa[c], vB[c], dp);
+            dp = mfma32(oa[c % PFO], vB[c], dp);
+            if (c + PFO < C::NCV) oa[c % PFO] = row_operand_swz<DV>(sdO, sh.l32, 16 * (c + PFO) + 8 * sh.h2);
             if (FIRE && c < C::NDMA_S) sh.fire(d, c);
 #pragma unroll
             for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f)
@@ -721,29 +717,29 @@ struct DkvSWave {
         }
         u32x4_t sa[2];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, pw[q >> 2][q & 3], q >> 2, q & 3);
+        for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, d4, pw[q >> 2][q & 3], q >> 2, q & 3);
 #pragma unroll
         for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));   // accumulators stay in AGPRs
-        if (next >= 0) read_ahead(next);
     }
 
     __device__ void first(int s, int par, int m, bool mask, const Dma& d) {
         (void)par;
         (void)m;
         (void)mask;
+        (void)s;
         fire_all(d);
-        read_ahead(s);
     }
     __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) {
+        (void)s;
         (void)m;
         (void)mask;
-        finish<true>(sp, par ^ 1, d, s);
+        finish<true>(sp, par ^ 1, d);
     }
     __device__ void drain(int sp, int par) {
         Dma d{};
-        finish<false>(sp, par, d, -1);
+        finish<false>(sp, par, d);
     }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
