@@ -302,17 +302,17 @@ __global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
 template <int DQK, int DV>
 struct DkvCfg {
     static constexpr int BN = 128;                          // keys per workgroup
-    static constexpr int BM = 32;                           // query rows per step
+    static constexpr int BM = 64;                           // query rows per step (one LDS stage)
+    static constexpr int NH = 2;                            // 32-row halves a wave computes per step
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int NR = NW / 2;                       // waves per role (32 keys each)
     static constexpr int Q_BYTES = BM * DQK * 2;
     static constexpr int O_BYTES = BM * DV * 2;
-    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[64], delta[64] (BM used)
-    static constexpr int STAGE_BYTES = STAT_OFF + 2 * 64 * 4;
-    static constexpr int NU = 2;                            // P fragments (cc) per P wave and step
-    static constexpr int XBUF_BYTES = NR * NU * 1024;       // P of all P waves for one step
-    static constexpr int NS = 4;                            // LDS ring stages (loads run two steps ahead)
+    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[64], delta[64]
+    static constexpr int STAGE_BYTES = STAT_OFF + 2 * BM * 4;
+    static constexpr int XBUF_BYTES = NR * NH * 2 * 1024;   // P of all P waves for one step, (wave, half, cc)
+    static constexpr int NS = 3;                            // LDS ring stages (loads run one step ahead)
     static constexpr int X_OFF = NS * STAGE_BYTES;
     static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
     static constexpr int NQI = Q_BYTES / 1024;              // 1 KiB loads per Q tile
@@ -324,9 +324,10 @@ struct DkvCfg {
     static constexpr int NCV = DV / 16;
     static constexpr int NDK = DQK / 32;
     static constexpr int NDV = DV / 32;
+    static_assert(BM == 64, "one statistics load (64 lanes) covers a step");
     static_assert(Q_BYTES % 1024 == 0 && O_BYTES % 1024 == 0, "tiles split into whole wave loads");
     static_assert(STAGE_BYTES % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(NDMA_P <= NCQ && NDMA_S <= NCV, "loads must fit between the first MFMAs");
+    static_assert(NDMA_P <= NH * NCQ && NDMA_S <= NH * NCV, "loads must fit between the MFMAs");
 };
 
 // Step sequence of one workgroup: every BM-row part of every kept query
@@ -452,7 +453,7 @@ struct DkvShared {
           b(b_), hk(hk_), n_base(n_base_) {
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) toff[k] = load_off(load_index(w, k), C::BM);
-        soff = uint32_t(4 * (lane < C::BM ? swap23(lane) : 0));   // lanes past BM re-read the first row
+        soff = uint32_t(4 * swap23(lane));         // LDS position L holds row swap23(L) of the step
     }
     // byte offset of this lane's 16 bytes in 1 KiB load j (Q or dO part) of a
     // swizzled tile (tile row t at LDS row swap23(t)); rows past `lim` read row lim
@@ -471,8 +472,9 @@ struct DkvShared {
     __device__ const float* stats(int s) const {
         return reinterpret_cast<const float*>(lds + s * (C::STAGE_BYTES / 2) + C::STAT_OFF / 2);
     }
-    __device__ char* xbuf(int par, int wr, int u) const {
-        return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + (wr * C::NU + u) * 1024 + lane * 16;
+    __device__ char* xbuf(int par, int wr, int hh, int cc) const {
+        return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + ((wr * C::NH + hh) * 2 + cc) * 1024 +
+               lane * 16;
     }
 
     // Plan the loads of the steps' current step into stage s.
@@ -500,9 +502,8 @@ struct DkvShared {
     // Point a plan at another stage (re-loads its rows there).
     __device__ void restage(Dma& d, int s) const { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); }
 
-    // Load k of this wave (k < KMAX: tile part; k == KMAX: the statistics row,
-    // dS waves only -- lse2 by even waves, delta by odd ones, 64 lanes, rows
-    // past BM landing in unused slots).  LDS position L holds row swap23(L).
+    // Load k of this wave (k < KMAX: tile part; k == KMAX: the step's 64
+    // statistics values, dS waves only -- lse2 by even waves, delta by odd ones).
     __device__ void fire(const Dma& d, int k) const {
         if (k < C::KMAX) {
             const int j = load_index(w, k);
@@ -519,14 +520,14 @@ template <int DQK, int DV>
 struct DkvPWave {
     using C = DkvCfg<DQK, DV>;
     using Dma = typename DkvShared<DQK, DV>::Dma;
-    static constexpr int NF = 2 * C::NDV;           // dO^T fragments (cc, j) of one step
+    static constexpr int NF = 2 * C::NDV;           // dO^T fragments (cc, j) of one half
     const DkvShared<DQK, DV>& sh;
     const BwdArgs& a;
     int wr;
     bf16x8_t kB[C::NCQ];                            // K rows of the wave's 32 keys
     f32x16_t dv[C::NDV];
     int qmin;                                       // first query row that sees the lane's key
-    u32x4_t npp[2];                                 // P of the step just computed (cc), for its dV update
+    u32x4_t npp[C::NH][2];                          // P of the step just computed (half, cc), for its dV update
 
     __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -539,85 +540,94 @@ struct DkvPWave {
         for (int j = 0; j < C::NDV; ++j) dv[j] = f32x16_t{};
     }
 
-    __device__ bf16x8_t dot_frag(const uint16_t* sdO, int f) const {   // f = (cc, j)
-        return b_operand_tr_swz<DV>(sdO, 0, f / C::NDV, 32 * (f % C::NDV), sh.lane);
+    __device__ bf16x8_t dot_frag(const uint16_t* sdO, int hh, int f) const {   // f = (cc, j)
+        return b_operand_tr_swz<DV>(sdO, 32 * hh, f / C::NDV, 32 * (f % C::NDV), sh.lane);
     }
 
-    // One step: S of stage s and P of it (to LDS parity par, read by the
-    // partner); with PREV, the dV MFMAs of the previous step (stage sp, its P
-    // kept in npp) are issued between the P arithmetic.  Masked steps fix the
-    // packed P up afterwards.
+    // One step, two 32-row halves: S of stage s and P of it (to LDS parity
+    // par, read by the partner); with PREV, the dV MFMAs of the same half of
+    // the previous step (stage sp, its P kept in npp) are issued between the
+    // P arithmetic.  Masked steps fix the packed P up afterwards.
     template <bool PREV>
     __device__ void body(int s, int sp, int par, int m, bool mask, const Dma& d) {
         const uint16_t* sQ = sh.q_tile(s);
         const uint16_t* sdO = sh.do_tile(sp);
-        constexpr int PFD = 2;                      // dO^T fragments read this many ahead
-        bf16x8_t fr[PFD + 1];
-        if (PREV) {
-#pragma unroll
-            for (int f = 0; f < PFD; ++f) fr[f] = dot_frag(sdO, f);
-        }
-        f32x16_t st = f32x16_t{};
-        {
-            constexpr int PF = 4;
-            bf16x8_t qa[PF];
-#pragma unroll
-            for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = row_operand_swz<DQK>(sQ, sh.l32, 16 * c + 8 * sh.h2);
-            // S MFMAs; this wave's loads for two steps ahead go out between them
-#pragma unroll
-            for (int c = 0; c < C::NCQ; ++c) {
-                st = mfma32(qa[c % PF], kB[c], st);
-                if (c + PF < C::NCQ) qa[c % PF] = row_operand_swz<DQK>(sQ, sh.l32, 16 * (c + PF) + 8 * sh.h2);
-                if (c < C::NDMA_P) sh.fire(d, c);
-            }
-        }
         const float* sL = sh.stats(s);
-        float4 l4[4];
+        u32x4_t pn[C::NH][2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * sh.h2);
-
-        // dV MFMAs f = (cc, j) of the previous step; P pairs q = (cc, jj) of
-        // this step between them
-        constexpr int NQ = 8;
-        u32x4_t pn[2];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
+        for (int hh = 0; hh < C::NH; ++hh) {
+            constexpr int PFD = 2;                  // dO^T fragments read this many ahead
+            bf16x8_t fr[PFD + 1];
             if (PREV) {
-                if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(sdO, f + PFD);
-                dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), fr[f % (PFD + 1)], dv[f % C::NDV]);
+#pragma unroll
+                for (int f = 0; f < PFD; ++f) fr[f] = dot_frag(sdO, hh, f);
             }
+            f32x16_t st = f32x16_t{};
+            {
+                constexpr int PF = 4;
+                bf16x8_t qa[PF];
 #pragma unroll
-            for (int q = f * NQ / NF; q < (f + 1) * NQ / NF; ++q) {
-                const int cc = q >> 2, jj = q & 3;
-                float p2[2];
+                for (int c = 0; c < PF && c < C::NCQ; ++c)
+                    qa[c] = row_operand_swz<DQK>(sQ, 32 * hh + sh.l32, 16 * c + 8 * sh.h2);
+                // S MFMAs; this wave's loads for the next step go out between them
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int i = 8 * cc + 2 * jj + e;
-                    const float4 lv = l4[i >> 2];
-                    const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
-                    p2[e] = fast_exp2(fmaf(st[i], a.scale_log2, -l));
+                for (int c = 0; c < C::NCQ; ++c) {
+                    st = mfma32(qa[c % PF], kB[c], st);
+                    if (c + PF < C::NCQ) qa[c % PF] = row_operand_swz<DQK>(sQ, 32 * hh + sh.l32, 16 * (c + PF) + 8 * sh.h2);
+                    if (hh * C::NCQ + c < C::NDMA_P) sh.fire(d, hh * C::NCQ + c);
                 }
-                pn[cc][jj] = pack_bf16x2(p2[0], p2[1]);
-                if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, cc)) = pn[cc];
+            }
+            float4 l4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 32 * hh + 8 * g + 4 * sh.h2);
+
+            // dV MFMAs f = (cc, j) of the previous step's half; P pairs q = (cc, jj) between them
+            constexpr int NQ = 8;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                if (PREV) {
+                    if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(sdO, hh, f + PFD);
+                    dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), fr[f % (PFD + 1)], dv[f % C::NDV]);
+                }
+#pragma unroll
+                for (int q = f * NQ / NF; q < (f + 1) * NQ / NF; ++q) {
+                    const int cc = q >> 2, jj = q & 3;
+                    float p2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int i = 8 * cc + 2 * jj + e;
+                        const float4 lv = l4[i >> 2];
+                        const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
+                        p2[e] = fast_exp2(fmaf(st[i], a.scale_log2, -l));
+                    }
+                    pn[hh][cc][jj] = pack_bf16x2(p2[0], p2[1]);
+                    if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, hh, cc)) = pn[hh][cc];
+                }
             }
         }
         if (mask) {
             // pairs whose row is below the lane key's first visible row (causal)
             // or whose key is past Sk: clear the bf16 halves and rewrite
-            const int tau = qmin - m - 8 * sh.h2;   // first visible row offset of this lane
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
+            for (int hh = 0; hh < C::NH; ++hh) {
+                const int tau = qmin - m - 32 * hh - 8 * sh.h2;   // first visible row offset of this lane
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int o = 16 * cc + 2 * jj;
-                    const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
-                    pn[cc][jj] &= keep;
+                for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int o = 16 * cc + 2 * jj;
+                        const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
+                        pn[hh][cc][jj] &= keep;
+                    }
+                    *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, hh, cc)) = pn[hh][cc];
                 }
-                *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, cc)) = pn[cc];
             }
         }
-        npp[0] = pn[0];
-        npp[1] = pn[1];
+#pragma unroll
+        for (int hh = 0; hh < C::NH; ++hh) {
+            npp[hh][0] = pn[hh][0];
+            npp[hh][1] = pn[hh][1];
+        }
     }
 
     __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, s, par, m, mask, d); }
@@ -626,14 +636,15 @@ struct DkvPWave {
 #pragma unroll
         for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
     }
-    // this wave's loads of the oldest outstanding step have landed (one newer step in flight)
-    __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_P>(); }
     // dV update of the last step (stage sp)
     __device__ void drain(int sp, int par) {
         (void)par;
         const uint16_t* sdO = sh.do_tile(sp);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) dv[f % C::NDV] = mfma32(as_bf16x8(npp[f / C::NDV]), dot_frag(sdO, f), dv[f % C::NDV]);
+        for (int hh = 0; hh < C::NH; ++hh)
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+                dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), dot_frag(sdO, hh, f), dv[f % C::NDV]);
     }
     __device__ void store() const {
         uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
@@ -683,43 +694,46 @@ struct DkvSWave {
         return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the query slice in stage s whose P is in LDS parity par: dP, dS,
-    // dK.  With FIRE this wave's loads for two steps ahead go out between the
-    // dP MFMAs.
+    // Finish the query slice in stage s whose P is in LDS parity par: per
+    // 32-row half dP, dS, dK.  With FIRE this wave's loads for the next step go
+    // out between the dP MFMAs.
     template <bool FIRE>
     __device__ void finish(int s, int par, const Dma& d) {
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));
         const uint16_t* sQ = sh.q_tile(s);
         const uint16_t* sdO = sh.do_tile(s);
-        constexpr int PFO = 4;                      // dO rows read this many ahead
-        bf16x8_t oa[PFO];
+        const float* sD = sh.stats(s) + C::BM;      // delta slot follows the lse2 slot
 #pragma unroll
-        for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, sh.l32, 16 * c + 8 * sh.h2);
-        const float* sD = sh.stats(s) + 64;         // delta slot follows the 64-float lse2 slot
-        float4 d4[4];
+        for (int hh = 0; hh < C::NH; ++hh) {
+            constexpr int PFO = 4;                  // dO rows read this many ahead
+            bf16x8_t oa[PFO];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 8 * g + 4 * sh.h2);
-        u32x4_t pw[2];
+            for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, 32 * hh + sh.l32, 16 * c + 8 * sh.h2);
+            float4 d4[4];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) pw[cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, cc));
-        constexpr int NQF = 2 * C::NDK;            // Q^T fragments (cc, j)
-        bf16x8_t qf[NQF];
-        f32x16_t dp = f32x16_t{};
+            for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 32 * hh + 8 * g + 4 * sh.h2);
+            u32x4_t pw[2];
 #pragma unroll
-        for (int c = 0; c < C::NCV; ++c) {
-            dp = mfma32(oa[c % PFO], vB[c], dp);
-            if (c + PFO < C::NCV) oa[c % PFO] = row_operand_swz<DV>(sdO, sh.l32, 16 * (c + PFO) + 8 * sh.h2);
-            if (FIRE && c < C::NDMA_S) sh.fire(d, c);
+            for (int cc = 0; cc < 2; ++cc) pw[cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, hh, cc));
+            constexpr int NQF = 2 * C::NDK;        // Q^T fragments (cc, j)
+            bf16x8_t qf[NQF];
+            f32x16_t dp = f32x16_t{};
 #pragma unroll
-            for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f)
-                qf[f] = b_operand_tr_swz<DQK>(sQ, 0, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+            for (int c = 0; c < C::NCV; ++c) {
+                dp = mfma32(oa[c % PFO], vB[c], dp);
+                if (c + PFO < C::NCV) oa[c % PFO] = row_operand_swz<DV>(sdO, 32 * hh + sh.l32, 16 * (c + PFO) + 8 * sh.h2);
+                if (FIRE && hh * C::NCV + c < C::NDMA_S) sh.fire(d, hh * C::NCV + c);
+#pragma unroll
+                for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f)
+                    qf[f] = b_operand_tr_swz<DQK>(sQ, 32 * hh, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+            }
+            u32x4_t sa[2];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, d4, pw[q >> 2][q & 3], q >> 2, q & 3);
+#pragma unroll
+            for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
         }
-        u32x4_t sa[2];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, d4, pw[q >> 2][q & 3], q >> 2, q & 3);
-#pragma unroll
-        for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));   // accumulators stay in AGPRs
     }
@@ -745,7 +759,6 @@ struct DkvSWave {
 #pragma unroll
         for (int k = 0; k < C::NDMA_S; ++k) sh.fire(d, k);
     }
-    __device__ void wait_oldest() const { wait_vmcnt<C::NDMA_S>(); }
 
     __device__ void store() const {
         uint16_t* g = a.dk + sh.b * a.dk_sb + sh.hk * a.dk_sh;
@@ -762,12 +775,12 @@ struct DkvSWave {
 
 // Steps, barriers and loads, shared by both roles.  Step t uses ring stage
 // t % NS and may read stage t - 1; its P goes to LDS parity t % 2.  The loads
-// of step t + 2 go out from inside step t's MFMA stream (their stage was last
-// read in step t - 1, before the barrier that opens step t), so each tile has
-// two steps to land; past the last step they re-read the last planned step's
-// rows into the free stage, which keeps the step bodies free of branches.  The
-// loop body is one straight-line block per role (masking is a fix-up on the
-// packed P, outside the MFMA block) so the accumulators stay put in registers.
+// of step t + 1 go out from inside step t's MFMA stream (their stage was last
+// read in step t - 1, before the barrier that opens step t); past the last
+// step they re-read the last planned step's rows into the free stage, which
+// keeps the step bodies free of branches.  The loop body is one
+// straight-line block per role (masking is a fix-up on the packed P, outside
+// the MFMA block) so the accumulators stay put in registers.
 template <int DQK, int DV, class Role>
 __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
                                          Role& role) {
@@ -784,31 +797,24 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     role.fire_all(d);
     bool have1 = steps.next();                      // step t + 1
     int m1 = steps.m;
+    wait_vmcnt<0>();
+    __syncthreads();
     if (have1) sh.plan(d, steps, 1);
     else sh.restage(d, 1);
-    role.fire_all(d);
-    bool have2 = have1 && steps.next();             // step t + 2
-    int m2 = steps.m;
-    role.wait_oldest();
-    __syncthreads();
-    if (have2) sh.plan(d, steps, 2);
-    else sh.restage(d, 2);
     role.first(0, 0, m, need_mask(m), d);
     int t = 0;
     while (have1) {
         ++t;
         m = m1;
-        const bool have3 = have2 && steps.next();
-        const int m3 = steps.m;
-        role.wait_oldest();
+        const bool have2 = steps.next();
+        const int m2 = steps.m;
+        wait_vmcnt<0>();                            // this wave's loads of step t landed
         __syncthreads();
-        if (have3) sh.plan(d, steps, (t + 2) % C::NS);
-        else sh.restage(d, (t + 2) % C::NS);
+        if (have2) sh.plan(d, steps, (t + 1) % C::NS);
+        else sh.restage(d, (t + 1) % C::NS);
         role.step(t % C::NS, (t + C::NS - 1) % C::NS, t & 1, m, need_mask(m), d);
         have1 = have2;
         m1 = m2;
-        have2 = have3;
-        m2 = m3;
     }
     wait_vmcnt<0>();                                // no load may land in LDS after the workgroup ends
     __syncthreads();
