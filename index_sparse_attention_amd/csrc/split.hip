@@ -85,7 +85,8 @@ struct DqCfg {
 };
 
 template <int DQK, int DV, int WR>
-__global__ __launch_bounds__(64 * (128 / WR), 1) void k_bwd_dq(BwdArgs a) {
+// two workgroups per CU (two waves per SIMD) where the registers allow
+__global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(BwdArgs a) {
     using C = DqCfg<DQK, DV, WR>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
@@ -887,8 +888,8 @@ hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s) {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_dq_t<64, 64, 64>(a, s);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_dq_t<128, 128, 64>(a, s);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_dq_t<64, 64, 32>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_dq_t<128, 128, 32>(a, s);
     if (a.Dqk == 192 && a.Dv == 128) return launch_dq_t<192, 128, 32>(a, s);
     return hipErrorInvalidValue;
 }
