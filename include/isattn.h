@@ -90,8 +90,9 @@ enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
 
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
  * (fp32 delta [B,Hq,Sq] plus head-major fp32 accumulators: dK,dV [B,Hk,Sk,D]
- * for LOOPK, dQ [B,Hq,Sq,Dqk] for LOOPQ, none for SPLIT; each part 256-byte
- * aligned).  Returns 0 for a NULL shape or unknown algo. */
+ * for LOOPK, dQ [B,Hq,Sq,Dqk] for LOOPQ; for SPLIT fp32 delta and
+ * lse * log2(e), each [B,Hq,ceil(Sq/128)*128]; each part 256-byte aligned).
+ * Returns 0 for a NULL shape or unknown algo. */
 size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
 
 /* Attention backward ([P1] Summary and Core changes 1-3): recompute
@@ -110,7 +111,10 @@ size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo
  * workspace: device buffer of at least isattn_attn_bwd_workspace_bytes bytes,
  *   256-byte aligned; its contents on entry do not matter.
  * stream: hipStream_t (NULL = default stream).
- * Supported: (dim_qk, dim_v) in {(64,64), (128,128), (192,128)}. */
+ * Supported: (dim_qk, dim_v) in {(64,64), (128,128), (192,128)}.  SPLIT
+ *   addresses rows within one head with 32-bit byte offsets: it returns
+ *   ISATTN_ERR_STRIDE_ALIGN unless ceil(S/128)*128 * stride_s * 2 < 2^31 for
+ *   q and dO (S = Sq) and for k and v (S = Sk). */
 isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape,
                                 const isattn_tensor_t* q, const isattn_tensor_t* k,
                                 const isattn_tensor_t* v, const isattn_tensor_t* o,

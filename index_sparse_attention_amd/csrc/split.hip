@@ -10,17 +10,20 @@
 // workspace.
 //
 // dQ pass (k_bwd_dq): workgroup = one 128-row query tile; each wave owns WR
-// query rows.  Per 64-key step: S^T = K Q^T and dP^T = V dO^T (A = K/V from
-// LDS, B = Q/dO held in registers), P and dS in registers, dQ += dS K with dS
-// taken straight from the accumulators and K read back with transposing LDS
-// loads.  K/V rows are staged at LDS row swap23(r), which makes each lane's
-// accumulator registers cover 8 consecutive keys.
+// query rows with their Q / dO rows resident in registers.  Per 32-key step:
+// S^T = K Q^T and dP^T = V dO^T (A = K/V from LDS), P and dS in registers,
+// dQ += dS K with dS taken straight from the accumulators and K read back with
+// transposing LDS loads.  K/V rows are staged at LDS row swap23(r), which makes
+// each lane's accumulator registers cover 8 consecutive keys.
 //
-// dK/dV pass (k_bwd_dkdv): workgroup = one 128-key tile; wave w owns keys
-// 32w..32w+31 for every query head of the GQA group.  Per 64-row query step:
-// S = Q K^T and dP = dO V^T (A = Q/dO from LDS, B = K/V in registers), then
-// dV += P^T dO and dK += dS^T Q with P / dS straight from the accumulators and
-// dO / Q read back with transposing LDS loads.
+// dK/dV pass (k_bwd_dkdv): workgroup = one 128-key tile, eight waves in two
+// roles (P waves with K resident and dV accumulators, dS waves with V resident
+// and dK accumulators) exchanging P through LDS; the Q/dO tiles of each query
+// step are staged once and read by both roles.
+//
+// Both passes fill their LDS rings with direct global->LDS loads issued from
+// inside the MFMA stream, a step or two ahead, and take one workgroup barrier
+// per step.
 #include <climits>
 
 #include "device_common.hpp"
@@ -30,45 +33,20 @@ namespace isattn {
 namespace {
 
 
-template <int D, int PITCH, int ROWS, int NT, bool PERM>
-__device__ __forceinline__ void stage(uint16_t* dst, const uint16_t* src, int64_t row_stride, int row0,
-                                      int limit, int tid) {
-    TileStager<D, PITCH, ROWS, NT, PERM> t;
-    t.load(src, row_stride, row0, limit, tid);
-    t.store(dst, tid);
-}
-
-// B operand (k = 8 consecutive tile rows, n = 32 columns) of a 32x32x16 MFMA
-// from a swap23-staged row-major tile: logical rows 16*cc + 8*h + 0..7 of the
-// 32-row group starting at `row32`, columns col0 + (lane % 32).
-__device__ __forceinline__ bf16x8_t b_operand_tr(const uint16_t* tile, int pitch, int row32, int cc, int col0,
-                                                 int lane) {
-    const int L = lane & 15;
-    const int g = lane >> 4;
-    const int h = g >> 1;
-    const int row = row32 + 16 * cc + 4 * h + (L >> 2);
-    const int col = col0 + 16 * (g & 1) + 4 * (L & 3);
-    const u32x2_t lo = lds_read_tr16(tile + row * pitch + col);
-    const u32x2_t hi = lds_read_tr16(tile + (row + 8) * pitch + col);
-    const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
-    return as_bf16x8(v);
-}
-
-// Pipeline shared by both passes (three LDS stages, one barrier per step):
-//   phase 1  finish the previous step's output GEMM from its stage (the only
-//            transposing LDS reads; the compiler's wait for outstanding
-//            direct-to-LDS loads lands here, on the loads of this step)
-//   barrier  this step's stage is complete in every wave
-//   phase 2  issue the direct-to-LDS loads of the next step into the third stage
-//   phase 3  S / dP of this step (ds_read_b128 operands, double-buffered)
-//   phase 4  P and dS in registers, kept packed for the next step's phase 1
-
 // 16-byte global row chunk as an MFMA operand (resident operands are read once
 // per workgroup straight from HBM).
 __device__ __forceinline__ bf16x8_t gload_operand(const uint16_t* p) { return as_bf16x8(gload128(p)); }
 
 // ---------------------------------------------------------------------------
 // dQ pass
+//
+// One workgroup per (batch, query head, 128-row query block); each wave owns
+// WR rows: their Q and dO rows stay in registers (B operands), dQ in
+// accumulators.  A step is 32 keys of a kept key block: S = K Q^T and
+// dP = V dO^T from the K/V tile in LDS, then P, dS = P (dP - delta), and the
+// dQ += dS K MFMAs of that step run at the start of the next one.  K/V tiles
+// go through a 4-stage LDS ring filled by direct global->LDS loads issued two
+// steps ahead from inside the MFMA stream.
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, int WR>
 struct DqCfg {
@@ -77,11 +55,57 @@ struct DqCfg {
     static constexpr int NW = BM / WR;
     static constexpr int NT = 64 * NW;
     static constexpr int QT = WR / 32;             // 32-row query tiles per wave
-    static constexpr int STAGE = BN * (DQK + DV);  // elements per K/V stage
-    static constexpr int LDS_BYTES = 3 * STAGE * 2;
+    static constexpr int K_BYTES = BN * DQK * 2;
+    static constexpr int V_BYTES = BN * DV * 2;
+    static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+    static constexpr int NS = 4;                   // LDS ring stages (loads run two steps ahead)
+    static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+    static constexpr int NKI = K_BYTES / 1024;     // 1 KiB loads per K tile
+    static constexpr int NI = STAGE_BYTES / 1024;  // 1 KiB loads per step
+    static constexpr int KMAX = NI / NW;           // loads per wave per step
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDT = DQK / 32;
+    static_assert(NI % NW == 0 && K_BYTES % 1024 == 0, "tiles split into whole wave loads");
+    static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
+};
+
+// Step sequence of a dQ workgroup: every 32-key part of every kept key block
+// that holds a key some row of the query block sees (key <= last, the last key
+// visible to the block's last row).  The kept key blocks are read 64 at a time
+// into a register (one per lane).
+struct DqSteps {
+    int it = -1, sub = 0, count = 0, n0 = 0, n_kb = 0, last = 0, lane = 0;
+    const int32_t* list = nullptr;
+    int chunk = 0, chunk_base = -1;
+
+    __device__ int kb_at() {
+        if (list == nullptr) return it;
+        const int base = it & ~63;
+        if (base != chunk_base) {
+            chunk_base = base;
+            chunk = base + lane < count ? list[base + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(chunk, it & 63);
+    }
+    __device__ bool next_block() {
+        for (;;) {
+            if (++it >= count) return false;
+            const int kb = kb_at();
+            if (kb < 0 || kb >= n_kb) continue;     // malformed entry: nothing to do
+            if (kb * kBlock > last) continue;
+            sub = 0;
+            n0 = kb * kBlock;
+            return true;
+        }
+    }
+    __device__ bool next() {
+        if (++sub < kBlock / 32 && n0 + 32 <= last) {
+            n0 += 32;
+            return true;
+        }
+        return next_block();
+    }
 };
 
 template <int DQK, int DV, int WR>
@@ -91,7 +115,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h2 = lane >> 5;
 
     // items (b, h, query block), head-major; within a head the longest rows
@@ -106,35 +130,22 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     const int m_base = qb * C::BM;
     const int last_row = min(m_base + C::BM - 1, a.Sq - 1);
     const int shift = a.Sk - a.Sq;
-    const int diag = last_row + shift;
 
-    int kb_count;
-    const int32_t* kb_list = nullptr;
+    DqSteps steps;
+    steps.lane = lane;
+    steps.n_kb = a.n_kb;
+    const int diag = last_row + shift;
+    steps.last = a.causal ? min(diag, a.Sk - 1) : a.Sk - 1;
     if (a.mask_kind == 1) {
         const int hm = h * a.Hm / a.Hq;
         const int r = (b * a.Hm + hm) * a.n_qb + qb;
         const int beg = a.q2k_ptr[r];
-        kb_count = a.q2k_ptr[r + 1] - beg;
-        kb_list = a.q2k_col + beg;
+        steps.count = a.q2k_ptr[r + 1] - beg;
+        steps.list = a.q2k_col + beg;
     } else {
-        kb_count = a.n_kb;
-        if (a.causal) kb_count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
+        steps.count = a.n_kb;
+        if (a.causal) steps.count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
     }
-    constexpr int SUB = kBlock / C::BN;            // steps per key block
-    const int T = kb_count * SUB;
-    auto step_n0 = [&](int t) -> int {             // key offset of step t, -1 if nothing visible
-        const int kb = kb_list ? kb_list[t / SUB] : t / SUB;
-        const int n0 = kb * kBlock + (t % SUB) * C::BN;
-        const bool ok = kb >= 0 && kb < a.n_kb && n0 < a.Sk && (!a.causal || n0 <= diag);
-        return ok ? n0 : -1;
-    };
-    auto next_step = [&](int t, int* n0) -> int {
-        for (++t; t < T; ++t) {
-            *n0 = step_n0(t);
-            if (*n0 >= 0) break;
-        }
-        return t;
-    };
 
     // ---- resident operands: this wave's Q / dO rows (B operands), LSE, delta
     const int wrow = w * WR;
@@ -162,16 +173,53 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t) dq[qt][t] = f32x16_t{};
 
+    // ---- K/V tile loads: per-lane byte offsets of this wave's 1 KiB loads
+    // (load k is instruction j = w + NW * k of the step: K tile parts, then V)
     const uint16_t* gk = a.k + b * a.k_sb + hk * a.k_sh;
     const uint16_t* gv = a.v + b * a.v_sb + hk * a.v_sh;
-    auto issue = [&](int n0, int stage_i) {
-        uint16_t* base = lds + stage_i * C::STAGE;
-        load_tile_async<DQK, C::BN, C::NW>(base, gk, a.k_ss, n0, a.Sk, w, lane);
-        load_tile_async<DV, C::BN, C::NW>(base + C::BN * DQK, gv, a.v_ss, n0, a.Sk, w, lane);
+    const uint32_t lds_base = lds_address(lds);
+    auto tile_off = [&](int j, int lim) -> uint32_t {      // tile rows past lim read row lim
+        const bool is_k = j < C::NKI;
+        const int jj = is_k ? j : j - C::NKI;
+        const int D = is_k ? DQK : DV;
+        const int e = 512 * jj + 8 * lane;
+        const int r = e / D;
+        const int c = ((e - r * D) >> 3) ^ chunk_swz(r);
+        return uint32_t(min(swap23(r), lim)) * uint32_t((is_k ? a.k_ss : a.v_ss) * 2) + uint32_t(16 * c);
     };
+    uint32_t toff[C::KMAX];
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) toff[k] = tile_off(w + C::NW * k, C::BN);
+    struct Dma {
+        uint32_t sb;
+        uint32_t off[C::KMAX];
+    } d;
+    auto plan = [&](int n0, int s) {
+        d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        if (n0 + C::BN <= a.Sk) {
+            const uint32_t mk = uint32_t(n0) * uint32_t(a.k_ss * 2), mv = uint32_t(n0) * uint32_t(a.v_ss * 2);
+#pragma unroll
+            for (int k = 0; k < C::KMAX; ++k) d.off[k] = toff[k] + (w + C::NW * k < C::NKI ? mk : mv);
+        } else {                                   // ragged tail: keys past Sk re-read key Sk - 1
+            const int nb = min(n0, a.Sk - 1);
+            const uint32_t mk = uint32_t(nb) * uint32_t(a.k_ss * 2), mv = uint32_t(nb) * uint32_t(a.v_ss * 2);
+#pragma unroll
+            for (int k = 0; k < C::KMAX; ++k)
+                d.off[k] = tile_off(w + C::NW * k, a.Sk - 1 - nb) + (w + C::NW * k < C::NKI ? mk : mv);
+        }
+    };
+    auto restage = [&](int s) { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); };
+    auto fire = [&](int k) {
+        const int j = w + C::NW * k;
+        const bool is_k = j < C::NKI;
+        dma16(is_k ? static_cast<const void*>(gk) : static_cast<const void*>(gv), d.off[k],
+              d.sb + uint32_t(is_k ? 1024 * j : C::K_BYTES + 1024 * (j - C::NKI)));
+    };
+
     bf16x8_t dsa[C::QT][2];                        // packed dS of the previous step
-    auto dq_update = [&](int stage_i) {
-        const uint16_t* sK = lds + stage_i * C::STAGE;
+    // dQ += dS K for the step in stage sp
+    auto dq_update = [&](int sp) {
+        const uint16_t* sK = lds + sp * (C::STAGE_BYTES / 2);
         constexpr int NF = 2 * C::NDT;             // B fragments, f = cc * NDT + dt
         constexpr int PF = NF < 3 ? NF : 3;        // prefetch depth
         bf16x8_t fr[PF + 1];
@@ -186,23 +234,11 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
             for (int qt = 0; qt < C::QT; ++qt) dq[qt][dt] = mfma32(dsa[qt][cc], fr[f % (PF + 1)], dq[qt][dt]);
         }
     };
-
-    int n0 = -1;
-    int t = next_step(-1, &n0);
-    if (t < T) issue(n0, 0);
-    int sidx = 0;
-    bool has_prev = false;
-    while (t < T) {
-        int n0n = -1;
-        const int tn = next_step(t, &n0n);
-        const int cur = sidx % 3;
-        if (has_prev) dq_update((sidx + 2) % 3);
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (tn < T) issue(n0n, (sidx + 1) % 3);
-
-        const uint16_t* sK = lds + cur * C::STAGE;
-        const uint16_t* sV = sK + C::BN * DQK;
+    // S, dP of the step in stage s (loads for two steps ahead issued between
+    // the MFMAs), then P and dS into dsa
+    auto scores = [&](int s, int n0) {
+        const uint16_t* sK = lds + s * (C::STAGE_BYTES / 2);
+        const uint16_t* sV = sK + C::K_BYTES / 2;
         f32x16_t st[C::QT], dpt[C::QT];
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt) {
@@ -227,9 +263,9 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
 #pragma unroll
                     for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c % (PF + 1)], doB[qt][c], dpt[qt]);
                 }
+                if (c < C::KMAX) fire(c);
             }
         }
-
         // P, dS; accumulator register i holds key n0 + 16*(i/8) + 8*h2 + i%8
         const bool need_mask = (n0 + C::BN > a.Sk) || (a.causal && n0 + C::BN - 1 > m_base + shift);
         if (need_mask) {
@@ -264,12 +300,46 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
                     pk[j] = pack_bf16x2(dpt[qt][8 * cc + 2 * j], dpt[qt][8 * cc + 2 * j + 1]);
                 dsa[qt][cc] = as_bf16x8(pk);
             }
-        has_prev = true;
-        ++sidx;
-        t = tn;
-        n0 = n0n;
+    };
+
+    if (steps.next_block()) {
+        int n0 = steps.n0;                         // step t
+        plan(n0, 0);
+#pragma unroll
+        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        bool have1 = steps.next();                 // step t + 1
+        int n1 = steps.n0;
+        if (have1) plan(n1, 1);
+        else restage(1);
+#pragma unroll
+        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        bool have2 = have1 && steps.next();        // step t + 2
+        int n2 = steps.n0;
+        wait_vmcnt<C::KMAX>();                     // this wave's loads of step t landed
+        __syncthreads();
+        if (have2) plan(n2, 2);
+        else restage(2);
+        scores(0, n0);
+        int t = 0;
+        while (have1) {
+            ++t;
+            n0 = n1;
+            const bool have3 = have2 && steps.next();
+            const int n3 = steps.n0;
+            wait_vmcnt<C::KMAX>();
+            __syncthreads();
+            if (have3) plan(n3, (t + 2) % C::NS);
+            else restage((t + 2) % C::NS);
+            dq_update((t + C::NS - 1) % C::NS);
+            scores(t % C::NS, n0);
+            have1 = have2;
+            n1 = n2;
+            have2 = have3;
+            n2 = n3;
+        }
+        wait_vmcnt<0>();                           // no load may land in LDS after the workgroup ends
+        dq_update(t % C::NS);
     }
-    if (has_prev) dq_update((sidx + 2) % 3);
 
     uint16_t* gdq = a.dq + b * a.dq_sb + h * a.dq_sh;
 #pragma unroll

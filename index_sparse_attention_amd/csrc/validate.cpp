@@ -115,8 +115,12 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     if ((st = check_view(dv, nk)) != ISATTN_OK) return st;
     if (nq > 0 && lse == nullptr) return ISATTN_ERR_NULL;
     if (algo == ISATTN_ALGO_SPLIT && nq > 0) {
-        const int64_t rows = int64_t(cdiv(s.seqlen_q, kBlock)) * kBlock;
-        if (rows * q->stride_s * 2 >= (int64_t(1) << 31) || rows * dO->stride_s * 2 >= (int64_t(1) << 31))
+        // 32-bit byte offsets within one head: Q/dO rows (dK/dV pass), K/V rows (dQ pass)
+        const int64_t lim = int64_t(1) << 31;
+        const int64_t rq = int64_t(cdiv(s.seqlen_q, kBlock)) * kBlock;
+        const int64_t rk = int64_t(cdiv(s.seqlen_k, kBlock)) * kBlock;
+        if (rq * q->stride_s * 2 >= lim || rq * dO->stride_s * 2 >= lim || rk * k->stride_s * 2 >= lim ||
+            rk * v->stride_s * 2 >= lim)
             return ISATTN_ERR_STRIDE_ALIGN;
     }
 

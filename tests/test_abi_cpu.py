@@ -122,11 +122,15 @@ def test_bwd_validation_errors(lib):
     c = Call(lib, Hq=4, Hk=2); c.mask = _abi.Mask(1, 128, 128, 3, FAKE, FAKE, FAKE, FAKE); assert c() == MASK
     c = Call(lib); c.mask = _abi.Mask(1, 128, 128, 2, None, None, FAKE, FAKE); assert c() == NULL
     c = Call(lib, algo=1); c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, None, None); assert c() == NULL
-    # SPLIT addresses a head's Q/dO rows with 32-bit byte offsets: (rows rounded up to 128) x stride x 2
+    # SPLIT addresses a head's Q/dO/K/V rows with 32-bit byte offsets: (rows rounded up to 128) x stride x 2
     # must stay below 2^31 (here 256 rows x 2^22 x 2 = 2^31)
     c = Call(lib, algo=2); c.views["q"].stride_s = 1 << 22; c.views["q"].stride_b = 256 << 22
     assert c() == STRIDE
     c = Call(lib, algo=2); c.views["do"].stride_s = 1 << 22; c.views["do"].stride_b = 256 << 22
+    assert c() == STRIDE
+    c = Call(lib, algo=2); c.views["k"].stride_s = 1 << 22; c.views["k"].stride_b = 256 << 22
+    assert c() == STRIDE
+    c = Call(lib, algo=2); c.views["v"].stride_s = 1 << 22; c.views["v"].stride_b = 256 << 22
     assert c() == STRIDE
     c = Call(lib, algo=2); c.ws_bytes -= 1; assert c() == WS
 
