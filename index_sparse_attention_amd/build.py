@@ -36,6 +36,11 @@ HIP_FLAGS = [
     "-I", INCLUDE,
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE]
+# Per-source additions.  split.hip: MFMA results go to VGPRs, so a kernel that
+# needs no AGPRs gets the whole 256-register budget of two waves per SIMD as
+# VGPRs (the default halves it between VGPRs and AGPRs) and its VALU reads the
+# accumulators without v_accvgpr copies.
+SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):
@@ -58,7 +63,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CPP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))

@@ -771,7 +771,7 @@ struct DkvSWave {
     template <bool FIRE>
     __device__ void finish(int s, int par, const Dma& d) {
 #pragma unroll
-        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));
         const uint16_t* sQ = sh.q_tile(s);
         const uint16_t* sdO = sh.do_tile(s);
         const float* sD = sh.stats(s) + C::BM;      // delta slot follows the lse2 slot
@@ -806,7 +806,7 @@ struct DkvSWave {
             for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
         }
 #pragma unroll
-        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+a"(dk[j]));   // accumulators stay in AGPRs
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));   // the accumulators are not moved
     }
 
     __device__ void first(int s, int par, int m, bool mask, const Dma& d) {
