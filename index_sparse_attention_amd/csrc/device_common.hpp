@@ -146,15 +146,23 @@ namespace isattn {
 
 // ---- swizzled LDS tiles filled by direct global->LDS loads -----------------
 // A tile of ROWS x D bf16 is stored unpadded (row r at element r * D); its
-// 16-byte chunk c sits at chunk position c ^ chunk_swz(r).  With this XOR the
-// 8 rows read by one 128-byte ds_read_b128 phase hit 8 different bank groups,
-// and so do the 4 rows x 2 chunks of a 16-lane ds_read_b64_tr_b16 phase that
-// starts at a row multiple of 4.
-__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// 16-byte chunk c sits at chunk position c ^ chunk_swz(r, D).  gfx950 LDS has
+// 64 banks of 4 bytes: a ds_read_b128 is served 16 lanes per pass and a
+// ds_read_b64(_tr_b16) 32 lanes per pass, each pass conflict-free when its
+// lanes cover distinct banks.  The XOR makes both patterns used here
+// conflict-free: 16 consecutive rows reading one chunk each (b128 operand
+// reads), and 4 consecutive rows x 4 consecutive chunks starting at a row
+// multiple of 4 (transposing reads).  With 16 or more chunks per row the rows
+// start on the same bank and the XOR spans 4 bits; with 8 or 24 chunks per row
+// odd rows start half a bank line later and a 3-bit XOR (which keeps a chunk
+// inside its aligned group of 8) suffices.
+__device__ __forceinline__ int chunk_swz(int r, int D) {
+    return (D / 8) % 16 == 0 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 template <int D>
 __device__ __forceinline__ int swz_off(int r, int elem) {
-    return r * D + ((((elem >> 3) ^ chunk_swz(r)) << 3) | (elem & 7));
+    return r * D + ((((elem >> 3) ^ chunk_swz(r, D)) << 3) | (elem & 7));
 }
 
 // Async copy of tile rows [row0, row0 + ROWS) of a [seq, D] slice into a
@@ -174,7 +182,7 @@ __device__ __forceinline__ void load_tile_async(uint16_t* tile, const uint16_t* 
         const int e = 512 * j + 8 * lane;          // element offset this lane fills
         const int r = e / D;
         const int p = (e - r * D) >> 3;
-        const int c = p ^ chunk_swz(r);
+        const int c = p ^ chunk_swz(r, D);
         const int gr = min(row0 + swap23(r), limit - 1);
         __builtin_amdgcn_global_load_lds(src + gr * row_stride + 8 * c,
                                          (__attribute__((address_space(3))) void*)(tile + 512 * j), 16, 0, 0);

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         const int D = is_k ? DQK : DV;
         const int e = 512 * jj + 8 * lane;
         const int r = e / D;
-        const int c = ((e - r * D) >> 3) ^ chunk_swz(r);
+        const int c = ((e - r * D) >> 3) ^ chunk_swz(r, D);
         return uint32_t(min(swap23(r), lim)) * uint32_t((is_k ? a.k_ss : a.v_ss) * 2) + uint32_t(16 * c);
     };
     uint32_t toff[C::KMAX];
@@ -532,7 +532,7 @@ struct DkvShared {
     __device__ uint32_t tile_off(int jj, int lim, int64_t ss) const {
         const int e = 512 * jj + 8 * lane;
         const int r = e / D;
-        const int c = ((e - r * D) >> 3) ^ chunk_swz(r);
+        const int c = ((e - r * D) >> 3) ^ chunk_swz(r, D);
         return uint32_t(min(swap23(r), lim)) * uint32_t(ss * 2) + uint32_t(16 * c);
     }
     __device__ uint32_t load_off(int j, int lim) const {
