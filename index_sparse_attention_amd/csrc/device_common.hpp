@@ -189,6 +189,50 @@ __device__ __forceinline__ void load_tile_async(uint16_t* tile, const uint16_t* 
     }
 }
 
+// ---- operand reads at per-lane LDS addresses ------------------------------
+// A kernel that walks a ring of LDS stages keeps, per lane, the address of
+// each of its operand reads as an LDS pointer (stage base included) and
+// advances it once per step; the compile-time part of an address (row group,
+// k-chunk) lands in the instruction's offset field.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ const lds_char* lds_ptr(const void* p) {
+    return (const lds_char*)((__attribute__((address_space(3))) const void*)(p));
+}
+__device__ __forceinline__ u32x4_t lds_ld128(const lds_char* p) {
+    return *(const __attribute__((address_space(3))) u32x4_t*)(p);
+}
+__device__ __forceinline__ f32x4_t lds_ldf4(const lds_char* p) {
+    return *(const __attribute__((address_space(3))) f32x4_t*)(p);
+}
+__device__ __forceinline__ void lds_st128(const lds_char* p, u32x4_t v) {
+    *(__attribute__((address_space(3))) u32x4_t*)(const_cast<lds_char*>(p)) = v;
+}
+__device__ __forceinline__ u32x2_t lds_ld_tr16(const lds_char* p) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+// Per-lane byte offsets inside a swizzled, swap23-staged tile of D-element rows:
+//   row_read_off: the A-operand read of chunk pair c of LDS row lane%32
+//     (elements 16c + 8*(lane/32) .. +7), as row_operand_swz reads it;
+//   tr_read_off: the lo (hi = 0) or hi (hi = 1) transposing read of the
+//     B operand of column group dt, as b_operand_tr_swz reads it at row32 = 0,
+//     cc = 0.
+// The swizzle repeats every 16 rows, so rows 16k further on add 32 * k * D
+// bytes: a compile-time offset.
+template <int D>
+__device__ __forceinline__ uint32_t row_read_off(int lane, int c) {
+    return 2u * uint32_t(swz_off<D>(lane & 31, 16 * c + 8 * (lane >> 5)));
+}
+template <int D>
+__device__ __forceinline__ uint32_t tr_read_off(int lane, int dt, int hi) {
+    const int L = lane & 15;
+    const int g = lane >> 4;
+    const int row = 4 * (g >> 1) + (L >> 2) + 8 * hi;
+    const int col = 32 * dt + 16 * (g & 1) + 4 * (L & 3);
+    return 2u * uint32_t(swz_off<D>(row, col));
+}
+
 // Direct global->LDS copies issued as inline assembly: lane L reads the bytes
 // at base + off (base a wave-uniform pointer, off a per-lane byte offset) and
 // they land at LDS byte address lds + 16 * L (dwordx4) or lds + 4 * L (dword).

@@ -367,8 +367,8 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
 //     finishes query slice t-1: dP = dO V^T, dS = P (dP - delta) with P from
 //     the partner, dK += dS^T Q.
 // A step is BM query rows of one kept query block of one head of the GQA
-// group.  The Q/dO tiles and the rows' lse2/delta go through a 4-stage LDS
-// ring filled by direct global->LDS loads issued two steps ahead.
+// group.  The Q/dO tiles and the rows' lse2/delta go through a 3-stage LDS
+// ring filled by direct global->LDS loads issued one step ahead.
 // ---------------------------------------------------------------------------
 template <int DQK, int DV>
 struct DkvCfg {
@@ -378,14 +378,20 @@ struct DkvCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int NR = NW / 2;                       // waves per role (32 keys each)
+    static constexpr int NS = 3;                            // LDS ring stages (loads run one step ahead)
     static constexpr int Q_BYTES = BM * DQK * 2;
     static constexpr int O_BYTES = BM * DV * 2;
-    static constexpr int STAT_OFF = Q_BYTES + O_BYTES;      // float lse2[64], delta[64]
-    static constexpr int STAGE_BYTES = STAT_OFF + 2 * BM * 4;
+    static constexpr int ST_BYTES = 2 * BM * 4;             // float lse2[64], delta[64]
     static constexpr int XBUF_BYTES = NR * NH * 2 * 1024;   // P of all P waves for one step, (wave, half, cc)
-    static constexpr int NS = 3;                            // LDS ring stages (loads run one step ahead)
-    static constexpr int X_OFF = NS * STAGE_BYTES;
+    // LDS regions: the NS Q tiles, the NS dO tiles, the NS statistics slots,
+    // two P buffers
+    static constexpr int Q_OFF = 0;
+    static constexpr int O_OFF = Q_OFF + NS * Q_BYTES;
+    static constexpr int S_OFF = O_OFF + NS * O_BYTES;
+    static constexpr int X_OFF = S_OFF + NS * ST_BYTES;
     static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
+    static constexpr int HQ = 32 * DQK * 2;                 // bytes of 32 Q rows
+    static constexpr int HO = 32 * DV * 2;
     static constexpr int NQI = Q_BYTES / 1024;              // 1 KiB loads per Q tile
     static constexpr int NI = (Q_BYTES + O_BYTES) / 1024;   // 1 KiB loads per step
     static constexpr int KMAX = (NI + NW - 1) / NW;         // tile loads per wave per step
@@ -397,8 +403,10 @@ struct DkvCfg {
     static constexpr int NDV = DV / 32;
     static_assert(BM == 64, "one statistics load (64 lanes) covers a step");
     static_assert(Q_BYTES % 1024 == 0 && O_BYTES % 1024 == 0, "tiles split into whole wave loads");
-    static_assert(STAGE_BYTES % 16 == 0 && LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(NDMA_P <= NH * NCQ && NDMA_S <= NH * NCV, "loads must fit between the MFMAs");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((NH - 1) * HQ + 48 * DQK * 2 < 65536 && (NH - 1) * HO + 48 * DV * 2 < 65536,
+                  "row-group offsets fit the LDS instruction offset field");
+    static_assert(NDMA_P <= NH * NCQ && NDMA_S <= NCV, "loads must fit between the MFMAs");
 };
 
 // Step sequence of one workgroup: every BM-row part of every kept query
@@ -490,23 +498,39 @@ struct DkvSteps {
     }
 };
 
+// A ring position: which of the NS stages a role's reads point at.  advance()
+// moves to the next stage and returns the byte distance in units of one
+// stage (+1, or 1 - NS at the wrap).
+template <int NS>
+struct RingPos {
+    int s;
+    __device__ int advance() {
+        const int n = s == NS - 1 ? 0 : s + 1;
+        const int d = n - s;
+        s = n;
+        return d;
+    }
+};
+
 template <int DQK, int DV>
 struct DkvShared {
     using C = DkvCfg<DQK, DV>;
     const BwdArgs& a;
     uint16_t* lds;
     uint32_t lds_base;
+    const lds_char* lp;                             // the LDS window as an LDS pointer
     int w, lane, l32, h2, b, hk, n_base;
     uint32_t toff[C::KMAX];                         // per-lane byte offsets of this wave's tile loads (no clamping)
     uint32_t soff;                                  // per-lane byte offset of the statistics load
 
     // The loads of one step: wave-uniform source pointers (a head's rows) and
-    // LDS stage, per-lane byte offsets (the step's rows included).
+    // LDS destinations (Q tile, dO tile, statistics slot of the stage),
+    // per-lane byte offsets (the step's rows included).
     struct Dma {
         const uint16_t* q;
         const uint16_t* o;
         const float* st;
-        uint32_t sb;
+        uint32_t lq, lo, ls;
         uint32_t off[C::KMAX];
         uint32_t soff;
     };
@@ -520,8 +544,8 @@ struct DkvShared {
     }
 
     __device__ DkvShared(const BwdArgs& a_, uint16_t* lds_, int w_, int lane_, int b_, int hk_, int n_base_)
-        : a(a_), lds(lds_), lds_base(lds_address(lds_)), w(w_), lane(lane_), l32(lane_ & 31), h2(lane_ >> 5),
-          b(b_), hk(hk_), n_base(n_base_) {
+        : a(a_), lds(lds_), lds_base(lds_address(lds_)), lp(lds_ptr(lds_)), w(w_), lane(lane_), l32(lane_ & 31),
+          h2(lane_ >> 5), b(b_), hk(hk_), n_base(n_base_) {
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) toff[k] = load_off(load_index(w, k), C::BM);
         soff = uint32_t(4 * swap23(lane));         // LDS position L holds row swap23(L) of the step
@@ -538,20 +562,11 @@ struct DkvShared {
     __device__ uint32_t load_off(int j, int lim) const {
         return j < C::NQI ? tile_off<DQK>(j, lim, a.q_ss) : tile_off<DV>(j - C::NQI, lim, a.do_ss);
     }
-    __device__ const uint16_t* q_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2); }
-    __device__ const uint16_t* do_tile(int s) const { return lds + s * (C::STAGE_BYTES / 2) + C::Q_BYTES / 2; }
-    __device__ const float* stats(int s) const {
-        return reinterpret_cast<const float*>(lds + s * (C::STAGE_BYTES / 2) + C::STAT_OFF / 2);
-    }
-    __device__ char* xbuf(int par, int wr, int hh, int cc) const {
-        return reinterpret_cast<char*>(lds) + C::X_OFF + par * C::XBUF_BYTES + ((wr * C::NH + hh) * 2 + cc) * 1024 +
-               lane * 16;
-    }
 
     // Plan the loads of the steps' current step into stage s.
     __device__ void plan(Dma& d, const DkvSteps<C::BM>& st, int s) const {
         const int m = st.m;
-        d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        restage(d, s);
         d.q = st.qh;
         d.o = st.oh;
         d.st = (w & 1) == 0 ? st.lh : st.dh;
@@ -571,7 +586,11 @@ struct DkvShared {
         }
     }
     // Point a plan at another stage (re-loads its rows there).
-    __device__ void restage(Dma& d, int s) const { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); }
+    __device__ void restage(Dma& d, int s) const {
+        d.lq = lds_base + uint32_t(C::Q_OFF + s * C::Q_BYTES);
+        d.lo = lds_base + uint32_t(C::O_OFF + s * C::O_BYTES);
+        d.ls = lds_base + uint32_t(C::S_OFF + s * C::ST_BYTES);
+    }
 
     // Load k of this wave (k < KMAX: tile part; k == KMAX: the step's 64
     // statistics values, dS waves only -- lse2 by even waves, delta by odd ones).
@@ -579,14 +598,16 @@ struct DkvShared {
         if (k < C::KMAX) {
             const int j = load_index(w, k);
             const bool is_q = j < C::NQI;
-            dma16(is_q ? d.q : d.o, d.off[k], d.sb + uint32_t(is_q ? 1024 * j : C::Q_BYTES + 1024 * (j - C::NQI)));
+            dma16(is_q ? d.q : d.o, d.off[k], is_q ? d.lq + uint32_t(1024 * j) : d.lo + uint32_t(1024 * (j - C::NQI)));
         } else {
-            dma4(d.st, d.soff, d.sb + uint32_t(C::STAT_OFF + (w & 1) * 256));
+            dma4(d.st, d.soff, d.ls + uint32_t((w & 1) * 256));
         }
     }
 };
 
-// P wave: S, P, dV for 32 keys.
+// P wave: S, P, dV for 32 keys.  Reads: Q rows of the step's stage (S),
+// dO^T of the previous step's stage (dV), lse2 of the step; writes P to the
+// step's P buffer.
 template <int DQK, int DV>
 struct DkvPWave {
     using C = DkvCfg<DQK, DV>;
@@ -599,6 +620,14 @@ struct DkvPWave {
     f32x16_t dv[C::NDV];
     int qmin;                                       // first query row that sees the lane's key
     u32x4_t npp[C::NH][2];                          // P of the step just computed (half, cc), for its dV update
+    // read / write addresses: Q rows (chunk pair c) and lse2 at stage qs, dO^T
+    // (column group j, lo / hi) at stage os, P buffer of parity par
+    const lds_char* qa_at[C::NCQ];
+    const lds_char* ot_at[C::NDV][2];
+    const lds_char* l_at;
+    const lds_char* x_at;
+    RingPos<C::NS> qs{0}, os{C::NS - 1};
+    int par = 0;
 
     __device__ DkvPWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -609,21 +638,48 @@ struct DkvPWave {
         qmin = in ? (a.causal ? key - (a.Sk - a.Sq) : -(1 << 30)) : INT_MAX;   // rows < 2^30: no overflow below
 #pragma unroll
         for (int j = 0; j < C::NDV; ++j) dv[j] = f32x16_t{};
+        const lds_char* q0 = sh.lp + C::Q_OFF;
+        const lds_char* o0 = sh.lp + C::O_OFF + (C::NS - 1) * C::O_BYTES;
+#pragma unroll
+        for (int c = 0; c < C::NCQ; ++c) qa_at[c] = q0 + row_read_off<DQK>(sh.lane, c);
+#pragma unroll
+        for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) ot_at[j][hi] = o0 + tr_read_off<DV>(sh.lane, j, hi);
+        l_at = sh.lp + C::S_OFF + 16 * sh.h2;
+        x_at = sh.lp + C::X_OFF + wr * C::NH * 2 * 1024 + 16 * sh.lane;
     }
 
-    __device__ bf16x8_t dot_frag(const uint16_t* sdO, int hh, int f) const {   // f = (cc, j)
-        return b_operand_tr_swz<DV>(sdO, 32 * hh, f / C::NDV, 32 * (f % C::NDV), sh.lane);
+    // next step: every read moves one stage on, the P buffer flips
+    __device__ void advance() {
+        const int kq = qs.advance(), ko = os.advance();
+#pragma unroll
+        for (int c = 0; c < C::NCQ; ++c) qa_at[c] += kq * C::Q_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::NDV; ++j) {
+            ot_at[j][0] += ko * C::O_BYTES;
+            ot_at[j][1] += ko * C::O_BYTES;
+        }
+        l_at += kq * C::ST_BYTES;
+        x_at += par ? -C::XBUF_BYTES : C::XBUF_BYTES;
+        par ^= 1;
     }
 
-    // One step, two 32-row halves: S of stage s and P of it (to LDS parity
-    // par, read by the partner); with PREV, the dV MFMAs of the same half of
-    // the previous step (stage sp, its P kept in npp) are issued between the
-    // P arithmetic.  Masked steps fix the packed P up afterwards.
+    __device__ bf16x8_t q_row(int hh, int c) const { return as_bf16x8(lds_ld128(qa_at[c] + hh * C::HQ)); }
+    __device__ bf16x8_t dot_frag(int hh, int f) const {   // f = (cc, j)
+        const int off = (32 * hh + 16 * (f / C::NDV)) * DV * 2;
+        const u32x2_t lo = lds_ld_tr16(ot_at[f % C::NDV][0] + off);
+        const u32x2_t hi = lds_ld_tr16(ot_at[f % C::NDV][1] + off);
+        const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+        return as_bf16x8(v);
+    }
+
+    // One step, two 32-row halves: S and P (to the P buffer, read by the
+    // partner); with PREV, the dV MFMAs of the same half of the previous step
+    // (its P kept in npp) are issued between the P arithmetic.  Masked steps
+    // fix the packed P up afterwards.
     template <bool PREV>
-    __device__ void body(int s, int sp, int par, int m, bool mask, const Dma& d) {
-        const uint16_t* sQ = sh.q_tile(s);
-        const uint16_t* sdO = sh.do_tile(sp);
-        const float* sL = sh.stats(s);
+    __device__ void body(int m, bool mask, const Dma& d) {
         u32x4_t pn[C::NH][2];
 #pragma unroll
         for (int hh = 0; hh < C::NH; ++hh) {
@@ -631,33 +687,32 @@ struct DkvPWave {
             bf16x8_t fr[PFD + 1];
             if (PREV) {
 #pragma unroll
-                for (int f = 0; f < PFD; ++f) fr[f] = dot_frag(sdO, hh, f);
+                for (int f = 0; f < PFD; ++f) fr[f] = dot_frag(hh, f);
             }
             f32x16_t st = f32x16_t{};
             {
                 constexpr int PF = 4;
                 bf16x8_t qa[PF];
 #pragma unroll
-                for (int c = 0; c < PF && c < C::NCQ; ++c)
-                    qa[c] = row_operand_swz<DQK>(sQ, 32 * hh + sh.l32, 16 * c + 8 * sh.h2);
+                for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = q_row(hh, c);
                 // S MFMAs; this wave's loads for the next step go out between them
 #pragma unroll
                 for (int c = 0; c < C::NCQ; ++c) {
                     st = mfma32(qa[c % PF], kB[c], st);
-                    if (c + PF < C::NCQ) qa[c % PF] = row_operand_swz<DQK>(sQ, 32 * hh + sh.l32, 16 * (c + PF) + 8 * sh.h2);
+                    if (c + PF < C::NCQ) qa[c % PF] = q_row(hh, c + PF);
                     if (hh * C::NCQ + c < C::NDMA_P) sh.fire(d, hh * C::NCQ + c);
                 }
             }
-            float4 l4[4];
+            f32x4_t l4[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const float4*>(sL + 32 * hh + 8 * g + 4 * sh.h2);
+            for (int g = 0; g < 4; ++g) l4[g] = lds_ldf4(l_at + 4 * (32 * hh + 8 * g));
 
             // dV MFMAs f = (cc, j) of the previous step's half; P pairs q = (cc, jj) between them
             constexpr int NQ = 8;
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
                 if (PREV) {
-                    if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(sdO, hh, f + PFD);
+                    if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(hh, f + PFD);
                     dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), fr[f % (PFD + 1)], dv[f % C::NDV]);
                 }
 #pragma unroll
@@ -667,12 +722,12 @@ struct DkvPWave {
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int i = 8 * cc + 2 * jj + e;
-                        const float4 lv = l4[i >> 2];
+                        const f32x4_t lv = l4[i >> 2];
                         const float l = (i & 3) == 0 ? lv.x : (i & 3) == 1 ? lv.y : (i & 3) == 2 ? lv.z : lv.w;
                         p2[e] = fast_exp2(fmaf(st[i], a.scale_log2, -l));
                     }
                     pn[hh][cc][jj] = pack_bf16x2(p2[0], p2[1]);
-                    if (jj == 3) *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, hh, cc)) = pn[hh][cc];
+                    if (jj == 3) lds_st128(x_at + (hh * 2 + cc) * 1024, pn[hh][cc]);
                 }
             }
         }
@@ -690,7 +745,7 @@ struct DkvPWave {
                         const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
                         pn[hh][cc][jj] &= keep;
                     }
-                    *reinterpret_cast<u32x4_t*>(sh.xbuf(par, wr, hh, cc)) = pn[hh][cc];
+                    lds_st128(x_at + (hh * 2 + cc) * 1024, pn[hh][cc]);
                 }
             }
         }
@@ -701,21 +756,19 @@ struct DkvPWave {
         }
     }
 
-    __device__ void first(int s, int par, int m, bool mask, const Dma& d) { body<false>(s, s, par, m, mask, d); }
-    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) { body<true>(s, sp, par, m, mask, d); }
+    __device__ void first(int m, bool mask, const Dma& d) { body<false>(m, mask, d); }
+    __device__ void step(int m, bool mask, const Dma& d) { body<true>(m, mask, d); }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
         for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
     }
-    // dV update of the last step (stage sp)
-    __device__ void drain(int sp, int par) {
-        (void)par;
-        const uint16_t* sdO = sh.do_tile(sp);
+    // dV update of the last step (its dO^T reads at the stage advance() moved to)
+    __device__ void drain() {
 #pragma unroll
         for (int hh = 0; hh < C::NH; ++hh)
 #pragma unroll
             for (int f = 0; f < NF; ++f)
-                dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), dot_frag(sdO, hh, f), dv[f % C::NDV]);
+                dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), dot_frag(hh, f), dv[f % C::NDV]);
     }
     __device__ void store() const {
         uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
@@ -730,7 +783,8 @@ struct DkvPWave {
     }
 };
 
-// dS wave: dP, dS, dK for 32 keys.
+// dS wave: dP, dS, dK for 32 keys, one step behind the P waves.  Reads: dO
+// rows (dP), Q^T (dK), delta and the partner's P, all of the previous step.
 template <int DQK, int DV>
 struct DkvSWave {
     using C = DkvCfg<DQK, DV>;
@@ -740,6 +794,14 @@ struct DkvSWave {
     int wr;
     bf16x8_t vB[C::NCV];
     f32x16_t dk[C::NDK];
+    // read addresses: dO rows (chunk pair c), Q^T (column group j, lo / hi)
+    // and delta at stage ss, P buffer of parity par
+    const lds_char* oa_at[C::NCV];
+    const lds_char* qt_at[C::NDK][2];
+    const lds_char* d_at;
+    const lds_char* x_at;
+    RingPos<C::NS> ss{C::NS - 1};
+    int par = 1;
 
     __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -749,15 +811,48 @@ struct DkvSWave {
         for (int c = 0; c < C::NCV; ++c) vB[c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) dk[j] = f32x16_t{};
+        const lds_char* o0 = sh.lp + C::O_OFF + (C::NS - 1) * C::O_BYTES;
+        const lds_char* q0 = sh.lp + C::Q_OFF + (C::NS - 1) * C::Q_BYTES;
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) oa_at[c] = o0 + row_read_off<DV>(sh.lane, c);
+#pragma unroll
+        for (int j = 0; j < C::NDK; ++j)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) qt_at[j][hi] = q0 + tr_read_off<DQK>(sh.lane, j, hi);
+        d_at = sh.lp + C::S_OFF + (C::NS - 1) * C::ST_BYTES + 4 * C::BM + 16 * sh.h2;   // delta slot follows lse2
+        x_at = sh.lp + C::X_OFF + C::XBUF_BYTES + wr * C::NH * 2 * 1024 + 16 * sh.lane;
+    }
+
+    __device__ void advance() {
+        const int k = ss.advance();
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) oa_at[c] += k * C::O_BYTES;
+#pragma unroll
+        for (int j = 0; j < C::NDK; ++j) {
+            qt_at[j][0] += k * C::Q_BYTES;
+            qt_at[j][1] += k * C::Q_BYTES;
+        }
+        d_at += k * C::ST_BYTES;
+        x_at += par ? -C::XBUF_BYTES : C::XBUF_BYTES;
+        par ^= 1;
+    }
+
+    __device__ bf16x8_t o_row(int hh, int c) const { return as_bf16x8(lds_ld128(oa_at[c] + hh * C::HO)); }
+    __device__ bf16x8_t qt_frag(int hh, int f) const {   // f = (cc, j)
+        const int off = (32 * hh + 16 * (f / C::NDK)) * DQK * 2;
+        const u32x2_t lo = lds_ld_tr16(qt_at[f % C::NDK][0] + off);
+        const u32x2_t hi = lds_ld_tr16(qt_at[f % C::NDK][1] + off);
+        const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+        return as_bf16x8(v);
     }
 
     // dS pair (cc, jj): packed bf16 of P * (dP - delta)
-    __device__ uint32_t ds_pair(const f32x16_t& dpt, const float4 (&d4)[4], uint32_t pw, int cc, int jj) const {
+    __device__ uint32_t ds_pair(const f32x16_t& dpt, const f32x4_t (&d4)[4], uint32_t pw, int cc, int jj) const {
         float r[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int i = 8 * cc + 2 * jj + e;
-            const float4 dv4 = d4[i >> 2];
+            const f32x4_t dv4 = d4[i >> 2];
             const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
             const float p = e == 0 ? bf16_lo(pw) : bf16_hi(pw);
             r[e] = p * (dpt[i] - dl);
@@ -765,39 +860,35 @@ struct DkvSWave {
         return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the query slice in stage s whose P is in LDS parity par: per
-    // 32-row half dP, dS, dK.  With FIRE this wave's loads for the next step go
-    // out between the dP MFMAs.
+    // Finish the previous step's query slice: per 32-row half dP, dS, dK.  With
+    // FIRE this wave's loads for the next step go out between the first dP
+    // MFMAs.
     template <bool FIRE>
-    __device__ void finish(int s, int par, const Dma& d) {
+    __device__ void finish(const Dma& d) {
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));
-        const uint16_t* sQ = sh.q_tile(s);
-        const uint16_t* sdO = sh.do_tile(s);
-        const float* sD = sh.stats(s) + C::BM;      // delta slot follows the lse2 slot
 #pragma unroll
         for (int hh = 0; hh < C::NH; ++hh) {
             constexpr int PFO = 4;                  // dO rows read this many ahead
             bf16x8_t oa[PFO];
 #pragma unroll
-            for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = row_operand_swz<DV>(sdO, 32 * hh + sh.l32, 16 * c + 8 * sh.h2);
-            float4 d4[4];
+            for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = o_row(hh, c);
+            f32x4_t d4[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const float4*>(sD + 32 * hh + 8 * g + 4 * sh.h2);
+            for (int g = 0; g < 4; ++g) d4[g] = lds_ldf4(d_at + 4 * (32 * hh + 8 * g));
             u32x4_t pw[2];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) pw[cc] = *reinterpret_cast<const u32x4_t*>(sh.xbuf(par, wr, hh, cc));
+            for (int cc = 0; cc < 2; ++cc) pw[cc] = lds_ld128(x_at + (hh * 2 + cc) * 1024);
             constexpr int NQF = 2 * C::NDK;        // Q^T fragments (cc, j)
             bf16x8_t qf[NQF];
             f32x16_t dp = f32x16_t{};
 #pragma unroll
             for (int c = 0; c < C::NCV; ++c) {
                 dp = mfma32(oa[c % PFO], vB[c], dp);
-                if (c + PFO < C::NCV) oa[c % PFO] = row_operand_swz<DV>(sdO, 32 * hh + sh.l32, 16 * (c + PFO) + 8 * sh.h2);
-                if (FIRE && hh * C::NCV + c < C::NDMA_S) sh.fire(d, hh * C::NCV + c);
+                if (c + PFO < C::NCV) oa[c % PFO] = o_row(hh, c + PFO);
+                if (FIRE && hh == 0 && c < C::NDMA_S) sh.fire(d, c);
 #pragma unroll
-                for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f)
-                    qf[f] = b_operand_tr_swz<DQK>(sQ, 32 * hh, f / C::NDK, 32 * (f % C::NDK), sh.lane);
+                for (int f = c * NQF / C::NCV; f < (c + 1) * NQF / C::NCV; ++f) qf[f] = qt_frag(hh, f);
             }
             u32x4_t sa[2];
 #pragma unroll
@@ -809,22 +900,19 @@ struct DkvSWave {
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));   // the accumulators are not moved
     }
 
-    __device__ void first(int s, int par, int m, bool mask, const Dma& d) {
-        (void)par;
+    __device__ void first(int m, bool mask, const Dma& d) {
         (void)m;
         (void)mask;
-        (void)s;
         fire_all(d);
     }
-    __device__ void step(int s, int sp, int par, int m, bool mask, const Dma& d) {
-        (void)s;
+    __device__ void step(int m, bool mask, const Dma& d) {
         (void)m;
         (void)mask;
-        finish<true>(sp, par ^ 1, d);
+        finish<true>(d);
     }
-    __device__ void drain(int sp, int par) {
+    __device__ void drain() {
         Dma d{};
-        finish<false>(sp, par, d);
+        finish<false>(d);
     }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
@@ -844,14 +932,15 @@ struct DkvSWave {
     }
 };
 
-// Steps, barriers and loads, shared by both roles.  Step t uses ring stage
-// t % NS and may read stage t - 1; its P goes to LDS parity t % 2.  The loads
-// of step t + 1 go out from inside step t's MFMA stream (their stage was last
-// read in step t - 1, before the barrier that opens step t); past the last
-// step they re-read the last planned step's rows into the free stage, which
-// keeps the step bodies free of branches.  The loop body is one
-// straight-line block per role (masking is a fix-up on the packed P, outside
-// the MFMA block) so the accumulators stay put in registers.
+// Steps, barriers and loads, shared by both roles.  Step t's tiles sit in
+// ring stage t % NS; the P waves read stage t, the dS waves stage t - 1; P
+// goes to buffer t % 2.  The loads of step t + 1 go out from inside step t's
+// MFMA stream (their stage was last read in step t - 1, before the barrier
+// that opens step t); past the last step they re-read the last planned
+// step's rows into the free stage, which keeps the step bodies free of
+// branches.  The loop body is one straight-line block per role (masking is a
+// fix-up on the packed P, outside the MFMA block) so the accumulators stay
+// put in registers.
 template <int DQK, int DV, class Role>
 __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
                                          Role& role) {
@@ -872,7 +961,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     __syncthreads();
     if (have1) sh.plan(d, steps, 1);
     else sh.restage(d, 1);
-    role.first(0, 0, m, need_mask(m), d);
+    role.first(m, need_mask(m), d);
     int t = 0;
     while (have1) {
         ++t;
@@ -883,13 +972,15 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
         __syncthreads();
         if (have2) sh.plan(d, steps, (t + 1) % C::NS);
         else sh.restage(d, (t + 1) % C::NS);
-        role.step(t % C::NS, (t + C::NS - 1) % C::NS, t & 1, m, need_mask(m), d);
+        role.advance();
+        role.step(m, need_mask(m), d);
         have1 = have2;
         m1 = m2;
     }
     wait_vmcnt<0>();                                // no load may land in LDS after the workgroup ends
     __syncthreads();
-    role.drain(t % C::NS, t & 1);
+    role.advance();
+    role.drain();
 }
 
 template <int DQK, int DV>
