@@ -39,8 +39,10 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE]
 # Per-source additions.  split.hip: MFMA results go to VGPRs, so a kernel that
 # needs no AGPRs gets the whole 256-register budget of two waves per SIMD as
 # VGPRs (the default halves it between VGPRs and AGPRs) and its VALU reads the
-# accumulators without v_accvgpr copies.
-SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# accumulators without v_accvgpr copies; the memory-clause scheduling strategy
+# issues the LDS operand reads in groups ahead of their MFMAs (measured 3-5%
+# faster dK/dV pass than the default strategy).
+SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def _run(cmd, verbose):

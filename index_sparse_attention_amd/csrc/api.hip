@@ -44,6 +44,7 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if (a.B == 0) return ISATTN_OK;
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
     a.lse2 = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
+    a.order = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_order)) : nullptr;
     a.acc0 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc0));
     a.acc1 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc1));
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -52,6 +53,7 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
 
     if ((st = record(timer, slot, 0, s)) != ISATTN_OK) return st;
     if (launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (algo == ISATTN_ALGO_SPLIT && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
     hipError_t e;
     if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);

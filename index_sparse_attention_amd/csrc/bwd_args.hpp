@@ -20,6 +20,7 @@ struct BwdArgs {
     const float* lse;     // [B, Hq, Sq] natural-log LSE
     float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O)
     float* lse2;          // [B, Hq, stat_ld] workspace (SPLIT only): lse * log2(e); else null
+    int32_t* order;       // SPLIT work order: B*Hk*n_kb dK/dV items, then B*Hq*n_qb dQ items; else null
     float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
     float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;

@@ -38,6 +38,104 @@ namespace {
 __device__ __forceinline__ bf16x8_t gload_operand(const uint16_t* p) { return as_bf16x8(gload128(p)); }
 
 // ---------------------------------------------------------------------------
+// Work order
+//
+// Each pass's work items are cut into 8 contiguous ranges -- the ranges
+// xcd_item hands to the 8 XCDs, so an XCD's workgroups share operand tiles in
+// its L2 -- and each range is sorted by decreasing work (the kept blocks the
+// item visits): every XCD starts its longest items first and the shortest
+// fill the end (longest-processing-time-first list scheduling).  Counting
+// sort on min(work, kSchedKeys - 1); items of equal work land in any order,
+// which never changes a result (every item writes only its own outputs).
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedKeys = 4096;
+
+// kept query blocks a dK/dV item (b, KV head, key block) visits, over its GQA group
+__device__ int item_work_kv(const BwdArgs& a, int item) {
+    const int bh = item / a.n_kb;
+    const int kb = item - bh * a.n_kb;
+    const int b = bh / a.Hk;
+    const int hk = bh - b * a.Hk;
+    if (a.mask_kind == 1) {
+        int w = 0;
+        for (int g = 0; g < a.G; ++g) {
+            const int h = hk * a.G + g;
+            const int r = (b * a.Hm + h * a.Hm / a.Hq) * a.n_kb + kb;
+            w += a.k2q_ptr[r + 1] - a.k2q_ptr[r];
+        }
+        return w;
+    }
+    const int first_row = kb * kBlock - (a.Sk - a.Sq);
+    const int first = a.causal && first_row > 0 ? first_row / kBlock : 0;
+    return a.G * max(0, a.n_qb - first);
+}
+// kept key blocks a dQ item (b, query head, query block) visits
+__device__ int item_work_q(const BwdArgs& a, int item) {
+    const int bh = item / a.n_qb;
+    const int qb = item - bh * a.n_qb;
+    const int b = bh / a.Hq;
+    const int h = bh - b * a.Hq;
+    if (a.mask_kind == 1) {
+        const int r = (b * a.Hm + h * a.Hm / a.Hq) * a.n_qb + qb;
+        return a.q2k_ptr[r + 1] - a.q2k_ptr[r];
+    }
+    if (!a.causal) return a.n_kb;
+    const int diag = min(qb * kBlock + kBlock - 1, a.Sq - 1) + (a.Sk - a.Sq);
+    return diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
+}
+
+// workgroup (pass, XCD range): counting sort of the range into a.order
+__global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
+    __shared__ int cnt[kSchedKeys];
+    __shared__ int wsum[kSchedThreads / 64];
+    const int pass = blockIdx.x / kXcds;
+    const int x = blockIdx.x - pass * kXcds;
+    const int n_kv = a.B * a.Hk * a.n_kb;
+    const int n = pass == 0 ? n_kv : a.B * a.Hq * a.n_qb;
+    int32_t* out = a.order + (pass == 0 ? 0 : n_kv);
+    const int per = xcd_items_per(n);
+    const int lo = min(n, x * per);
+    const int hi = min(n, lo + per);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    auto key = [&](int i) {
+        const int wk = pass == 0 ? item_work_kv(a, i) : item_work_q(a, i);
+        return kSchedKeys - 1 - min(wk, kSchedKeys - 1);
+    };
+    for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
+    __syncthreads();
+    for (int i = lo + tid; i < hi; i += kSchedThreads) atomicAdd(&cnt[key(i)], 1);
+    __syncthreads();
+    // exclusive scan of the counts: thread t owns keys PER * t .. PER * t + PER - 1
+    constexpr int PER = kSchedKeys / kSchedThreads;
+    int v[PER];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        v[j] = cnt[PER * tid + j];
+        sum += v[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[tid >> 6] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < (tid >> 6); ++w) run += wsum[w];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        cnt[PER * tid + j] = run;
+        run += v[j];
+    }
+    __syncthreads();
+    for (int i = lo + tid; i < hi; i += kSchedThreads) out[lo + atomicAdd(&cnt[key(i)], 1)] = i;
+}
+
+// ---------------------------------------------------------------------------
 // dQ pass
 //
 // One workgroup per (batch, query head, 128-row query block); each wave owns
@@ -118,12 +216,12 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h2 = lane >> 5;
 
-    // items (b, h, query block), head-major; within a head the longest rows
-    // (most kept keys under a causal mask) first
-    const int item = xcd_item(blockIdx.x, a.n_qb * a.B * a.Hq);
-    if (item < 0) return;
+    // items (b, h, query block) in the per-XCD work order
+    const int slot = xcd_item(blockIdx.x, a.n_qb * a.B * a.Hq);
+    if (slot < 0) return;
+    const int item = a.order[a.B * a.Hk * a.n_kb + slot];
     const int bh = item / a.n_qb;
-    const int qb = a.n_qb - 1 - (item - bh * a.n_qb);
+    const int qb = item - bh * a.n_qb;
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int hk = h / a.G;
@@ -990,10 +1088,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps role and load addresses scalar
-    // items (b, KV head, key block), head-major; within a head the longest key
-    // columns (most kept query blocks under a causal mask) first
-    const int item = xcd_item(blockIdx.x, a.n_kb * a.B * a.Hk);
-    if (item < 0) return;
+    // items (b, KV head, key block) in the per-XCD work order
+    const int slot = xcd_item(blockIdx.x, a.n_kb * a.B * a.Hk);
+    if (slot < 0) return;
+    const int item = a.order[slot];
     const int bh = item / a.n_kb;
     const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
@@ -1040,6 +1138,12 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s) {
+    if (int64_t(a.B) * (int64_t(a.Hk) * a.n_kb + int64_t(a.Hq) * a.n_qb) == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_split_schedule, dim3(2 * kXcds), dim3(kSchedThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s) {
     if (a.Dqk == 64 && a.Dv == 64) return launch_dkdv_t<64, 64>(a, s);

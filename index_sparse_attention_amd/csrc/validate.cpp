@@ -60,6 +60,12 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
     p.off_lse2 = off;
     if (algo == ISATTN_ALGO_SPLIT) off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
+    // SPLIT: work order of the two passes (dK/dV items, then dQ items)
+    p.off_order = off;
+    if (algo == ISATTN_ALGO_SPLIT) {
+        const int64_t items = int64_t(s.batch) * (int64_t(s.heads_k) * p.n_kb + int64_t(s.heads_q) * p.n_qb);
+        off = align_up(off + size_t(items) * sizeof(int32_t), kWsAlign);
+    }
     if (algo == ISATTN_ALGO_LOOPK) {
         p.acc0_elems = rows_k * s.dim_qk;
         p.acc1_elems = rows_k * s.dim_v;

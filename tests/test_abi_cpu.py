@@ -57,9 +57,10 @@ def test_workspace_sizes(lib):
     delta = al(2 * 300 * 4 * 4)
     assert ws_bytes(lib, s, 0) == delta + al(2 * 200 * 2 * 128 * 4) * 2
     assert ws_bytes(lib, s, 1) == delta + al(2 * 300 * 4 * 128 * 4)
-    # SPLIT: delta and lse*log2(e), each padded per (batch, head) to whole 128-row blocks
+    # SPLIT: delta and lse*log2(e), each padded per (batch, head) to whole 128-row blocks, then the
+    # work order of the two passes (B*Hk*n_kb + B*Hq*n_qb int32)
     stats = al(2 * 4 * 384 * 4)
-    assert ws_bytes(lib, s, 2) == 2 * stats
+    assert ws_bytes(lib, s, 2) == 2 * stats + al((2 * 2 * 2 + 2 * 4 * 3) * 4)
     assert ws_bytes(lib, s, 7) == 0
     assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
     # converter: presence B*H*nQB*nKB bytes + row and column counts
