@@ -25,6 +25,7 @@
 // inside the MFMA stream, a step or two ahead, and take one workgroup barrier
 // per step.
 #include <climits>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -314,90 +315,108 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
               d.sb + uint32_t(is_k ? 1024 * j : C::K_BYTES + 1024 * (j - C::NKI)));
     };
 
-    bf16x8_t dsa[C::QT][2];                        // packed dS of the previous step
-    // dQ += dS K for the step in stage sp
-    auto dq_update = [&](int sp) {
-        const uint16_t* sK = lds + sp * (C::STAGE_BYTES / 2);
-        constexpr int NF = 2 * C::NDT;             // B fragments, f = cc * NDT + dt
-        constexpr int PF = NF < 3 ? NF : 3;        // prefetch depth
-        bf16x8_t fr[PF + 1];
-#pragma unroll
-        for (int f = 0; f < PF; ++f) fr[f] = b_operand_tr_swz<DQK>(sK, 0, f / C::NDT, 32 * (f % C::NDT), lane);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if (f + PF < NF)
-                fr[(f + PF) % (PF + 1)] = b_operand_tr_swz<DQK>(sK, 0, (f + PF) / C::NDT, 32 * ((f + PF) % C::NDT), lane);
-            const int cc = f / C::NDT, dt = f % C::NDT;
-#pragma unroll
-            for (int qt = 0; qt < C::QT; ++qt) dq[qt][dt] = mfma32(dsa[qt][cc], fr[f % (PF + 1)], dq[qt][dt]);
-        }
+    // K^T fragment f = (cc, dt) of the dQ MFMAs from stage sp
+    auto k_frag = [&](int sp, int f) {
+        return b_operand_tr_swz<DQK>(lds + sp * (C::STAGE_BYTES / 2), 0, f / C::NDT, 32 * (f % C::NDT), lane);
     };
-    // S, dP of the step in stage s (loads for two steps ahead issued between
-    // the MFMAs), then P and dS into dsa
-    auto scores = [&](int s, int n0) {
+    // S and dP MFMAs of the step in stage s; the loads for two steps ahead go
+    // out between them
+    auto sdp = [&](int s, f32x16_t (&st)[C::QT], f32x16_t (&dpt)[C::QT]) {
         const uint16_t* sK = lds + s * (C::STAGE_BYTES / 2);
         const uint16_t* sV = sK + C::K_BYTES / 2;
-        f32x16_t st[C::QT], dpt[C::QT];
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt) {
             st[qt] = f32x16_t{};
             dpt[qt] = f32x16_t{};
         }
-        {
-            constexpr int PF = 2;                  // prefetch depth (chunks)
-            bf16x8_t ka[PF + 1], va[PF + 1];
+        constexpr int PF = 2;                      // prefetch depth (chunks)
+        bf16x8_t ka[PF + 1], va[PF + 1];
 #pragma unroll
-            for (int c = 0; c < PF; ++c) {
-                ka[c] = row_operand_swz<DQK>(sK, l32, 16 * c + 8 * h2);
-                if (c < C::NCV) va[c] = row_operand_swz<DV>(sV, l32, 16 * c + 8 * h2);
-            }
-#pragma unroll
-            for (int c = 0; c < C::NCQ; ++c) {
-                if (c + PF < C::NCQ) ka[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sK, l32, 16 * (c + PF) + 8 * h2);
-                if (c + PF < C::NCV) va[(c + PF) % (PF + 1)] = row_operand_swz<DV>(sV, l32, 16 * (c + PF) + 8 * h2);
-#pragma unroll
-                for (int qt = 0; qt < C::QT; ++qt) st[qt] = mfma32(ka[c % (PF + 1)], qB[qt][c], st[qt]);
-                if (c < C::NCV) {
-#pragma unroll
-                    for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c % (PF + 1)], doB[qt][c], dpt[qt]);
-                }
-                if (c < C::KMAX) fire(c);
-            }
+        for (int c = 0; c < PF; ++c) {
+            ka[c] = row_operand_swz<DQK>(sK, l32, 16 * c + 8 * h2);
+            if (c < C::NCV) va[c] = row_operand_swz<DV>(sV, l32, 16 * c + 8 * h2);
         }
-        // P, dS; accumulator register i holds key n0 + 16*(i/8) + 8*h2 + i%8
-        const bool need_mask = (n0 + C::BN > a.Sk) || (a.causal && n0 + C::BN - 1 > m_base + shift);
-        if (need_mask) {
+#pragma unroll
+        for (int c = 0; c < C::NCQ; ++c) {
+            if (c + PF < C::NCQ) ka[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sK, l32, 16 * (c + PF) + 8 * h2);
+            if (c + PF < C::NCV) va[(c + PF) % (PF + 1)] = row_operand_swz<DV>(sV, l32, 16 * (c + PF) + 8 * h2);
+#pragma unroll
+            for (int qt = 0; qt < C::QT; ++qt) st[qt] = mfma32(ka[c % (PF + 1)], qB[qt][c], st[qt]);
+            if (c < C::NCV) {
+#pragma unroll
+                for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c % (PF + 1)], doB[qt][c], dpt[qt]);
+            }
+            if (c < C::KMAX) fire(c);
+        }
+    };
+    // P and dS of a step (packed into dsn, accumulator register i holding key
+    // n0 + 16*(i/8) + 8*h2 + i%8) with, when PREV, the dQ += dS K MFMAs of the
+    // previous step (its dS in dsp, its K in stage sp) issued between the
+    // arithmetic.  Masked steps clear the packed pairs afterwards.
+    bf16x8_t dsp[C::QT][2];
+    auto ds_step = [&](auto prev, int sp, const f32x16_t (&st)[C::QT], const f32x16_t (&dpt)[C::QT], int n0,
+                       bf16x8_t (&dsn)[C::QT][2]) {
+        constexpr bool PREV = decltype(prev)::value;
+        constexpr int NF = 2 * C::NDT;             // dQ B fragments, f = cc * NDT + dt
+        constexpr int PF = NF < 3 ? NF : 3;        // prefetch depth
+        constexpr int NP = 8 * C::QT;              // packed pairs (qt, cc, jj)
+        bf16x8_t fr[PF + 1];
+        if (PREV) {
+#pragma unroll
+            for (int f = 0; f < PF; ++f) fr[f] = k_frag(sp, f);
+        }
+        u32x4_t pk[C::QT][2];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (PREV) {
+                if (f + PF < NF) fr[(f + PF) % (PF + 1)] = k_frag(sp, f + PF);
+                const int cc = f / C::NDT, dt = f % C::NDT;
+#pragma unroll
+                for (int qt = 0; qt < C::QT; ++qt) dq[qt][dt] = mfma32(dsp[qt][cc], fr[f % (PF + 1)], dq[qt][dt]);
+            }
+#pragma unroll
+            for (int q = f * NP / NF; q < (f + 1) * NP / NF; ++q) {
+                const int qt = q >> 3, cc = (q >> 2) & 1, jj = q & 3;
+                float r[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int i = 8 * cc + 2 * jj + e;
+                    const float pv = fast_exp2(st[qt][i] * a.scale_log2 - lse2[qt]);
+                    r[e] = pv * (dpt[qt][i] - dlt[qt]);
+                }
+                pk[qt][cc][jj] = pack_bf16x2(r[0], r[1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);     // keep one MFMA and its share of the arithmetic together
+        }
+        if ((n0 + C::BN > a.Sk) || (a.causal && n0 + C::BN - 1 > m_base + shift)) {
+            // keys past Sk or (causal) past the row's last visible key: clear the pair halves
 #pragma unroll
             for (int qt = 0; qt < C::QT; ++qt) {
                 const int qrow = m_base + wrow + 32 * qt + l32;
-                const int nmax = min(a.Sk - 1, a.causal ? qrow + shift : a.Sk - 1);
+                const int rel = min(a.Sk - 1, a.causal ? qrow + shift : a.Sk - 1) - n0 - 8 * h2;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int n = n0 + 16 * (i >> 3) + 8 * h2 + (i & 7);
-                    float p = fast_exp2(st[qt][i] * a.scale_log2 - lse2[qt]);
-                    p = n <= nmax ? p : 0.f;
-                    dpt[qt][i] = p * (dpt[qt][i] - dlt[qt]);
-                }
+                for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int o = 16 * cc + 2 * jj;
+                        pk[qt][cc][jj] &= (o <= rel ? 0x0000ffffu : 0u) | (o + 1 <= rel ? 0xffff0000u : 0u);
+                    }
             }
-        } else {
-#pragma unroll
-            for (int qt = 0; qt < C::QT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(st[qt][i] * a.scale_log2 - lse2[qt]);
-                    dpt[qt][i] = p * (dpt[qt][i] - dlt[qt]);
-                }
         }
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                u32x4_t pk;
+            for (int cc = 0; cc < 2; ++cc) dsn[qt][cc] = as_bf16x8(pk[qt][cc]);
+    };
+    // dQ += dS K of the last step (stage sp)
+    auto dq_last = [&](int sp) {
+        constexpr int NF = 2 * C::NDT;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pk[j] = pack_bf16x2(dpt[qt][8 * cc + 2 * j], dpt[qt][8 * cc + 2 * j + 1]);
-                dsa[qt][cc] = as_bf16x8(pk);
-            }
+        for (int f = 0; f < NF; ++f) {
+            const bf16x8_t fr = k_frag(sp, f);
+#pragma unroll
+            for (int qt = 0; qt < C::QT; ++qt) dq[qt][f % C::NDT] = mfma32(dsp[qt][f / C::NDT], fr, dq[qt][f % C::NDT]);
+        }
     };
 
     if (steps.next_block()) {
@@ -417,7 +436,15 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         __syncthreads();
         if (have2) plan(n2, 2);
         else restage(2);
-        scores(0, n0);
+        f32x16_t st[C::QT], dpt[C::QT];
+        bf16x8_t dsn[C::QT][2];
+        sdp(0, st, dpt);
+        ds_step(std::false_type{}, 0, st, dpt, n0, dsn);
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt) {
+            dsp[qt][0] = dsn[qt][0];
+            dsp[qt][1] = dsn[qt][1];
+        }
         int t = 0;
         while (have1) {
             ++t;
@@ -428,15 +455,20 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
             __syncthreads();
             if (have3) plan(n3, (t + 2) % C::NS);
             else restage((t + 2) % C::NS);
-            dq_update((t + C::NS - 1) % C::NS);
-            scores(t % C::NS, n0);
+            sdp(t % C::NS, st, dpt);
+            ds_step(std::true_type{}, (t + C::NS - 1) % C::NS, st, dpt, n0, dsn);
+#pragma unroll
+            for (int qt = 0; qt < C::QT; ++qt) {
+                dsp[qt][0] = dsn[qt][0];
+                dsp[qt][1] = dsn[qt][1];
+            }
             have1 = have2;
             n1 = n2;
             have2 = have3;
             n2 = n3;
         }
         wait_vmcnt<0>();                           // no load may land in LDS after the workgroup ends
-        dq_update(t % C::NS);
+        dq_last(t % C::NS);
     }
 
     uint16_t* gdq = a.dq + b * a.dq_sb + h * a.dq_sh;
