@@ -14,7 +14,7 @@
 //                      a block is marked), writes the uint8 presence row and
 //                      its popcount.  HBM-bound on the index read.
 //   k_row_counts     : popcount of presence rows (block-mask path only).
-//   k_col_counts     : per-(b, h, kb) column counts, coalesced across kb.
+//   k_col_counts     : per-(b, h, kb) column counts, coalesced across kb, rows split over 4 waves.
 //   k_scan2          : two exclusive scans (rows, columns) -> row_ptr arrays.
 //   k_fill_q2k/k2q   : one wave per CSR row, ballot + prefix popcount writes
 //                      the ascending column list.
@@ -128,16 +128,24 @@ __global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ 
     if (lane == 0) qcnt[row] = c;
 }
 
+// Block (bh, 64-column tile): lane = column, wave w sums rows w, w + 4, ...
 __global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ presence,
                                                      int32_t n_qb, int32_t n_kb, int32_t tiles,
                                                      int32_t* __restrict__ kcnt) {
+    __shared__ int part[4][64];
     const int bh = blockIdx.x / tiles;
-    const int kb = (blockIdx.x - bh * tiles) * 256 + threadIdx.x;
-    if (kb >= n_kb) return;
-    const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int kb = (blockIdx.x - bh * tiles) * 64 + lane;
     int c = 0;
-    for (int qb = 0; qb < n_qb; ++qb) c += p[int64_t(qb) * n_kb] != 0;
-    kcnt[int64_t(bh) * n_kb + kb] = c;
+    if (kb < n_kb) {
+        const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
+#pragma unroll 4
+        for (int qb = w; qb < n_qb; qb += 4) c += p[int64_t(qb) * n_kb] != 0;
+    }
+    part[w][lane] = c;
+    __syncthreads();
+    if (w == 0 && kb < n_kb) kcnt[int64_t(bh) * n_kb + kb] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
 }
 
 // Block 0 scans cnt0 -> ptr0, block 1 scans cnt1 -> ptr1 (exclusive, with
@@ -262,7 +270,7 @@ hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n
         hipLaunchKernelGGL(k_row_counts, dim3((rows + 3) / 4), dim3(256), 0, s, presence, rows, n_kb,
                            qcnt);
     if (cols > 0) {
-        const int tiles = (n_kb + 255) / 256;
+        const int tiles = (n_kb + 63) / 64;
         hipLaunchKernelGGL(k_col_counts, dim3(BH * tiles), dim3(256), 0, s, presence, n_qb, n_kb, tiles,
                            kcnt);
     }

@@ -21,36 +21,51 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Delta blocks: RPB rows per pass, R passes per block, every thread issuing
+// the 2R 16-byte loads of its R rows before any arithmetic.
+constexpr int kPreRows = 4;
+
 template <int DV>
 __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk_delta, int64_t n4_0,
                                                          int64_t n4_1) {
     constexpr int L = DV / 8;          // lanes per row, 8 bf16 each
-    constexpr int RPB = kThreads / L;  // rows per block
+    constexpr int RPB = kThreads / L;  // rows per pass
+    constexpr int R = kPreRows;
     if (int32_t(blockIdx.x) < nblk_delta) {
         // rows (b, h, i) of the statistics arrays, i fastest (memory order);
         // rows i >= Sq are padding: delta = 0, lse2 = +inf
         const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
-        const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / L;
         const int sub = threadIdx.x % L;
-        float acc = 0.f;
-        const int64_t i = row % a.stat_ld;
-        const int64_t bh = row / a.stat_ld;
-        if (row < rows && i < a.Sq) {
-            const int64_t h = bh % a.Hq;
-            const int64_t b = bh / a.Hq;
-            const u32x4_t o = gload128(a.o + b * a.o_sb + i * a.o_ss + h * a.o_sh + 8 * sub);
-            const u32x4_t g = gload128(a.dO + b * a.do_sb + i * a.do_ss + h * a.do_sh + 8 * sub);
+        int64_t row[R], bh[R], i[R];
+        u32x4_t o[R], g[R];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc = fmaf(bf16_lo(o[j]), bf16_lo(g[j]), acc);
-                acc = fmaf(bf16_hi(o[j]), bf16_hi(g[j]), acc);
+        for (int r = 0; r < R; ++r) {
+            row[r] = (int64_t(blockIdx.x) * R + r) * RPB + threadIdx.x / L;
+            i[r] = row[r] % a.stat_ld;
+            bh[r] = row[r] / a.stat_ld;
+            o[r] = u32x4_t{0u, 0u, 0u, 0u};
+            g[r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (row[r] < rows && i[r] < a.Sq) {
+                const int64_t h = bh[r] % a.Hq;
+                const int64_t b = bh[r] / a.Hq;
+                o[r] = gload128(a.o + b * a.o_sb + i[r] * a.o_ss + h * a.o_sh + 8 * sub);
+                g[r] = gload128(a.dO + b * a.do_sb + i[r] * a.do_ss + h * a.do_sh + 8 * sub);
             }
         }
 #pragma unroll
-        for (int o = L / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (row < rows && sub == 0) {
-            a.delta[row] = acc;
-            if (a.lse2 != nullptr) a.lse2[row] = i < a.Sq ? a.lse[bh * a.Sq + i] * kLog2e : __builtin_inff();
+        for (int r = 0; r < R; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = fmaf(bf16_lo(o[r][j]), bf16_lo(g[r][j]), acc);
+                acc = fmaf(bf16_hi(o[r][j]), bf16_hi(g[r][j]), acc);
+            }
+#pragma unroll
+            for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+            if (row[r] < rows && sub == 0) {
+                a.delta[row[r]] = acc;
+                if (a.lse2 != nullptr) a.lse2[row[r]] = i[r] < a.Sq ? a.lse[bh[r] * a.Sq + i[r]] * kLog2e : __builtin_inff();
+            }
         }
     } else {
         const int64_t n4 = n4_0 + n4_1;
@@ -116,7 +131,7 @@ hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s) {
     (void)algo;
     const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
     const int L = a.Dv / 8;
-    const int rpb = kThreads / L;
+    const int rpb = kThreads / L * kPreRows;
     const int32_t nblk_delta = int32_t((rows + rpb - 1) / rpb);
     const int64_t n4_0 = a.acc0_elems / 4;
     const int64_t n4_1 = a.acc1_elems / 4;
