@@ -811,6 +811,12 @@ struct DkvPWave {
     template <bool PREV>
     __device__ void body(int m, bool mask, const Dma& d) {
         u32x4_t pn[C::NH][2];
+        // Q row operands of the S MFMAs, a ring PF chunks deep; the next
+        // half's first PF chunks are read during this half's dV MFMAs
+        constexpr int PF = 4;
+        bf16x8_t qa[PF];
+#pragma unroll
+        for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = q_row(0, c);
 #pragma unroll
         for (int hh = 0; hh < C::NH; ++hh) {
             constexpr int PFD = 2;                  // dO^T fragments read this many ahead
@@ -821,10 +827,6 @@ struct DkvPWave {
             }
             f32x16_t st = f32x16_t{};
             {
-                constexpr int PF = 4;
-                bf16x8_t qa[PF];
-#pragma unroll
-                for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = q_row(hh, c);
                 // S MFMAs; this wave's loads for the next step go out between them
 #pragma unroll
                 for (int c = 0; c < C::NCQ; ++c) {
@@ -841,6 +843,11 @@ struct DkvPWave {
             constexpr int NQ = 8;
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
+                if (f == 2 && hh + 1 < C::NH) {
+#pragma unroll
+                    for (int c = 0; c < PF && c < C::NCQ; ++c) qa[c] = q_row(hh + 1, c);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (PREV) {
                     if (f + PFD < NF) fr[(f + PFD) % (PFD + 1)] = dot_frag(hh, f + PFD);
                     dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), fr[f % (PFD + 1)], dv[f % C::NDV]);
