@@ -10,7 +10,10 @@ postprocess).  Inputs are resident in HBM before the timed region.  FLOP are
 counted over computed blocks only: 2 * (3*Dqk + 2*Dv) per (query, key) pair of
 every kept block, whatever the algorithm executes.
 
-Printed on stdout: one JSON line.  Progress goes to stderr.
+Printed on stdout: one JSON line.  Progress goes to stderr.  Besides the
+contract fields it carries the per-step median / min / P90, the mask
+conversion alone as GB/s (`converter`), the pre/postprocess GB/s, the main
+kernels' TFLOP/s and, unless --no-compare, the other algorithms' step times.
 """
 from __future__ import annotations
 
@@ -244,19 +247,42 @@ def main():
             step(None)
         torch.cuda.synchronize()
         timer.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        e0.record()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             step(timer)
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ev_ms = e0.elapsed_time(e1)
+        ev_ms = ev[0].elapsed_time(ev[-1])
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
         n, stage = timer.read()
         timer.close()
         return {"ms_per_step": ev_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+                "step_ms": {"median": float(np.median(per)), "min": float(per.min()),
+                            "p90": float(np.percentile(per, 90))},
                 "stage_ms": [s / max(n, 1) for s in stage], "n_timed": n}
+
+    def time_converter(reps=20):
+        """The mask conversion alone (it is also inside every step), as GB/s
+        over the bytes it must read: the presence matrix (block masks) or the
+        index tensor (index masks)."""
+        if w.mask not in ("block", "index"):
+            return None
+        for _ in range(3):
+            mk()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            mk()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        nbytes = int(pres_dev.numel()) if w.mask == "block" else int(idx_dev.numel()) * 4
+        return {"ms": round(ms, 4), "bytes_read": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "what": "presence -> CSR" if w.mask == "block" else "indices -> presence -> CSR"}
 
     log(f"timing {args.algo}: {args.warmup} warmup + {args.steps} steps")
     r = run(args.algo, args.steps, args.warmup)
@@ -295,6 +321,8 @@ def main():
         "kernels": kern,
         "stages_ms": {"pre": round(r["stage_ms"][0], 4), "main_a": round(r["stage_ms"][1], 4),
                       "main_b": round(r["stage_ms"][2], 4), "post": round(r["stage_ms"][3], 4)},
+        "step_ms": {k: round(v, 4) for k, v in r["step_ms"].items()},
+        "converter": time_converter(),
     }
     rows_q = w.batch * w.seqlen_q * w.heads_q
     rows_k = w.batch * w.seqlen_k * w.heads_k
