@@ -91,8 +91,11 @@ enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
  * (fp32 delta [B,Hq,Sq] plus head-major fp32 accumulators: dK,dV [B,Hk,Sk,D]
  * for LOOPK, dQ [B,Hq,Sq,Dqk] for LOOPQ; for SPLIT fp32 delta and
- * lse * log2(e), each [B,Hq,ceil(Sq/128)*128]; each part 256-byte aligned).
- * Returns 0 for a NULL shape or unknown algo. */
+ * lse * log2(e), each [B,Hq,ceil(Sq/128)*128], the int32 work order of its
+ * two passes, and -- when there are fewer than 512 (b, KV head, 128-key
+ * block) items -- the schedule and fp32 partial dK|dV of the items cut into
+ * parts; each part 256-byte aligned).  Returns 0 for a NULL shape or unknown
+ * algo. */
 size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
 
 /* Attention backward ([P1] Summary and Core changes 1-3): recompute

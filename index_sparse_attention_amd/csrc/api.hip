@@ -45,6 +45,11 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
     a.lse2 = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
     a.order = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_order)) : nullptr;
+    a.kv_parts_T = plan.kv_parts_T;
+    a.kv_units_bound = plan.kv_units_bound;
+    a.units = plan.kv_parts_T > 0 ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_units)) : nullptr;
+    a.item_info = plan.kv_parts_T > 0 ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_info)) : nullptr;
+    a.partial = plan.kv_parts_T > 0 ? reinterpret_cast<float*>(ws_at(workspace, plan.off_partial)) : nullptr;
     a.acc0 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc0));
     a.acc1 = reinterpret_cast<float*>(ws_at(workspace, plan.off_acc1));
     hipStream_t s = static_cast<hipStream_t>(stream);

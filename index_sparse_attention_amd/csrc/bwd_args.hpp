@@ -6,6 +6,12 @@
 namespace isattn {
 
 constexpr int kBlock = 128;   // mask block (query rows x keys) of the block-sparse path
+// SPLIT dK/dV pass with fewer (b, KV head, key block) items than twice the
+// CUs of an MI355X: items are cut into parts over their query-block lists
+// (the "part mode"), parts of one item write fp32 partial dK/dV that a
+// reduction sums in part order.
+constexpr int kPartModeItems = 512;
+constexpr int kMaxParts = 64;
 
 struct BwdArgs {
     // bf16 tensors [batch, seq, heads, dim], last dim contiguous, strides in elements
@@ -21,6 +27,14 @@ struct BwdArgs {
     float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O)
     float* lse2;          // [B, Hq, stat_ld] workspace (SPLIT only): lse * log2(e); else null
     int32_t* order;       // SPLIT work order: B*Hk*n_kb dK/dV items, then B*Hq*n_qb dQ items; else null
+    // SPLIT part mode (kv_parts_T > 0): target blocks per part, the units
+    // (item << 6 | part) in longest-first order with their count in units[bound],
+    // per item {work, parts, partial slot}, and the fp32 partial dK|dV slots
+    // [slot][128 keys][Dqk + Dv]
+    int32_t kv_parts_T, kv_units_bound;
+    int32_t* units;
+    int32_t* item_info;
+    float* partial;
     float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
     float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;

@@ -86,12 +86,88 @@ __device__ int item_work_q(const BwdArgs& a, int item) {
     return diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
 }
 
+// Exclusive block-wide scan of one value per thread (kSchedThreads threads);
+// returns this thread's prefix, *total gets the sum.
+__device__ int block_scan(int v, int* wsum, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[tid >> 6] = incl;
+    __syncthreads();
+    int pre = incl - v, tot = 0;
+    for (int w = 0; w < kSchedThreads / 64; ++w) {
+        if (w < (tid >> 6)) pre += wsum[w];
+        tot += wsum[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return pre;
+}
+
+// Part mode of the dK/dV pass (fewer than kPartModeItems items, so at most
+// one item per thread): item i gets P_i = ceil(work_i / T) parts (at most
+// kMaxParts), the units (i, p) are sorted by decreasing part length into
+// a.units (count at a.units[kv_units_bound]), and items with P_i > 1 get
+// consecutive fp32 partial slots.
+__device__ void schedule_parts(const BwdArgs& a, int* cnt, int* wsum) {
+    const int n = a.B * a.Hk * a.n_kb;
+    const int tid = threadIdx.x;
+    int work = 0, parts = 0, len = 0;
+    if (tid < n) {
+        work = item_work_kv(a, tid);
+        parts = min(kMaxParts, max(1, (work + a.kv_parts_T - 1) / a.kv_parts_T));
+        len = (work + parts - 1) / parts;
+    }
+    int n_units = 0, n_slots = 0;
+    block_scan(parts, wsum, &n_units);
+    const int slot = block_scan(parts > 1 ? parts : 0, wsum, &n_slots);
+    if (tid < n) {
+        a.item_info[3 * tid] = work;
+        a.item_info[3 * tid + 1] = parts;
+        a.item_info[3 * tid + 2] = slot;
+    }
+    if (tid == 0) a.units[a.kv_units_bound] = n_units;
+    const int key = kSchedKeys - 1 - min(len, kSchedKeys - 1);
+    for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
+    __syncthreads();
+    if (tid < n) atomicAdd(&cnt[key], parts);
+    __syncthreads();
+    constexpr int PER = kSchedKeys / kSchedThreads;
+    int v[PER];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        v[j] = cnt[PER * tid + j];
+        sum += v[j];
+    }
+    int total = 0;
+    int run = block_scan(sum, wsum, &total);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        cnt[PER * tid + j] = run;
+        run += v[j];
+    }
+    __syncthreads();
+    if (tid < n) {
+        const int at = atomicAdd(&cnt[key], parts);
+        for (int q = 0; q < parts; ++q) a.units[at + q] = (tid << 6) | q;
+    }
+}
+
 // workgroup (pass, XCD range): counting sort of the range into a.order
 __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
     __shared__ int cnt[kSchedKeys];
     __shared__ int wsum[kSchedThreads / 64];
     const int pass = blockIdx.x / kXcds;
     const int x = blockIdx.x - pass * kXcds;
+    if (pass == 0 && a.kv_parts_T > 0) {            // part mode: one workgroup schedules the dK/dV units
+        if (x == 0) schedule_parts(a, cnt, wsum);
+        return;
+    }
     const int n_kv = a.B * a.Hk * a.n_kb;
     const int n = pass == 0 ? n_kv : a.B * a.Hq * a.n_qb;
     int32_t* out = a.order + (pass == 0 ? 0 : n_kv);
@@ -552,6 +628,8 @@ struct DkvSteps {
     int b, hk, kb, n_base, shift, lane;
     int gi = 0, it = -1, part = 0, count = 0, first = 0;
     int m = 0;                                      // first row of the current step
+    int cum = 0;                                    // blocks in the group's earlier heads
+    int lo = 0, hi = INT_MAX;                       // range of the group's concatenated block lists
     const int32_t* list = nullptr;
     int chunk = 0, chunk_base = -1;
     // the current head's Q, dO and statistics rows
@@ -599,14 +677,17 @@ struct DkvSteps {
         return __builtin_amdgcn_readlane(chunk, it & 63);
     }
     // next kept block some row of which sees the key block; false at the end
+    // (of the item, or of its [lo, hi) range)
     __device__ bool next_block() {
         for (;;) {
             ++it;
             while (it >= count) {
                 if (++gi >= a.G) return false;
+                cum += count;
                 load_head();
                 it = 0;
             }
+            if (cum + it >= hi) return false;
             const int qb = qb_at();
             if (qb < 0 || qb >= a.n_qb) continue;  // malformed entry: nothing to do
             if (a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base) continue;
@@ -617,6 +698,12 @@ struct DkvSteps {
     }
     __device__ bool start() {
         load_head();
+        while (cum + count <= lo) {                 // heads entirely before the range
+            if (++gi >= a.G) return false;
+            cum += count;
+            load_head();
+        }
+        it = lo - cum - 1;
         return next_block();
     }
     __device__ bool next() {
@@ -907,7 +994,16 @@ struct DkvPWave {
             for (int f = 0; f < NF; ++f)
                 dv[f % C::NDV] = mfma32(as_bf16x8(npp[hh][f / C::NDV]), dot_frag(hh, f), dv[f % C::NDV]);
     }
-    __device__ void store() const {
+    __device__ void store(float* partial) const {
+        if (partial != nullptr) {                   // fp32 partial dV: slot columns Dqk ..
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = 32 * wr + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+#pragma unroll
+                for (int j = 0; j < C::NDV; ++j) partial[n * (DQK + DV) + DQK + 32 * j + sh.l32] = dv[j][i];
+            }
+            return;
+        }
         uint16_t* g = a.dv + sh.b * a.dv_sb + sh.hk * a.dv_sh;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1056,7 +1152,16 @@ struct DkvSWave {
         for (int k = 0; k < C::NDMA_S; ++k) sh.fire(d, k);
     }
 
-    __device__ void store() const {
+    __device__ void store(float* partial) const {
+        if (partial != nullptr) {                   // fp32 partial dK (unscaled): slot columns 0 .. Dqk
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = 32 * wr + 8 * (i >> 2) + 4 * sh.h2 + (i & 3);
+#pragma unroll
+                for (int j = 0; j < C::NDK; ++j) partial[n * (DQK + DV) + 32 * j + sh.l32] = dk[j][i];
+            }
+            return;
+        }
         uint16_t* g = a.dk + sh.b * a.dk_sb + sh.hk * a.dk_sh;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -1127,24 +1232,41 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps role and load addresses scalar
-    // items (b, KV head, key block) in the per-XCD work order
-    const int slot = xcd_item(blockIdx.x, a.n_kb * a.B * a.Hk);
-    if (slot < 0) return;
-    const int item = a.order[slot];
+    // items (b, KV head, key block) in the per-XCD work order, or in part mode
+    // the units (item, part) longest first
+    int item, lo = 0, hi = INT_MAX;
+    float* partial = nullptr;
+    if (a.kv_parts_T > 0) {
+        if (int(blockIdx.x) >= a.units[a.kv_units_bound]) return;
+        const int unit = a.units[blockIdx.x];
+        item = unit >> 6;
+        const int part = unit & (kMaxParts - 1);
+        const int work = a.item_info[3 * item], parts = a.item_info[3 * item + 1];
+        const int len = (work + parts - 1) / parts;
+        lo = part * len;
+        hi = min(work, lo + len);
+        if (parts > 1) partial = a.partial + int64_t(a.item_info[3 * item + 2] + part) * kBlock * (DQK + DV);
+    } else {
+        const int slot = xcd_item(blockIdx.x, a.n_kb * a.B * a.Hk);
+        if (slot < 0) return;
+        item = a.order[slot];
+    }
     const int bh = item / a.n_kb;
     const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
     DkvSteps<C::BM> steps(a, b, hk, kb, lane);
+    steps.lo = lo;
+    steps.hi = hi;
     if (w < C::NR) {
         DkvPWave<DQK, DV> role(sh, w);
         dkdv_run<DQK, DV>(sh, steps, role);
-        role.store();
+        role.store(partial);
     } else {
         DkvSWave<DQK, DV> role(sh, w - C::NR);
         dkdv_run<DQK, DV>(sh, steps, role);
-        role.store();
+        role.store(partial);
     }
 }
 
@@ -1162,6 +1284,38 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Part mode: dK = scale * sum of the parts' partial dK, dV = sum of the
+// partial dV, in part order, for the items cut into more than one part.
+// Workgroup (item, 8-key group): thread t covers columns 4t .. 4t+3 of the
+// slot rows (dK columns, then dV).
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
+    constexpr int W = DQK + DV;
+    const int item = blockIdx.x / (kBlock / 8);
+    const int parts = a.item_info[3 * item + 1];
+    if (parts <= 1) return;
+    const int slot = a.item_info[3 * item + 2];
+    const int bh = item / a.n_kb;
+    const int kb = item - bh * a.n_kb;
+    const int b = bh / a.Hk;
+    const int hk = bh - b * a.Hk;
+    const int key0 = (blockIdx.x % (kBlock / 8)) * 8;
+    for (int u = threadIdx.x; u < 8 * W / 4; u += 256) {
+        const int r = key0 + (4 * u) / W;
+        const int c = (4 * u) % W;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < parts; ++p)
+            acc += *reinterpret_cast<const f32x4_t*>(a.partial + (int64_t(slot + p) * kBlock + r) * W + c);
+        const int n = kb * kBlock + r;
+        if (n >= a.Sk) continue;
+        uint16_t* dst = c < DQK ? a.dk + b * a.dk_sb + hk * a.dk_sh + int64_t(n) * a.dk_ss + c
+                                : a.dv + b * a.dv_sb + hk * a.dv_sh + int64_t(n) * a.dv_ss + (c - DQK);
+        const float mul = c < DQK ? a.scale : 1.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = to_bf16(acc[e] * mul);
+    }
+}
+
 template <int DQK, int DV>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<DQK, DV>;
@@ -1172,6 +1326,13 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
+    if (a.kv_parts_T > 0) {                        // part mode: one workgroup per unit, then the reduction
+        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((k_dkdv_reduce<DQK, DV>), dim3(unsigned(items * (kBlock / 8))), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }

@@ -1,6 +1,8 @@
 // Host-side argument checking and workspace planning (no HIP calls).
 #include "validate.hpp"
 
+#include <algorithm>
+
 #include <cmath>
 #include <limits>
 
@@ -65,6 +67,25 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     if (algo == ISATTN_ALGO_SPLIT) {
         const int64_t items = int64_t(s.batch) * (int64_t(s.heads_k) * p.n_kb + int64_t(s.heads_q) * p.n_qb);
         off = align_up(off + size_t(items) * sizeof(int32_t), kWsAlign);
+    }
+    // SPLIT part mode: few dK/dV items, each cut into parts of about T
+    // query blocks (T spreads the dense-equivalent work over ~4 parts per CU)
+    p.kv_parts_T = 0;
+    p.kv_units_bound = 0;
+    p.off_units = p.off_info = p.off_partial = off;
+    const int64_t n_kv = int64_t(s.batch) * s.heads_k * p.n_kb;
+    if (algo == ISATTN_ALGO_SPLIT && n_kv > 0 && n_kv < kPartModeItems) {
+        const int64_t per_item = int64_t(p.G) * p.n_qb;      // query blocks of an item, dense
+        const int64_t T = std::max<int64_t>(1, (per_item * n_kv + 4 * kPartModeItems / 2 - 1) / (4 * kPartModeItems / 2));
+        const int64_t pmax = std::min<int64_t>(kMaxParts, std::max<int64_t>(1, (per_item + T - 1) / T));
+        p.kv_parts_T = int32_t(T);
+        p.kv_units_bound = int32_t(n_kv * pmax);
+        p.off_units = off;
+        off = align_up(off + size_t(p.kv_units_bound + 1) * sizeof(int32_t), kWsAlign);
+        p.off_info = off;
+        off = align_up(off + size_t(3 * n_kv) * sizeof(int32_t), kWsAlign);
+        p.off_partial = off;
+        off = align_up(off + size_t(p.kv_units_bound) * kBlock * (s.dim_qk + s.dim_v) * sizeof(float), kWsAlign);
     }
     if (algo == ISATTN_ALGO_LOOPK) {
         p.acc0_elems = rows_k * s.dim_qk;

@@ -27,6 +27,12 @@ CASES = {
     "tiny_1x1": Case(1, 1, 1, 1, 1, 64, 64, seed=15),
     "sk_one": Case(1, 130, 1, 2, 2, 128, 128, seed=16),
     "sq_one_causal": Case(1, 1, 257, 2, 2, 128, 128, causal=True, seed=17),
+    # 512 or more (b, KV head, key block) items: the SPLIT dK/dV pass runs one
+    # workgroup per item in the per-XCD order; the cases above (fewer items)
+    # cut items into parts with fp32 partials and a reduction
+    "many_items_dense": Case(4, 256, 256, 64, 64, 128, 128, seed=18),
+    "many_items_causal_ragged": Case(4, 256, 320, 64, 64, 128, 128, causal=True, seed=19),
+    "many_items_block_gqa": Case(2, 256, 256, 256, 128, 64, 64, mask="block", Hm=128, keep=0.5, seed=20),
 }
 
 _built = {}
