@@ -1093,11 +1093,84 @@ struct DkvSWave {
         return pack_bf16x2(r[0], r[1]);
     }
 
-    // Finish the previous step's query slice: per 32-row half dP, dS, dK.  With
-    // FIRE this wave's loads for the next step go out between the first dP
-    // MFMAs.
+    // Finish the previous step's query slice as a two-half pipeline that
+    // keeps the dS arithmetic under MFMAs: dP(0); dP(1) with dS(0) between
+    // its MFMAs; dK(0) with dS(1) between its MFMAs; dK(1).  With FIRE this
+    // wave's loads for the next step go out between the dP(0) MFMAs.
     template <bool FIRE>
-    __device__ void finish(const Dma& d) {
+    __device__ void finish_pipe(const Dma& d) {
+#pragma unroll
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));
+        constexpr int PFO = 4;                      // dO rows read this many ahead
+        constexpr int NQF = 2 * C::NDK;             // Q^T fragments (cc, j) of a half
+        constexpr int PFQ = 3;                      // Q^T fragments read this many ahead
+        static_assert(C::NH == 2, "two 32-row halves per step");
+        f32x16_t dp[C::NH];
+        f32x4_t d4[C::NH][4];
+        u32x4_t pw[C::NH][2];
+        u32x4_t sa[C::NH][2];
+        auto load_stats = [&](int hh) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) d4[hh][g] = lds_ldf4(d_at + 4 * (32 * hh + 8 * g));
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) pw[hh][cc] = lds_ld128(x_at + (hh * 2 + cc) * 1024);
+        };
+        auto ds_q = [&](int hh, int q) {
+            sa[hh][q >> 2][q & 3] = ds_pair(dp[hh], d4[hh], pw[hh][q >> 2][q & 3], q >> 2, q & 3);
+        };
+        bf16x8_t oa[PFO];
+        // dP(0)
+#pragma unroll
+        for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = o_row(0, c);
+        load_stats(0);
+        dp[0] = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) {
+            dp[0] = mfma32(oa[c % PFO], vB[c], dp[0]);
+            if (c + PFO < C::NCV) oa[c % PFO] = o_row(0, c + PFO);
+            if (FIRE && c < C::NDMA_S) sh.fire(d, c);
+        }
+        // dP(1) with dS(0) between its MFMAs
+#pragma unroll
+        for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = o_row(1, c);
+        load_stats(1);
+        dp[1] = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) {
+            dp[1] = mfma32(oa[c % PFO], vB[c], dp[1]);
+            if (c + PFO < C::NCV) oa[c % PFO] = o_row(1, c + PFO);
+#pragma unroll
+            for (int q = c * 8 / C::NCV; q < (c + 1) * 8 / C::NCV; ++q) ds_q(0, q);
+            __builtin_amdgcn_sched_barrier(0);     // one MFMA and its share of the arithmetic together
+        }
+        // dK(0) with dS(1) between its MFMAs
+        bf16x8_t qf[PFQ + 1];
+#pragma unroll
+        for (int f = 0; f < PFQ; ++f) qf[f] = qt_frag(0, f);
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) {
+            if (f + PFQ < NQF) qf[(f + PFQ) % (PFQ + 1)] = qt_frag(0, f + PFQ);
+            else qf[(f + PFQ) % (PFQ + 1)] = qt_frag(1, f + PFQ - NQF);
+            dk[f % C::NDK] = mfma32(as_bf16x8(sa[0][f / C::NDK]), qf[f % (PFQ + 1)], dk[f % C::NDK]);
+#pragma unroll
+            for (int q = f * 8 / NQF; q < (f + 1) * 8 / NQF; ++q) ds_q(1, q);
+            __builtin_amdgcn_sched_barrier(0);     // one MFMA and its share of the arithmetic together
+        }
+        // dK(1)
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) {
+            const int g = NQF + f;                  // fragment index across both halves
+            if (f + PFQ < NQF) qf[(g + PFQ) % (PFQ + 1)] = qt_frag(1, f + PFQ);
+            dk[f % C::NDK] = mfma32(as_bf16x8(sa[1][f / C::NDK]), qf[g % (PFQ + 1)], dk[f % C::NDK]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));   // the accumulators are not moved
+    }
+
+    // The same, half by half (dP, dS, dK per 32-row half): fewer live
+    // registers, for Dqk = 192.
+    template <bool FIRE>
+    __device__ void finish_halves(const Dma& d) {
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));
 #pragma unroll
@@ -1131,6 +1204,14 @@ struct DkvSWave {
         }
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) asm volatile("" : "+v"(dk[j]));   // the accumulators are not moved
+    }
+
+    // Finish the previous step's query slice; the two-half pipeline where its
+    // registers fit (Dqk <= 128).
+    template <bool FIRE>
+    __device__ void finish(const Dma& d) {
+        if constexpr (DQK <= 128) finish_pipe<FIRE>(d);
+        else finish_halves<FIRE>(d);
     }
 
     __device__ void first(int m, bool mask, const Dma& d) {
