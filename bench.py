@@ -10,10 +10,14 @@ postprocess).  Inputs are resident in HBM before the timed region.  FLOP are
 counted over computed blocks only: 2 * (3*Dqk + 2*Dv) per (query, key) pair of
 every kept block, whatever the algorithm executes.
 
+The backward's O and LSE come from the GPU forward (`attn_fwd`) on the same
+mask, run once before timing.
+
 Printed on stdout: one JSON line.  Progress goes to stderr.  Besides the
 contract fields it carries the per-step median / min / P90, the mask
-conversion alone as GB/s (`converter`), the pre/postprocess GB/s, the main
-kernels' TFLOP/s and, unless --no-compare, the other algorithms' step times.
+conversion alone as GB/s (`converter`), the forward alone (`forward`), the
+pre/postprocess GB/s, the main kernels' TFLOP/s and, unless --no-compare, the
+other algorithms' step times.
 """
 from __future__ import annotations
 
@@ -226,11 +230,28 @@ def main():
         idx_presence.reshape(-1, w.n_kb)[rows, qc] = 1
     kept = kept_blocks(w, presence, idx_presence)
     flop = flop_per_step(w, kept)
-    mean_keys = kept * 128.0 / (w.batch * w.heads_q * w.seqlen_q)
-    o_bits, lse_np = synth.stand_in_forward_stats(w, mean_keys)
-    o = t(o_bits)
-    lse = torch.from_numpy(lse_np).to(dev)
+    # the backward's O and LSE come from the GPU forward on the same mask
+    o, lse = isa.attn_fwd(q, k, v, mask=m0, causal=w.causal, softmax_scale=w.scale)
+    torch.cuda.synchronize()
     log(f"kept blocks {kept}, {flop / 1e9:.1f} GFLOP per step")
+
+    def time_forward(reps=20):
+        """The forward alone (not part of the backward step): O and LSE from Q,
+        K, V and the mask; FLOP = 2 GEMMs per kept pair."""
+        for _ in range(3):
+            isa.attn_fwd(q, k, v, mask=m0, causal=w.causal, softmax_scale=w.scale, o=o, lse=lse)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            isa.attn_fwd(q, k, v, mask=m0, causal=w.causal, softmax_scale=w.scale, o=o, lse=lse)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        fwd_flop = kept * 128 * 128 * 2 * (w.dim_qk + w.dim_v)
+        tf = fwd_flop / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(tf, 3), "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+                "flop": fwd_flop}
 
     def run(algo, steps, warmup):
         ws = torch.empty(isa.attn_bwd_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_k,
@@ -323,6 +344,7 @@ def main():
                       "main_b": round(r["stage_ms"][2], 4), "post": round(r["stage_ms"][3], 4)},
         "step_ms": {k: round(v, 4) for k, v in r["step_ms"].items()},
         "converter": time_converter(),
+        "forward": time_forward(),
     }
     rows_q = w.batch * w.seqlen_q * w.heads_q
     rows_k = w.batch * w.seqlen_k * w.heads_k

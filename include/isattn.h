@@ -129,6 +129,25 @@ isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape,
                                 int32_t algo, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Attention forward on the same mask descriptor: the outputs the backward
+ * consumes ([P1] Summary: the backward recomputes P from the forward's LSE;
+ * online rescaling as in the attention notes of the nvfp4-megamoe-kernel log):
+ *   S = softmax_scale * Q K^T on the kept pairs,
+ *   LSE = ln sum_j exp(S_ij)  (natural log, fp32; +inf for a row with none),
+ *   O = sum_j exp(S_ij - LSE_i) V_j  (bf16, 0 for a row with no kept key).
+ * q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv]: bf16 inputs; o
+ * [B,Sq,Hq,Dv] bf16 output; lse fp32 [B,Hq,Sq] contiguous output.  Both are
+ * overwritten.  mask_desc: NULL (dense) or a block CSR whose q2k lists are
+ * read (k2q may be NULL); causal as for isattn_attn_bwd.  No workspace.
+ * Errors as for isattn_attn_bwd; K/V rows are addressed with 32-bit byte
+ * offsets within a head (ceil(Sk/128)*128 * stride_s * 2 < 2^31 for k and v,
+ * else ISATTN_ERR_STRIDE_ALIGN).  stream: hipStream_t (NULL = default). */
+isattn_status_t isattn_attn_fwd(const isattn_shape_t* shape,
+                                const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                const isattn_tensor_t* v, const isattn_mask_t* mask_desc,
+                                int32_t causal, float softmax_scale,
+                                const isattn_tensor_t* o, float* lse, void* stream);
+
 /* Bytes of device workspace isattn_index_to_block_sparse needs (presence
  * matrix plus row/column counts, 256-byte aligned parts). */
 size_t isattn_index_to_block_sparse_workspace_bytes(int32_t batch, int32_t seqlen_q,

@@ -2,8 +2,9 @@
 
 Entry points (thin wrappers over the C ABI in include/isattn.h):
 
+* ``attn_fwd``              -- O and LSE of masked attention (same masks).
 * ``attn_bwd``              -- dQ, dK, dV of masked attention (dense, causal,
-                               GQA, 128x128 block-sparse); LoopK or LoopQ.
+                               GQA, 128x128 block-sparse); SPLIT, LoopK or LoopQ.
 * ``index_to_block_sparse`` -- int32 top-k token indices -> BlockMask (CSR).
 * ``block_mask_to_csr``     -- uint8 block presence -> BlockMask (CSR).
 """
@@ -12,6 +13,7 @@ from .api import (  # noqa: F401
     BlockMask,
     Timer,
     attn_bwd,
+    attn_fwd,
     attn_bwd_workspace_bytes,
     block_mask_to_csr,
     index_to_block_sparse,

@@ -40,6 +40,8 @@ SIGNATURES = {
     "isattn_attn_bwd_workspace_bytes": (c_size_t, [POINTER(Shape), c_int32]),
     "isattn_attn_bwd": (c_int32, _BWD_ARGS),
     "isattn_attn_bwd_timed": (c_int32, _BWD_ARGS + [c_void_p]),
+    "isattn_attn_fwd": (c_int32, [POINTER(Shape), _T, _T, _T, POINTER(Mask), c_int32, c_float, _T, c_void_p,
+                                  c_void_p]),
     "isattn_index_to_block_sparse_workspace_bytes": (c_size_t, [c_int32] * 6),
     "isattn_index_to_block_sparse": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,

@@ -139,6 +139,30 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     return dq, dk, dv
 
 
+def attn_fwd(q, k, v, mask: BlockMask | None = None, causal: bool = False, softmax_scale: float | None = None,
+             o=None, lse=None, stream=None):
+    """Attention forward on the GPU.  Returns (o bf16 [B,Sq,Hq,Dv], lse fp32
+    [B,Hq,Sq], natural log, +inf for a row with no kept key).  Same mask and
+    causal conventions as ``attn_bwd``; outputs are allocated when not given.
+    """
+    lib = _abi.load()
+    B, Sq, Hq, Dqk = q.shape
+    Sk, Hk, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    o = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
+    vq, vk, vv, vo = (_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")))
+    m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
+    _abi.check(lib.isattn_attn_fwd(ctypes.byref(shape), ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv),
+                                   ctypes.byref(m), int(bool(causal)), float(softmax_scale), ctypes.byref(vo),
+                                   lse.data_ptr(), _stream_ptr(stream)), "isattn_attn_fwd")
+    return o, lse
+
+
 def _csr_buffers(rows_q, rows_k, nnz_max, device):
     i32 = dict(dtype=torch.int32, device=device)
     return (torch.empty(rows_q + 1, **i32), torch.empty(max(nnz_max, 1), **i32),

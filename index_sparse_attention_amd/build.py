@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libisattn.so")
 
-HIP_SOURCES = ["api.hip", "convert.hip", "prepost.hip", "loopk.hip", "loopq.hip", "split.hip"]
+HIP_SOURCES = ["api.hip", "convert.hip", "prepost.hip", "loopk.hip", "loopq.hip", "split.hip", "fwd.hip"]
 CPP_SOURCES = ["validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,7 +42,8 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE]
 # accumulators without v_accvgpr copies; the memory-clause scheduling strategy
 # issues the LDS operand reads in groups ahead of their MFMAs (measured 3-5%
 # faster dK/dV pass than the default strategy).
-SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+                "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):

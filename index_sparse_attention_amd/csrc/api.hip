@@ -96,6 +96,17 @@ isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape, const isattn_tensor
                          workspace, workspace_bytes, stream, nullptr);
 }
 
+isattn_status_t isattn_attn_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                                const isattn_tensor_t* k, const isattn_tensor_t* v,
+                                const isattn_mask_t* mask_desc, int32_t causal, float softmax_scale,
+                                const isattn_tensor_t* o, float* lse, void* stream) {
+    FwdArgs a{};
+    const isattn_status_t st = validate_fwd(shape, q, k, v, mask_desc, causal, softmax_scale, o, lse, &a);
+    if (st != ISATTN_OK) return st;
+    if (a.B == 0) return ISATTN_OK;
+    return launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
+}
+
 isattn_status_t isattn_attn_bwd_timed(const isattn_shape_t* shape, const isattn_tensor_t* q,
                                       const isattn_tensor_t* k, const isattn_tensor_t* v,
                                       const isattn_tensor_t* o, const isattn_tensor_t* dO,

@@ -50,4 +50,18 @@ struct BwdArgs {
     float scale_log2;     // softmax_scale * log2(e)
 };
 
+// Launch arguments of the forward (O and LSE from Q, K, V and the mask).
+struct FwdArgs {
+    const uint16_t* q; int64_t q_sb, q_ss, q_sh;
+    const uint16_t* k; int64_t k_sb, k_ss, k_sh;
+    const uint16_t* v; int64_t v_sb, v_ss, v_sh;
+    uint16_t* o; int64_t o_sb, o_ss, o_sh;
+    float* lse;           // [B, Hq, Sq] natural-log LSE (+inf for a row with no kept key)
+    const int32_t* q2k_ptr; const int32_t* q2k_col;   // block CSR (mask_kind == 1)
+    int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
+    int32_t Hm, n_qb, n_kb;
+    int32_t mask_kind, causal;
+    float scale_log2;     // softmax_scale * log2(e)
+};
+
 }  // namespace isattn

@@ -60,6 +60,9 @@ __device__ __forceinline__ u32x2_t lds_read64(const uint16_t* p) {
 __device__ __forceinline__ u32x4_t gload128(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
 }
+// 16-byte global row chunk as an MFMA operand (resident operands are read once
+// per workgroup straight from HBM).
+__device__ __forceinline__ bf16x8_t gload_operand(const uint16_t* p) { return as_bf16x8(gload128(p)); }
 
 }  // namespace isattn
 

@@ -15,6 +15,8 @@ hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s);
 hipError_t launch_loopk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_loopq(const BwdArgs& a, hipStream_t s);
 // Atomic-free two-pass backward: dK/dV pass (key-outer), dQ pass (query-outer).
+// Attention forward: O and LSE.
+hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
 // Work order of the two passes (into a.order); runs before either.
 hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);

@@ -29,14 +29,12 @@
 
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "key_steps.hpp"
 
 namespace isattn {
 namespace {
 
 
-// 16-byte global row chunk as an MFMA operand (resident operands are read once
-// per workgroup straight from HBM).
-__device__ __forceinline__ bf16x8_t gload_operand(const uint16_t* p) { return as_bf16x8(gload128(p)); }
 
 // ---------------------------------------------------------------------------
 // Work order
@@ -245,44 +243,6 @@ struct DqCfg {
     static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
 };
 
-// Step sequence of a dQ workgroup: every 32-key part of every kept key block
-// that holds a key some row of the query block sees (key <= last, the last key
-// visible to the block's last row).  The kept key blocks are read 64 at a time
-// into a register (one per lane).
-struct DqSteps {
-    int it = -1, sub = 0, count = 0, n0 = 0, n_kb = 0, last = 0, lane = 0;
-    const int32_t* list = nullptr;
-    int chunk = 0, chunk_base = -1;
-
-    __device__ int kb_at() {
-        if (list == nullptr) return it;
-        const int base = it & ~63;
-        if (base != chunk_base) {
-            chunk_base = base;
-            chunk = base + lane < count ? list[base + lane] : -1;
-        }
-        return __builtin_amdgcn_readlane(chunk, it & 63);
-    }
-    __device__ bool next_block() {
-        for (;;) {
-            if (++it >= count) return false;
-            const int kb = kb_at();
-            if (kb < 0 || kb >= n_kb) continue;     // malformed entry: nothing to do
-            if (kb * kBlock > last) continue;
-            sub = 0;
-            n0 = kb * kBlock;
-            return true;
-        }
-    }
-    __device__ bool next() {
-        if (++sub < kBlock / 32 && n0 + 32 <= last) {
-            n0 += 32;
-            return true;
-        }
-        return next_block();
-    }
-};
-
 template <int DQK, int DV, int WR>
 // two workgroups per CU (two waves per SIMD) where the registers allow
 __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(BwdArgs a) {
@@ -306,7 +266,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     const int last_row = min(m_base + C::BM - 1, a.Sq - 1);
     const int shift = a.Sk - a.Sq;
 
-    DqSteps steps;
+    KeySteps steps;
     steps.lane = lane;
     steps.n_kb = a.n_kb;
     const int diag = last_row + shift;

@@ -239,6 +239,68 @@ static isattn_status_t check_csr_outputs(int64_t rows_q_total, int64_t nnz_max,
     return ISATTN_OK;
 }
 
+isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                             const isattn_tensor_t* k, const isattn_tensor_t* v,
+                             const isattn_mask_t* mask, int32_t causal, float softmax_scale,
+                             const isattn_tensor_t* o, const float* lse, FwdArgs* args) {
+    if (shape == nullptr) return ISATTN_ERR_NULL;
+    const isattn_shape_t s = *shape;
+    if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
+        return ISATTN_ERR_SHAPE;
+    if (s.heads_q % s.heads_k != 0) return ISATTN_ERR_SHAPE;
+    if (s.seqlen_q >= (1 << 30) || s.seqlen_k >= (1 << 30)) return ISATTN_ERR_SHAPE;
+    if (int64_t(s.batch) * s.heads_q * cdiv(s.seqlen_q, kBlock) >= (int64_t(1) << 31) - 8)
+        return ISATTN_ERR_SHAPE;
+    if (!supported_dims(s.dim_qk, s.dim_v)) return ISATTN_ERR_UNSUPPORTED;
+    if (!std::isfinite(softmax_scale)) return ISATTN_ERR_UNSUPPORTED;
+    const int64_t nq = int64_t(s.batch) * s.seqlen_q * s.heads_q;
+    const int64_t nk = int64_t(s.batch) * s.seqlen_k * s.heads_k;
+    isattn_status_t st;
+    if ((st = check_view(q, nq)) != ISATTN_OK) return st;
+    if ((st = check_view(k, nk)) != ISATTN_OK) return st;
+    if ((st = check_view(v, nk)) != ISATTN_OK) return st;
+    if ((st = check_view(o, nq)) != ISATTN_OK) return st;
+    if (nq > 0 && lse == nullptr) return ISATTN_ERR_NULL;
+    if (nq > 0) {
+        // K/V rows of a head are addressed with 32-bit byte offsets
+        const int64_t rk = int64_t(cdiv(s.seqlen_k, kBlock)) * kBlock;
+        if (rk * k->stride_s * 2 >= (int64_t(1) << 31) || rk * v->stride_s * 2 >= (int64_t(1) << 31))
+            return ISATTN_ERR_STRIDE_ALIGN;
+    }
+    FwdArgs a{};
+    a.mask_kind = ISATTN_MASK_DENSE;
+    if (mask != nullptr && mask->kind != ISATTN_MASK_DENSE) {
+        if (mask->kind != ISATTN_MASK_BLOCK_CSR) return ISATTN_ERR_MASK;
+        if (mask->block_q != kBlock || mask->block_k != kBlock) return ISATTN_ERR_UNSUPPORTED;
+        if (mask->heads != 1 && mask->heads != s.heads_k && mask->heads != s.heads_q)
+            return ISATTN_ERR_MASK;
+        if (mask->q2k_row_ptr == nullptr || mask->q2k_col == nullptr) return ISATTN_ERR_NULL;
+        a.mask_kind = ISATTN_MASK_BLOCK_CSR;
+        a.Hm = mask->heads;
+        a.q2k_ptr = mask->q2k_row_ptr;
+        a.q2k_col = mask->q2k_col;
+    }
+    copy_view(q, &a.q, &a.q_sb, &a.q_ss, &a.q_sh);
+    copy_view(k, &a.k, &a.k_sb, &a.k_ss, &a.k_sh);
+    copy_view(v, &a.v, &a.v_sb, &a.v_ss, &a.v_sh);
+    copy_view_out(o, &a.o, &a.o_sb, &a.o_ss, &a.o_sh);
+    a.lse = const_cast<float*>(lse);
+    a.B = s.batch;
+    a.Sq = s.seqlen_q;
+    a.Sk = s.seqlen_k;
+    a.Hq = s.heads_q;
+    a.Hk = s.heads_k;
+    a.G = s.heads_q / s.heads_k;
+    a.Dqk = s.dim_qk;
+    a.Dv = s.dim_v;
+    a.n_qb = cdiv(s.seqlen_q, kBlock);
+    a.n_kb = cdiv(s.seqlen_k, kBlock);
+    a.causal = causal != 0;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    *args = a;
+    return ISATTN_OK;
+}
+
 isattn_status_t validate_index(const int32_t* indices, int32_t batch, int32_t seqlen_q,
                                int32_t seqlen_k, int32_t nhk, int32_t topk, int32_t block_q,
                                int32_t block_k, const int32_t* q2k_row_ptr, const int32_t* q2k_col,

@@ -97,6 +97,7 @@ def build_case(c: Case) -> Case:
         d["omask"] = oracle.dense_mask()
     f = {k: oracle.bf16_to_f64(d[k]) for k in ("q", "k", "v", "do")}
     O, L = oracle.attn_fwd(f["q"], f["k"], f["v"], d["omask"], c.causal, c.scale, heads=c.heads)
+    d["o64"], d["lse64"] = O, L
     d["o"] = oracle.round_to_bf16(O)
     d["lse"] = oracle.round_to_f32(L)
     return c

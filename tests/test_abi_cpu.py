@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
@@ -140,6 +140,27 @@ def test_bwd_validation_errors(lib):
     c = Call(lib, algo=2); c.views["v"].stride_s = 1 << 22; c.views["v"].stride_b = 256 << 22
     assert c() == STRIDE
     c = Call(lib, algo=2); c.ws_bytes -= 1; assert c() == WS
+
+
+def test_fwd_validation_errors(lib):
+    s = shape()
+    views = {n: _abi.Tensor(FAKE, 256 * 2 * 128, 2 * 128, 128) for n in ("q", "k", "v", "o")}
+
+    def call(shape_ptr=True, lse=FAKE, mask=None, scale=0.125, **over):
+        vv = dict(views, **over)
+        ref = lambda t: ctypes.byref(t) if t is not None else None
+        return lib.isattn_attn_fwd(ctypes.byref(s) if shape_ptr else None, ref(vv["q"]), ref(vv["k"]),
+                                   ref(vv["v"]), ctypes.byref(mask) if mask is not None else None, 0, scale,
+                                   ref(vv["o"]), lse, None)
+    assert call(shape_ptr=False) == NULL
+    assert call(q=None) == NULL
+    assert call(lse=None) == NULL
+    assert call(o=_abi.Tensor(FAKE + 8, 0, 256, 128)) == STRIDE
+    assert call(scale=float("inf")) == UNSUP
+    assert call(mask=_abi.Mask(7, 128, 128, 2, FAKE, FAKE, None, None)) == MASK
+    assert call(mask=_abi.Mask(1, 128, 128, 2, None, None, FAKE, FAKE)) == NULL
+    assert call(mask=_abi.Mask(1, 64, 64, 2, FAKE, FAKE, None, None)) == UNSUP
+    assert call(k=_abi.Tensor(FAKE, 0, 1 << 22, 128)) == STRIDE     # 256 rows x 2^22 x 2 B = 2^31
 
 
 def test_index_converter_validation_errors(lib):
