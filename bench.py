@@ -46,9 +46,9 @@ def main_kernels(algo, dqk, dv):
         return [("k_bwd_loopk", 1, full, full)]
     if algo == "loopq":
         return [("k_bwd_loopq", 1, full, full)]
-    # split: the dK/dV pass does S, dP, dV, dK; the dQ pass does dQ plus a recompute of S and dP
-    return [("k_bwd_dkdv", 1, 2 * (2 * dqk + 2 * dv), 2 * (2 * dqk + 2 * dv)),
-            ("k_bwd_dq", 2, 2 * dqk, 2 * (2 * dqk + dv))]
+    # split: the dQ pass (first) does dQ plus a recompute of S and dP; the dK/dV pass does S, dP, dV, dK
+    return [("k_bwd_dq", 1, 2 * dqk, 2 * (2 * dqk + dv)),
+            ("k_bwd_dkdv", 2, 2 * (2 * dqk + 2 * dv), 2 * (2 * dqk + 2 * dv))]
 
 
 def log(*a):

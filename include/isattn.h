@@ -83,9 +83,10 @@ typedef struct isattn_mask {
  * query tiles of every head of the GQA group; dK/dV stay on chip and are
  * stored directly, dQ is reduced as fp32 atomics and converted afterwards.
  * SPLIT: both loop orders, each restricted to the outputs it keeps on chip --
- * a LOOPQ pass for dK/dV and a LOOPK pass for dQ -- recomputing P and dS in
- * each; no atomics and no fp32 accumulators (1.4x the MFMA work at
- * Dqk = Dv). */
+ * a LOOPK pass for dQ, which runs first and also computes delta and
+ * lse * log2(e) of every query row, then a LOOPQ pass for dK/dV --
+ * recomputing P and dS in each; no atomics, no fp32 accumulators and no
+ * separate preprocess (1.4x the MFMA work at Dqk = Dv). */
 enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
 
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
@@ -199,9 +200,10 @@ const char* isattn_version(void);
 
 /* ---- Stage timing (measurement support) -----------------------------------
  * A timer records HIP events on the call's stream around the launches of
- * isattn_attn_bwd_timed: stage [0] preprocess, [1] first main kernel (LOOPK /
- * LOOPQ main loop, or the SPLIT dK/dV pass), [2] second main kernel (the SPLIT
- * dQ pass; empty otherwise), [3] postprocess (empty for SPLIT).
+ * isattn_attn_bwd_timed: stage [0] preprocess (for SPLIT only its work-order
+ * kernel), [1] first main kernel (LOOPK / LOOPQ main loop, or the SPLIT dQ
+ * pass), [2] second main kernel (the SPLIT dK/dV pass; empty otherwise),
+ * [3] postprocess (empty for SPLIT).
  * isattn_timer_read synchronises on the recorded events and returns the number
  * of timed calls and the summed milliseconds per stage (stage_ms[4]).  A timer
  * holds `capacity` calls; further calls wrap and overwrite. */

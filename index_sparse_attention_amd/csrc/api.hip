@@ -57,16 +57,18 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if (timer != nullptr) slot = timer->recorded % timer->capacity;
 
     if ((st = record(timer, slot, 0, s)) != ISATTN_OK) return st;
-    if (launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    // SPLIT needs no preprocess launch: its dQ pass, which runs first,
+    // computes delta and lse2 for the dK/dV pass
+    if (algo != ISATTN_ALGO_SPLIT && launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
     if (algo == ISATTN_ALGO_SPLIT && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
     hipError_t e;
     if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);
     else if (algo == ISATTN_ALGO_LOOPQ) e = launch_loopq(a, s);
-    else e = launch_split_dkdv(a, s);
+    else e = launch_split_dq(a, s);
     if (e != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 2, s)) != ISATTN_OK) return st;
-    if (algo == ISATTN_ALGO_SPLIT && launch_split_dq(a, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (algo == ISATTN_ALGO_SPLIT && launch_split_dkdv(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 3, s)) != ISATTN_OK) return st;
     if (launch_postprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 4, s)) != ISATTN_OK) return st;

@@ -13,11 +13,14 @@
 //                      an LDS bitmap (test-then-set keeps LDS atomics rare once
 //                      a block is marked), writes the uint8 presence row and
 //                      its popcount.  HBM-bound on the index read.
-//   k_row_counts     : popcount of presence rows (block-mask path only).
-//   k_col_counts     : per-(b, h, kb) column counts, coalesced across kb, rows split over 4 waves.
+//   k_counts         : popcount of presence rows (block-mask path only) and
+//                      per-(b, h, kb) column counts (coalesced across kb, rows
+//                      split over 4 waves), one launch with two block roles.
 //   k_scan2          : two exclusive scans (rows, columns) -> row_ptr arrays.
-//   k_fill_q2k/k2q   : one wave per CSR row, ballot + prefix popcount writes
-//                      the ascending column list.
+//   k_fill           : one wave per CSR row of either form, ballot + prefix
+//                      popcount writes the ascending column list; one launch.
+// The conversion is latency-bound at the benchmark's sizes, so launches are
+// fused wherever no result crosses workgroups.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -115,28 +118,29 @@ __global__ __launch_bounds__(kPresThreads) void k_index_presence(
     }
 }
 
-__global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ presence,
-                                                     int32_t rows, int32_t n_kb,
-                                                     int32_t* __restrict__ qcnt) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const uint8_t* p = presence + int64_t(row) * n_kb;
-    int c = 0;
-    for (int kb = lane; kb < n_kb; kb += 64) c += p[kb] != 0;
-    c = wave_sum(c);
-    if (lane == 0) qcnt[row] = c;
-}
-
-// Block (bh, 64-column tile): lane = column, wave w sums rows w, w + 4, ...
-__global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ presence,
-                                                     int32_t n_qb, int32_t n_kb, int32_t tiles,
-                                                     int32_t* __restrict__ kcnt) {
+// Row counts (blocks [0, row_blocks): 4 rows per block, one per wave) and
+// column counts (the rest: block = (bh, 64-column tile), lane = column, wave
+// w sums rows w, w + 4, ...) in one launch.
+__global__ __launch_bounds__(256) void k_counts(const uint8_t* __restrict__ presence, int32_t rows,
+                                                int32_t row_blocks, int32_t n_qb, int32_t n_kb,
+                                                int32_t tiles, int32_t* __restrict__ qcnt,
+                                                int32_t* __restrict__ kcnt) {
     __shared__ int part[4][64];
-    const int bh = blockIdx.x / tiles;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int kb = (blockIdx.x - bh * tiles) * 64 + lane;
+    if (int32_t(blockIdx.x) < row_blocks) {
+        const int row = blockIdx.x * 4 + w;
+        if (row >= rows) return;
+        const uint8_t* p = presence + int64_t(row) * n_kb;
+        int c = 0;
+        for (int kb = lane; kb < n_kb; kb += 64) c += p[kb] != 0;
+        c = wave_sum(c);
+        if (lane == 0) qcnt[row] = c;
+        return;
+    }
+    const int cb = blockIdx.x - row_blocks;
+    const int bh = cb / tiles;
+    const int kb = (cb - bh * tiles) * 64 + lane;
     int c = 0;
     if (kb < n_kb) {
         const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
@@ -200,36 +204,38 @@ __global__ __launch_bounds__(kScanThreads) void k_scan2(const int32_t* __restric
     }
 }
 
-__global__ __launch_bounds__(256) void k_fill_q2k(const uint8_t* __restrict__ presence, int32_t rows,
-                                                   int32_t n_kb, const int32_t* __restrict__ q2k_ptr,
-                                                   int32_t* __restrict__ q2k_col) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+// Column lists in one launch: blocks [0, q_blocks) fill the Q->K rows (one
+// row per wave, lanes over 64 columns at a time), the rest the K->Q columns
+// (one column per wave, lanes over 64 rows at a time); ballot + popcount
+// place each kept block at its ascending position.
+__global__ __launch_bounds__(256) void k_fill(const uint8_t* __restrict__ presence, int32_t rows,
+                                              int32_t cols, int32_t q_blocks, int32_t n_qb,
+                                              int32_t n_kb, const int32_t* __restrict__ q2k_ptr,
+                                              int32_t* __restrict__ q2k_col,
+                                              const int32_t* __restrict__ k2q_ptr,
+                                              int32_t* __restrict__ k2q_col) {
     const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const uint8_t* p = presence + int64_t(row) * n_kb;
-    int base = q2k_ptr[row];
     const uint64_t below = (uint64_t(1) << lane) - 1;
-    for (int c0 = 0; c0 < n_kb; c0 += 64) {
-        const int kb = c0 + lane;
-        const bool on = kb < n_kb && p[kb] != 0;
-        const uint64_t m = __ballot(on);
-        if (on) q2k_col[base + __popcll(m & below)] = kb;
-        base += __popcll(m);
+    if (int32_t(blockIdx.x) < q_blocks) {
+        const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (row >= rows) return;
+        const uint8_t* p = presence + int64_t(row) * n_kb;
+        int base = q2k_ptr[row];
+        for (int c0 = 0; c0 < n_kb; c0 += 64) {
+            const int kb = c0 + lane;
+            const bool on = kb < n_kb && p[kb] != 0;
+            const uint64_t m = __ballot(on);
+            if (on) q2k_col[base + __popcll(m & below)] = kb;
+            base += __popcll(m);
+        }
+        return;
     }
-}
-
-__global__ __launch_bounds__(256) void k_fill_k2q(const uint8_t* __restrict__ presence, int32_t cols,
-                                                   int32_t n_qb, int32_t n_kb,
-                                                   const int32_t* __restrict__ k2q_ptr,
-                                                   int32_t* __restrict__ k2q_col) {
-    const int col = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int col = (blockIdx.x - q_blocks) * 4 + (threadIdx.x >> 6);
     if (col >= cols) return;
     const int bh = col / n_kb;
     const int kb = col - bh * n_kb;
     const uint8_t* p = presence + int64_t(bh) * n_qb * n_kb + kb;
     int base = k2q_ptr[col];
-    const uint64_t below = (uint64_t(1) << lane) - 1;
     for (int q0 = 0; q0 < n_qb; q0 += 64) {
         const int qb = q0 + lane;
         const bool on = qb < n_qb && p[int64_t(qb) * n_kb] != 0;
@@ -266,22 +272,19 @@ hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n
                                   int32_t* k2q_ptr, int32_t* k2q_col, hipStream_t s) {
     const int32_t rows = BH * n_qb;
     const int32_t cols = BH * n_kb;
-    if (rows > 0 && !have_row_counts)
-        hipLaunchKernelGGL(k_row_counts, dim3((rows + 3) / 4), dim3(256), 0, s, presence, rows, n_kb,
-                           qcnt);
-    if (cols > 0) {
-        const int tiles = (n_kb + 63) / 64;
-        hipLaunchKernelGGL(k_col_counts, dim3(BH * tiles), dim3(256), 0, s, presence, n_qb, n_kb, tiles,
-                           kcnt);
-    }
+    const int32_t row_blocks = rows > 0 && !have_row_counts ? (rows + 3) / 4 : 0;
+    const int32_t tiles = (n_kb + 63) / 64;
+    const int32_t col_blocks = cols > 0 ? BH * tiles : 0;
+    if (row_blocks + col_blocks > 0)
+        hipLaunchKernelGGL(k_counts, dim3(row_blocks + col_blocks), dim3(256), 0, s, presence, rows,
+                           row_blocks, n_qb, n_kb, tiles, qcnt, kcnt);
     hipLaunchKernelGGL(k_scan2, dim3(2), dim3(kScanThreads), 0, s, qcnt, rows, q2k_ptr, kcnt, cols,
                        k2q_ptr);
-    if (rows > 0 && n_kb > 0)
-        hipLaunchKernelGGL(k_fill_q2k, dim3((rows + 3) / 4), dim3(256), 0, s, presence, rows, n_kb,
-                           q2k_ptr, q2k_col);
-    if (cols > 0 && n_qb > 0)
-        hipLaunchKernelGGL(k_fill_k2q, dim3((cols + 3) / 4), dim3(256), 0, s, presence, cols, n_qb,
-                           n_kb, k2q_ptr, k2q_col);
+    const int32_t q_blocks = rows > 0 && n_kb > 0 ? (rows + 3) / 4 : 0;
+    const int32_t k_blocks = cols > 0 && n_qb > 0 ? (cols + 3) / 4 : 0;
+    if (q_blocks + k_blocks > 0)
+        hipLaunchKernelGGL(k_fill, dim3(q_blocks + k_blocks), dim3(256), 0, s, presence, rows, cols,
+                           q_blocks, n_qb, n_kb, q2k_ptr, q2k_col, k2q_ptr, k2q_col);
     return hipGetLastError();
 }
 

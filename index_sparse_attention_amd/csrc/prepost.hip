@@ -1,10 +1,10 @@
 // Preprocess and postprocess of the attention backward.
 //
-// Preprocess: delta[b, h, i] = sum_d dO[b,i,h,d] * O[b,i,h,d] (fp32 sum of
-// exact bf16 products); for SPLIT also lse2 = lse * log2(e), the form the
-// dK/dV pass copies straight into LDS; plus zeroing of the fp32 accumulators the main loop
-// reduces into (dK/dV for LoopK, dQ for LoopQ).  The zeroing is a plain fill
-// kernel, not a memset node, so the whole call can be graph-captured.
+// Preprocess of LoopK and LoopQ: delta[b, h, i] = sum_d dO[b,i,h,d] *
+// O[b,i,h,d] (fp32 sum of exact bf16 products), plus zeroing of the fp32
+// accumulators the main loop reduces into (dK/dV for LoopK, dQ for LoopQ).
+// The zeroing is a plain fill kernel, not a memset node, so the whole call can
+// be graph-captured.  (SPLIT computes delta in its dQ pass instead.)
 //
 // Postprocess: fp32 accumulator -> bf16 output (round to nearest even), times
 // softmax_scale for dK and dQ.  MagiAttention PR #334, Core changes item 3:
@@ -32,22 +32,24 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
     constexpr int RPB = kThreads / L;  // rows per pass
     constexpr int R = kPreRows;
     if (int32_t(blockIdx.x) < nblk_delta) {
-        // rows (b, h, i) of the statistics arrays, i fastest (memory order);
-        // rows i >= Sq are padding: delta = 0, lse2 = +inf
+        // rows taken in (b, i, h) order, h fastest: the token-major memory
+        // order of O and dO, so a block reads whole token rows; they are
+        // written to the statistics array at (b, h, i)
         const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
         const int sub = threadIdx.x % L;
-        int64_t row[R], bh[R], i[R];
+        int64_t row[R], stat[R], i[R];
         u32x4_t o[R], g[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             row[r] = (int64_t(blockIdx.x) * R + r) * RPB + threadIdx.x / L;
-            i[r] = row[r] % a.stat_ld;
-            bh[r] = row[r] / a.stat_ld;
+            const int64_t h = row[r] % a.Hq;
+            const int64_t bi = row[r] / a.Hq;
+            i[r] = bi % a.stat_ld;
+            const int64_t b = bi / a.stat_ld;
+            stat[r] = (b * a.Hq + h) * a.stat_ld + i[r];
             o[r] = u32x4_t{0u, 0u, 0u, 0u};
             g[r] = u32x4_t{0u, 0u, 0u, 0u};
             if (row[r] < rows && i[r] < a.Sq) {
-                const int64_t h = bh[r] % a.Hq;
-                const int64_t b = bh[r] / a.Hq;
                 o[r] = gload128(a.o + b * a.o_sb + i[r] * a.o_ss + h * a.o_sh + 8 * sub);
                 g[r] = gload128(a.dO + b * a.do_sb + i[r] * a.do_ss + h * a.do_sh + 8 * sub);
             }
@@ -62,10 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
             }
 #pragma unroll
             for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-            if (row[r] < rows && sub == 0) {
-                a.delta[row[r]] = acc;
-                if (a.lse2 != nullptr) a.lse2[row[r]] = i[r] < a.Sq ? a.lse[bh[r] * a.Sq + i[r]] * kLog2e : __builtin_inff();
-            }
+            if (row[r] < rows && sub == 0) a.delta[stat[r]] = acc;
         }
     } else {
         const int64_t n4 = n4_0 + n4_1;

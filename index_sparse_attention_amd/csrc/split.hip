@@ -14,7 +14,10 @@
 // S^T = K Q^T and dP^T = V dO^T (A = K/V from LDS), P and dS in registers,
 // dQ += dS K with dS taken straight from the accumulators and K read back with
 // transposing LDS loads.  K/V rows are staged at LDS row swap23(r), which makes
-// each lane's accumulator registers cover 8 consecutive keys.
+// each lane's accumulator registers cover 8 consecutive keys.  This pass runs
+// first: its prologue also computes each query row's delta = rowsum(dO * O)
+// and lse * log2(e) and stores them for the dK/dV pass, so the backward needs
+// no separate preprocess launch.
 //
 // dK/dV pass (k_bwd_dkdv): workgroup = one 128-key tile, eight waves in two
 // roles (P waves with K resident and dV accumulators, dS waves with V resident
@@ -33,8 +36,6 @@
 
 namespace isattn {
 namespace {
-
-
 
 // ---------------------------------------------------------------------------
 // Work order
@@ -282,7 +283,12 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         if (a.causal) steps.count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
     }
 
-    // ---- resident operands: this wave's Q / dO rows (B operands), LSE, delta
+    // ---- resident operands: this wave's Q / dO rows (B operands), and the
+    // rows' statistics, computed here and stored for the dK/dV pass (which
+    // runs after this one): delta = rowsum(dO * O) over the lane's half of the
+    // O row at the same positions as its dO operands plus the partner lane's
+    // half, and lse2 = lse * log2(e).  Padding rows past Sq get lse2 = +inf
+    // (P = 0) and delta = 0.
     const int wrow = w * WR;
     bf16x8_t qB[C::QT][C::NCQ], doB[C::QT][C::NCV];
     float lse2[C::QT], dlt[C::QT];
@@ -292,14 +298,32 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         const bool in = qrow < a.Sq;
         const uint16_t* qr = a.q + b * a.q_sb + h * a.q_sh + int64_t(in ? qrow : 0) * a.q_ss + 8 * h2;
         const uint16_t* dr = a.dO + b * a.do_sb + h * a.do_sh + int64_t(in ? qrow : 0) * a.do_ss + 8 * h2;
+        const uint16_t* orow = a.o + b * a.o_sb + h * a.o_sh + int64_t(in ? qrow : 0) * a.o_ss + 8 * h2;
 #pragma unroll
         for (int c = 0; c < C::NCQ; ++c) qB[qt][c] = in ? gload_operand(qr + 16 * c) : bf16x8_t{};
+        u32x4_t ov[C::NCV];
 #pragma unroll
-        for (int c = 0; c < C::NCV; ++c) doB[qt][c] = in ? gload_operand(dr + 16 * c) : bf16x8_t{};
-        // padded statistics: rows past Sq read lse2 = +inf (P = 0) and delta = 0
-        const int64_t si = (int64_t(b) * a.Hq + h) * a.stat_ld + qrow;
-        lse2[qt] = a.lse2[si];
-        dlt[qt] = a.delta[si];
+        for (int c = 0; c < C::NCV; ++c) {
+            doB[qt][c] = in ? gload_operand(dr + 16 * c) : bf16x8_t{};
+            ov[c] = in ? gload128(orow + 16 * c) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        lse2[qt] = in ? a.lse[(int64_t(b) * a.Hq + h) * a.Sq + qrow] * kLog2e : __builtin_inff();
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::NCV; ++c) {
+            const u32x4_t g = __builtin_bit_cast(u32x4_t, doB[qt][c]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = fmaf(bf16_lo(ov[c][j]), bf16_lo(g[j]), acc);
+                acc = fmaf(bf16_hi(ov[c][j]), bf16_hi(g[j]), acc);
+            }
+        }
+        dlt[qt] = acc + __shfl_xor(acc, 32, 64);
+        if (h2 == 0) {
+            const int64_t si = (int64_t(b) * a.Hq + h) * a.stat_ld + qrow;
+            a.lse2[si] = lse2[qt];
+            a.delta[si] = dlt[qt];
+        }
     }
 
     f32x16_t dq[C::QT][C::NDT];
