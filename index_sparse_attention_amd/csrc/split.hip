@@ -584,9 +584,14 @@ struct DkvCfg {
     static constexpr int HO = 32 * DV * 2;
     static constexpr int NQI = Q_BYTES / 1024;              // 1 KiB loads per Q tile
     static constexpr int NI = (Q_BYTES + O_BYTES) / 1024;   // 1 KiB loads per step
-    static constexpr int KMAX = (NI + NW - 1) / NW;         // tile loads per wave per step
-    static constexpr int NDMA_P = KMAX;                     // loads a P wave issues per step
-    static constexpr int NDMA_S = KMAX + 1;                 // a dS wave also loads one statistics row
+    // Where the registers allow (Dqk <= 128) only the P waves load, so the
+    // dS waves never wait on the memory counter at a step barrier; else all
+    // eight waves share the tile loads and the dS waves load the statistics.
+    static constexpr bool P_LOADS = DQK <= 128;
+    static constexpr int NLW = P_LOADS ? NR : NW;           // waves sharing the tile loads
+    static constexpr int KMAX = (NI + NLW - 1) / NLW;       // tile loads per loading wave per step
+    static constexpr int NDMA_P = P_LOADS ? KMAX + 1 : KMAX;   // loads a P wave issues per step
+    static constexpr int NDMA_S = P_LOADS ? 0 : KMAX + 1;      // loads a dS wave issues per step
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDK = DQK / 32;
@@ -736,12 +741,12 @@ struct DkvShared {
         uint32_t soff;
     };
 
-    // 1 KiB tile load k of this wave: instruction j = w + NW * k of the step's
-    // Q tile (j < NQI) then dO tile; a j past the last re-issues j - NW, which
-    // writes the same bytes again.
+    // 1 KiB tile load k of loading wave w: instruction j = w + NLW * k of the
+    // step's Q tile (j < NQI) then dO tile; a j past the last re-issues
+    // j - NLW, which writes the same bytes again.
     static __device__ int load_index(int w, int k) {
-        const int j = w + C::NW * k;
-        return j < C::NI ? j : j - C::NW;
+        const int j = w + C::NLW * k;
+        return j < C::NI ? j : j - C::NLW;
     }
 
     __device__ DkvShared(const BwdArgs& a_, uint16_t* lds_, int w_, int lane_, int b_, int hk_, int n_base_)
@@ -794,7 +799,8 @@ struct DkvShared {
     }
 
     // Load k of this wave (k < KMAX: tile part; k == KMAX: the step's 64
-    // statistics values, dS waves only -- lse2 by even waves, delta by odd ones).
+    // statistics values, by the P waves or the dS waves -- lse2 by even
+    // waves, delta by odd ones).
     __device__ void fire(const Dma& d, int k) const {
         if (k < C::KMAX) {
             const int j = load_index(w, k);
@@ -811,6 +817,7 @@ struct DkvShared {
 // step's P buffer.
 template <int DQK, int DV>
 struct DkvPWave {
+    static constexpr bool kLoads = true;            // issues the step's tile and statistics loads
     using C = DkvCfg<DQK, DV>;
     using Dma = typename DkvShared<DQK, DV>::Dma;
     static constexpr int NF = 2 * C::NDV;           // dO^T fragments (cc, j) of one half
@@ -1004,6 +1011,7 @@ struct DkvPWave {
 // rows (dP), Q^T (dK), delta and the partner's P, all of the previous step.
 template <int DQK, int DV>
 struct DkvSWave {
+    static constexpr bool kLoads = DkvCfg<DQK, DV>::NDMA_S > 0;
     using C = DkvCfg<DQK, DV>;
     using Dma = typename DkvShared<DQK, DV>::Dma;
     const DkvShared<DQK, DV>& sh;
@@ -1080,7 +1088,8 @@ struct DkvSWave {
     // Finish the previous step's query slice as a two-half pipeline that
     // keeps the dS arithmetic under MFMAs: dP(0); dP(1) with dS(0) between
     // its MFMAs; dK(0) with dS(1) between its MFMAs; dK(1).  With FIRE this
-    // wave's loads for the next step go out between the dP(0) MFMAs.
+    // wave's loads for the next step (if it has any) go out between the dP(0)
+    // MFMAs.
     template <bool FIRE>
     __device__ void finish_pipe(const Dma& d) {
 #pragma unroll
@@ -1239,13 +1248,28 @@ struct DkvSWave {
     }
 };
 
+// The barrier between steps: a loading wave first waits for its own loads of
+// the step (direct-to-LDS, not tracked by the compiler); a wave that issues
+// no loads waits only for its LDS accesses, so global stores it has in
+// flight do not hold it up.
+template <bool LOADS>
+__device__ __forceinline__ void step_barrier() {
+    if constexpr (LOADS) {
+        wait_vmcnt<0>();
+        __syncthreads();
+    } else {
+        __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0); vmcnt and expcnt unconstrained
+        __builtin_amdgcn_s_barrier();
+    }
+}
+
 // Steps, barriers and loads, shared by both roles.  Step t's tiles sit in
 // ring stage t % NS; the P waves read stage t, the dS waves stage t - 1; P
-// goes to buffer t % 2.  The loads of step t + 1 go out from inside step t's
-// MFMA stream (their stage was last read in step t - 1, before the barrier
-// that opens step t); past the last step they re-read the last planned
-// step's rows into the free stage, which keeps the step bodies free of
-// branches.  The loop body is one straight-line block per role (masking is a
+// goes to buffer t % 2.  The loads of step t + 1 go out from inside the P
+// waves' step t MFMA stream (their stage was last read in step t - 1,
+// before the barrier that opens step t); past the last step they re-read the
+// last planned step's rows into the free stage, which keeps the step bodies
+// free of branches.  The loop body is one straight-line block per role (masking is a
 // fix-up on the packed P, outside the MFMA block) so the accumulators stay
 // put in registers.
 template <int DQK, int DV, class Role>
@@ -1264,8 +1288,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     role.fire_all(d);
     bool have1 = steps.next();                      // step t + 1
     int m1 = steps.m;
-    wait_vmcnt<0>();
-    __syncthreads();
+    step_barrier<Role::kLoads>();
     if (have1) sh.plan(d, steps, 1);
     else sh.restage(d, 1);
     role.first(m, need_mask(m), d);
@@ -1275,8 +1298,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
         m = m1;
         const bool have2 = steps.next();
         const int m2 = steps.m;
-        wait_vmcnt<0>();                            // this wave's loads of step t landed
-        __syncthreads();
+        step_barrier<Role::kLoads>();               // the loads of step t landed
         if (have2) sh.plan(d, steps, (t + 1) % C::NS);
         else sh.restage(d, (t + 1) % C::NS);
         role.advance();
@@ -1284,8 +1306,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
         have1 = have2;
         m1 = m2;
     }
-    wait_vmcnt<0>();                                // no load may land in LDS after the workgroup ends
-    __syncthreads();
+    step_barrier<Role::kLoads>();                   // no load may land in LDS after the workgroup ends
     role.advance();
     role.drain();
 }
