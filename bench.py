@@ -46,6 +46,10 @@ def main_kernels(algo, dqk, dv):
         return [("k_bwd_loopk", 1, full, full)]
     if algo == "loopq":
         return [("k_bwd_loopq", 1, full, full)]
+    if algo == "split_ds":
+        # the dK/dV pass (first) also stores dS; the dQ pass streams it back (dQ GEMM only)
+        return [("k_bwd_dkdv", 1, 2 * (2 * dqk + 2 * dv), 2 * (2 * dqk + 2 * dv)),
+                ("k_bwd_dq_ds", 2, 2 * dqk, 2 * dqk)]
     # split: the dQ pass (first) does dQ plus a recompute of S and dP; the dK/dV pass does S, dP, dV, dK
     return [("k_bwd_dq", 1, 2 * dqk, 2 * (2 * dqk + dv)),
             ("k_bwd_dkdv", 2, 2 * (2 * dqk + 2 * dv), 2 * (2 * dqk + 2 * dv))]
@@ -184,7 +188,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--algo", default="split", choices=["split", "loopk", "loopq"])
+    ap.add_argument("--algo", default="split", choices=["split", "split_ds", "loopk", "loopq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other loop order")
     args = ap.parse_args()
@@ -315,6 +319,8 @@ def main():
         kern.append({"kernel": name, "avg_launch_ms": round(ms, 4),
                      "algorithmic_tflops": round(pairs * alg_pp / (ms * 1e-3) / 1e12, 3),
                      "executed_mfma_tflops": round(pairs * exe_pp / (ms * 1e-3) / 1e12, 3)})
+        if name == "k_bwd_dq_ds":                  # streams 2 bytes of stored dS per pair
+            kern[-1]["ds_read_gbs"] = round(pairs * 2 / (ms * 1e-3) / 1e9, 1)
     dom = max(kern, key=lambda k: k["avg_launch_ms"])
     traffic = load_traffic(f"{dom['kernel']}:{w.name}")
     out = {
@@ -355,6 +361,8 @@ def main():
         post_bytes = rows_k * (w.dim_qk + w.dim_v) * (4 + 2)
     elif args.algo == "loopq":
         pre_bytes += rows_q * w.dim_qk * 4
+    elif args.algo == "split_ds":
+        pre_bytes += rows_q * 4                    # lse * log2(e)
         post_bytes = rows_q * w.dim_qk * (4 + 2)
     out["prepost_gbs"] = {"pre": round(pre_bytes / (r["stage_ms"][0] * 1e-3) / 1e9, 1),
                           "post": (round(post_bytes / (r["stage_ms"][3] * 1e-3) / 1e9, 1)
@@ -362,7 +370,7 @@ def main():
                           "peak": HBM_PEAK_GBS}
     if not args.no_compare:
         out["compare"] = []
-        for other in [a for a in ("split", "loopk", "loopq") if a != args.algo]:
+        for other in [a for a in ("split", "split_ds", "loopk", "loopq") if a != args.algo]:
             log(f"timing {other} for comparison")
             r2 = run(other, max(10, args.steps // 2), 3)
             out["compare"].append({"algo": other, "ms_per_step": round(r2["ms_per_step"], 4),

@@ -63,7 +63,8 @@ enum { ISATTN_MASK_DENSE = 0, ISATTN_MASK_BLOCK_CSR = 1 };
  * pairs transposed (per key block, its query blocks: the K2Q metadata of [P4]
  * CSR Tile Mapping).  Rows are flattened as ((b * heads + hm) * n_blocks +
  * block); columns ascend within a row; row_ptr[0] == 0.  LoopK reads only
- * q2k_*, LoopQ only k2q_*, SPLIT both; a pair not read may be NULL.  Inside a kept block
+ * q2k_*, LoopQ only k2q_*, SPLIT and SPLIT_DS both (and need the two forms
+ * to hold the same pairs); a pair not read may be NULL.  Inside a kept block
  * every pair is attended.  block_q = block_k = 128; heads is 1, heads_k or
  * heads_q. */
 typedef struct isattn_mask {
@@ -86,8 +87,14 @@ typedef struct isattn_mask {
  * a LOOPK pass for dQ, which runs first and also computes delta and
  * lse * log2(e) of every query row, then a LOOPQ pass for dK/dV --
  * recomputing P and dS in each; no atomics, no fp32 accumulators and no
- * separate preprocess (1.4x the MFMA work at Dqk = Dv). */
-enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
+ * separate preprocess (1.4x the MFMA work at Dqk = Dv).
+ * SPLIT_DS: the LOOPQ pass for dK/dV runs first (after a preprocess for
+ * delta) and also stores every dS tile it forms (bf16) in the workspace; a
+ * LOOPK pass then accumulates dQ = dS K from them, streaming 32 KiB of dS per
+ * kept block instead of recomputing S and dP.  Same results as SPLIT up to
+ * rounding order, for a workspace of B*Hq*ceil(Sq/128)*ceil(Sk/128)*32 KiB
+ * (every block slot, kept or not). */
+enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2, ISATTN_ALGO_SPLIT_DS = 3 };
 
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
  * (fp32 delta [B,Hq,Sq] plus head-major fp32 accumulators: dK,dV [B,Hk,Sk,D]
@@ -95,8 +102,9 @@ enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2 };
  * lse * log2(e), each [B,Hq,ceil(Sq/128)*128], the int32 work order of its
  * two passes, and -- when there are fewer than 512 (b, KV head, 128-key
  * block) items -- the schedule and fp32 partial dK|dV of the items cut into
- * parts; each part 256-byte aligned).  Returns 0 for a NULL shape or unknown
- * algo. */
+ * parts; for SPLIT_DS the same plus the bf16 dS tiles,
+ * [B,Hq,ceil(Sq/128),ceil(Sk/128)] x 128 x 128; each part 256-byte
+ * aligned).  Returns 0 for a NULL shape or unknown algo. */
 size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
 
 /* Attention backward ([P1] Summary and Core changes 1-3): recompute
@@ -111,12 +119,13 @@ size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo
  * mask_desc: see isattn_mask_t; NULL means dense.
  * causal: nonzero adds the bottom-right causal term j <= i + Sk - Sq.
  * dq, dk, dv: bf16 outputs with q/k/v's shapes; overwritten, not accumulated.
- * algo: ISATTN_ALGO_LOOPK, ISATTN_ALGO_LOOPQ or ISATTN_ALGO_SPLIT.
+ * algo: ISATTN_ALGO_LOOPK, ISATTN_ALGO_LOOPQ, ISATTN_ALGO_SPLIT or
+ *   ISATTN_ALGO_SPLIT_DS.
  * workspace: device buffer of at least isattn_attn_bwd_workspace_bytes bytes,
  *   256-byte aligned; its contents on entry do not matter.
  * stream: hipStream_t (NULL = default stream).
- * Supported: (dim_qk, dim_v) in {(64,64), (128,128), (192,128)}.  SPLIT
- *   addresses rows within one head with 32-bit byte offsets: it returns
+ * Supported: (dim_qk, dim_v) in {(64,64), (128,128), (192,128)}.  SPLIT and
+ *   SPLIT_DS address rows within one head with 32-bit byte offsets: they return
  *   ISATTN_ERR_STRIDE_ALIGN unless ceil(S/128)*128 * stride_s * 2 < 2^31 for
  *   q and dO (S = Sq) and for k and v (S = Sk). */
 isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape,
@@ -201,9 +210,10 @@ const char* isattn_version(void);
 /* ---- Stage timing (measurement support) -----------------------------------
  * A timer records HIP events on the call's stream around the launches of
  * isattn_attn_bwd_timed: stage [0] preprocess (for SPLIT only its work-order
- * kernel), [1] first main kernel (LOOPK / LOOPQ main loop, or the SPLIT dQ
- * pass), [2] second main kernel (the SPLIT dK/dV pass; empty otherwise),
- * [3] postprocess (empty for SPLIT).
+ * kernel), [1] first main kernel (LOOPK / LOOPQ main loop, the SPLIT dQ pass
+ * or the SPLIT_DS dK/dV pass), [2] second main kernel (the SPLIT dK/dV pass
+ * or the SPLIT_DS dQ pass; empty otherwise), [3] postprocess (empty for
+ * SPLIT and SPLIT_DS).
  * isattn_timer_read synchronises on the recorded events and returns the number
  * of timed calls and the summed milliseconds per stage (stage_ms[4]).  A timer
  * holds `capacity` calls; further calls wrap and overwrite. */

@@ -13,7 +13,7 @@ STATUS = {
     7: "ISATTN_ERR_CAPACITY", 8: "ISATTN_ERR_HIP",
 }
 MASK_DENSE, MASK_BLOCK_CSR = 0, 1
-ALGO_LOOPK, ALGO_LOOPQ, ALGO_SPLIT = 0, 1, 2
+ALGO_LOOPK, ALGO_LOOPQ, ALGO_SPLIT, ALGO_SPLIT_DS = 0, 1, 2, 3
 
 
 class Shape(ctypes.Structure):

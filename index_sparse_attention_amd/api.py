@@ -14,7 +14,8 @@ import torch
 
 from . import _abi
 
-ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ, "split": _abi.ALGO_SPLIT}
+ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ, "split": _abi.ALGO_SPLIT,
+         "split_ds": _abi.ALGO_SPLIT_DS}
 
 
 def _stream_ptr(stream) -> int:

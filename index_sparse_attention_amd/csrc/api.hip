@@ -43,8 +43,10 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if (st != ISATTN_OK) return st;
     if (a.B == 0) return ISATTN_OK;
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
-    a.lse2 = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
-    a.order = algo == ISATTN_ALGO_SPLIT ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_order)) : nullptr;
+    const bool split = algo == ISATTN_ALGO_SPLIT || algo == ISATTN_ALGO_SPLIT_DS;
+    a.lse2 = split ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
+    a.order = split ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_order)) : nullptr;
+    a.ds = algo == ISATTN_ALGO_SPLIT_DS ? reinterpret_cast<uint16_t*>(ws_at(workspace, plan.off_ds)) : nullptr;
     a.kv_parts_T = plan.kv_parts_T;
     a.kv_units_bound = plan.kv_units_bound;
     a.units = plan.kv_parts_T > 0 ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_units)) : nullptr;
@@ -60,15 +62,18 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     // SPLIT needs no preprocess launch: its dQ pass, which runs first,
     // computes delta and lse2 for the dK/dV pass
     if (algo != ISATTN_ALGO_SPLIT && launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
-    if (algo == ISATTN_ALGO_SPLIT && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (split && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
     hipError_t e;
     if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);
     else if (algo == ISATTN_ALGO_LOOPQ) e = launch_loopq(a, s);
-    else e = launch_split_dq(a, s);
+    else if (algo == ISATTN_ALGO_SPLIT) e = launch_split_dq(a, s);
+    else e = launch_split_dkdv(a, s);                // SPLIT_DS: dK/dV pass first, storing dS
     if (e != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 2, s)) != ISATTN_OK) return st;
-    if (algo == ISATTN_ALGO_SPLIT && launch_split_dkdv(a, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (algo == ISATTN_ALGO_SPLIT) e = launch_split_dkdv(a, s);
+    else if (algo == ISATTN_ALGO_SPLIT_DS) e = launch_split_ds_dq(a, s);
+    if (e != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 3, s)) != ISATTN_OK) return st;
     if (launch_postprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 4, s)) != ISATTN_OK) return st;

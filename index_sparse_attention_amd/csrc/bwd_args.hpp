@@ -35,6 +35,7 @@ struct BwdArgs {
     int32_t* units;
     int32_t* item_info;
     float* partial;
+    uint16_t* ds;         // SPLIT_DS: bf16 dS tiles [B, Hq, n_qb, n_kb][128 x 128]; else null
     float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
     float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;

@@ -259,6 +259,14 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base))
                  : "memory");
 }
+// The same with the non-temporal hint, for data read exactly once (keeps it
+// from displacing reused tiles in L2).
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base))
+                 : "memory");
+}
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  :

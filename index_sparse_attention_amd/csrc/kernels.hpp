@@ -21,6 +21,8 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
+// SPLIT_DS second pass: dQ from the dS tiles the dK/dV pass stored.
+hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
 hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,

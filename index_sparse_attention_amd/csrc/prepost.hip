@@ -1,10 +1,13 @@
 // Preprocess and postprocess of the attention backward.
 //
-// Preprocess of LoopK and LoopQ: delta[b, h, i] = sum_d dO[b,i,h,d] *
-// O[b,i,h,d] (fp32 sum of exact bf16 products), plus zeroing of the fp32
-// accumulators the main loop reduces into (dK/dV for LoopK, dQ for LoopQ).
-// The zeroing is a plain fill kernel, not a memset node, so the whole call can
-// be graph-captured.  (SPLIT computes delta in its dQ pass instead.)
+// Preprocess of LoopK, LoopQ and SPLIT_DS: delta[b, h, i] = sum_d
+// dO[b,i,h,d] * O[b,i,h,d] (fp32 sum of exact bf16 products); for SPLIT_DS
+// also lse2 = lse * log2(e), the form its dK/dV pass copies straight into
+// LDS, both padded to whole 128-row blocks (delta = 0, lse2 = +inf); plus
+// zeroing of the fp32 accumulators the main loop reduces into (dK/dV for
+// LoopK, dQ for LoopQ).  The zeroing is a plain fill kernel, not a memset
+// node, so the whole call can be graph-captured.  (SPLIT computes delta in
+// its dQ pass instead.)
 //
 // Postprocess: fp32 accumulator -> bf16 output (round to nearest even), times
 // softmax_scale for dK and dQ.  MagiAttention PR #334, Core changes item 3:
@@ -64,7 +67,13 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
             }
 #pragma unroll
             for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-            if (row[r] < rows && sub == 0) a.delta[stat[r]] = acc;
+            if (row[r] < rows && sub == 0) {
+                a.delta[stat[r]] = acc;
+                if (a.lse2 != nullptr) {
+                    const int64_t bh = stat[r] / a.stat_ld;
+                    a.lse2[stat[r]] = i[r] < a.Sq ? a.lse[bh * a.Sq + i[r]] * kLog2e : __builtin_inff();
+                }
+            }
         }
     } else {
         const int64_t n4 = n4_0 + n4_1;
@@ -151,7 +160,7 @@ hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s) {
 }
 
 hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s) {
-    if (algo == 2) return hipSuccess;           // SPLIT stores bf16 outputs directly
+    if (algo == 2 || algo == 3) return hipSuccess;   // SPLIT and SPLIT_DS store bf16 outputs directly
     if (algo == 0) {
         hipError_t e = post_dispatch(a.Dqk, a.acc0, a.dk, a.dk_sb, a.dk_ss, a.dk_sh, a.B, a.Sk, a.Hk,
                                      a.scale, s);

@@ -631,6 +631,12 @@ struct DkvSteps {
         : a(a_), b(b_), hk(hk_), kb(kb_), n_base(kb_ * kBlock), shift(a_.Sk - a_.Sq), lane(lane_) {}
 
     __device__ int hq() const { return hk * a.G + gi; }
+    // element offset of the current step's part of its dS tile (SPLIT_DS):
+    // tile (b, h, qb, kb) of 128 x 128 bf16, the step's 64 rows its half p
+    __device__ int64_t ds_off() const {
+        return (((int64_t(b) * a.Hq + hq()) * a.n_qb + m / kBlock) * a.n_kb + kb) * (kBlock * kBlock) +
+               (m % kBlock) * kBlock;
+    }
 
     __device__ void load_head() {
         const int h = hq();
@@ -971,8 +977,8 @@ struct DkvPWave {
         }
     }
 
-    __device__ void first(int m, bool mask, const Dma& d) { body<false>(m, mask, d); }
-    __device__ void step(int m, bool mask, const Dma& d) { body<true>(m, mask, d); }
+    __device__ void first(int m, bool mask, const Dma& d, int64_t) { body<false>(m, mask, d); }
+    __device__ void step(int m, bool mask, const Dma& d, int64_t) { body<true>(m, mask, d); }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
         for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
@@ -1009,7 +1015,7 @@ struct DkvPWave {
 
 // dS wave: dP, dS, dK for 32 keys, one step behind the P waves.  Reads: dO
 // rows (dP), Q^T (dK), delta and the partner's P, all of the previous step.
-template <int DQK, int DV>
+template <int DQK, int DV, bool DS>
 struct DkvSWave {
     static constexpr bool kLoads = DkvCfg<DQK, DV>::NDMA_S > 0;
     using C = DkvCfg<DQK, DV>;
@@ -1027,6 +1033,20 @@ struct DkvSWave {
     const lds_char* x_at;
     RingPos<C::NS> ss{C::NS - 1};
     int par = 1;
+    int64_t ds_prev = 0;                            // dS tile part of the step being finished (DS)
+
+    // DS: store the packed dS of half hh (this lane: key 32 wr + l32, query
+    // rows 32 hh + 16 cc + 8 h2 + 0..7 of the step) as two 1 KiB chunks, each
+    // written whole by one instruction: chunk (wr, hh, cc) of the step's
+    // half tile, lane L at 16 L.  Non-temporal: nothing here reads it again.
+    __device__ void store_ds(int hh, const u32x4_t (&sa)[2]) const {
+        if constexpr (DS) {
+            uint16_t* dst = a.ds + ds_prev + ((wr * 2 + hh) * 2) * 512 + 8 * sh.lane;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                __builtin_nontemporal_store(sa[cc], reinterpret_cast<u32x4_t*>(dst + 512 * cc));
+        }
+    }
 
     __device__ DkvSWave(const DkvShared<DQK, DV>& sh_, int wr_) : sh(sh_), a(sh_.a), wr(wr_) {
         const int key = sh.n_base + 32 * wr + sh.l32;
@@ -1136,6 +1156,7 @@ struct DkvSWave {
             for (int q = c * 8 / C::NCV; q < (c + 1) * 8 / C::NCV; ++q) ds_q(0, q);
             __builtin_amdgcn_sched_barrier(0);     // one MFMA and its share of the arithmetic together
         }
+        store_ds(0, sa[0]);
         // dK(0) with dS(1) between its MFMAs
         bf16x8_t qf[PFQ + 1];
 #pragma unroll
@@ -1149,6 +1170,7 @@ struct DkvSWave {
             for (int q = f * 8 / NQF; q < (f + 1) * 8 / NQF; ++q) ds_q(1, q);
             __builtin_amdgcn_sched_barrier(0);     // one MFMA and its share of the arithmetic together
         }
+        store_ds(1, sa[1]);
         // dK(1)
 #pragma unroll
         for (int f = 0; f < NQF; ++f) {
@@ -1192,6 +1214,7 @@ struct DkvSWave {
             u32x4_t sa[2];
 #pragma unroll
             for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, d4, pw[q >> 2][q & 3], q >> 2, q & 3);
+            store_ds(hh, sa);
 #pragma unroll
             for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
         }
@@ -1207,15 +1230,17 @@ struct DkvSWave {
         else finish_halves<FIRE>(d);
     }
 
-    __device__ void first(int m, bool mask, const Dma& d) {
+    __device__ void first(int m, bool mask, const Dma& d, int64_t dso) {
         (void)m;
         (void)mask;
+        ds_prev = dso;
         fire_all(d);
     }
-    __device__ void step(int m, bool mask, const Dma& d) {
+    __device__ void step(int m, bool mask, const Dma& d, int64_t dso) {
         (void)m;
         (void)mask;
         finish<true>(d);
+        ds_prev = dso;
     }
     __device__ void drain() {
         Dma d{};
@@ -1284,34 +1309,39 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     if (!steps.start()) return;
     typename DkvShared<DQK, DV>::Dma d;
     int m = steps.m;                                // step t
+    int64_t dso = steps.ds_off();
     sh.plan(d, steps, 0);
     role.fire_all(d);
     bool have1 = steps.next();                      // step t + 1
     int m1 = steps.m;
+    int64_t dso1 = steps.ds_off();
     step_barrier<Role::kLoads>();
     if (have1) sh.plan(d, steps, 1);
     else sh.restage(d, 1);
-    role.first(m, need_mask(m), d);
+    role.first(m, need_mask(m), d, dso);
     int t = 0;
     while (have1) {
         ++t;
         m = m1;
+        dso = dso1;
         const bool have2 = steps.next();
         const int m2 = steps.m;
+        const int64_t dso2 = steps.ds_off();
         step_barrier<Role::kLoads>();               // the loads of step t landed
         if (have2) sh.plan(d, steps, (t + 1) % C::NS);
         else sh.restage(d, (t + 1) % C::NS);
         role.advance();
-        role.step(m, need_mask(m), d);
+        role.step(m, need_mask(m), d, dso);
         have1 = have2;
         m1 = m2;
+        dso1 = dso2;
     }
     step_barrier<Role::kLoads>();                   // no load may land in LDS after the workgroup ends
     role.advance();
     role.drain();
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool DS>
 __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     using C = DkvCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -1350,7 +1380,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
         dkdv_run<DQK, DV>(sh, steps, role);
         role.store(partial);
     } else {
-        DkvSWave<DQK, DV> role(sh, w - C::NR);
+        DkvSWave<DQK, DV, DS> role(sh, w - C::NR);
         dkdv_run<DQK, DV>(sh, steps, role);
         role.store(partial);
     }
@@ -1402,24 +1432,24 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
     }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool DS>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<DQK, DV>;
     const int64_t items = int64_t(a.n_kb) * a.B * a.Hk;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV, DS>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     if (a.kv_parts_T > 0) {                        // part mode: one workgroup per unit, then the reduction
-        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
+        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_dkdv_reduce<DQK, DV>), dim3(unsigned(items * (kBlock / 8))), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -1432,9 +1462,12 @@ hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s) {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_dkdv_t<64, 64>(a, s);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_dkdv_t<128, 128>(a, s);
-    if (a.Dqk == 192 && a.Dv == 128) return launch_dkdv_t<192, 128>(a, s);
+    const bool ds = a.ds != nullptr;               // SPLIT_DS: also store dS
+    if (a.Dqk == 64 && a.Dv == 64) return ds ? launch_dkdv_t<64, 64, true>(a, s) : launch_dkdv_t<64, 64, false>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128)
+        return ds ? launch_dkdv_t<128, 128, true>(a, s) : launch_dkdv_t<128, 128, false>(a, s);
+    if (a.Dqk == 192 && a.Dv == 128)
+        return ds ? launch_dkdv_t<192, 128, true>(a, s) : launch_dkdv_t<192, 128, false>(a, s);
     return hipErrorInvalidValue;
 }
 

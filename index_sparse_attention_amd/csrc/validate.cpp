@@ -47,24 +47,27 @@ void copy_view_out(const isattn_tensor_t* t, uint16_t** p, int64_t* sb, int64_t*
 bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
         return false;
-    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT) return false;
+    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT &&
+        algo != ISATTN_ALGO_SPLIT_DS)
+        return false;
+    const bool split = algo == ISATTN_ALGO_SPLIT || algo == ISATTN_ALGO_SPLIT_DS;
     BwdPlan p{};
     p.n_qb = cdiv(s.seqlen_q, kBlock);
     p.n_kb = cdiv(s.seqlen_k, kBlock);
     p.G = s.heads_k > 0 ? s.heads_q / s.heads_k : 0;
     const int64_t rows_q = int64_t(s.batch) * s.seqlen_q * s.heads_q;
     const int64_t rows_k = int64_t(s.batch) * s.seqlen_k * s.heads_k;
-    // SPLIT pads the per-row statistics of each (b, h) to whole 128-row blocks
-    p.stat_ld = algo == ISATTN_ALGO_SPLIT ? p.n_qb * kBlock : s.seqlen_q;
+    // SPLIT and SPLIT_DS pad the per-row statistics of each (b, h) to whole 128-row blocks
+    p.stat_ld = split ? p.n_qb * kBlock : s.seqlen_q;
     const int64_t stat_rows = int64_t(s.batch) * s.heads_q * p.stat_ld;
     size_t off = 0;
     p.off_delta = off;
     off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
     p.off_lse2 = off;
-    if (algo == ISATTN_ALGO_SPLIT) off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
+    if (split) off = align_up(off + size_t(stat_rows) * sizeof(float), kWsAlign);
     // SPLIT: work order of the two passes (dK/dV items, then dQ items)
     p.off_order = off;
-    if (algo == ISATTN_ALGO_SPLIT) {
+    if (split) {
         const int64_t items = int64_t(s.batch) * (int64_t(s.heads_k) * p.n_kb + int64_t(s.heads_q) * p.n_qb);
         off = align_up(off + size_t(items) * sizeof(int32_t), kWsAlign);
     }
@@ -74,7 +77,7 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     p.kv_units_bound = 0;
     p.off_units = p.off_info = p.off_partial = off;
     const int64_t n_kv = int64_t(s.batch) * s.heads_k * p.n_kb;
-    if (algo == ISATTN_ALGO_SPLIT && n_kv > 0 && n_kv < kPartModeItems) {
+    if (split && n_kv > 0 && n_kv < kPartModeItems) {
         const int64_t per_item = int64_t(p.G) * p.n_qb;      // query blocks of an item, dense
         const int64_t T = std::max<int64_t>(1, (per_item * n_kv + 4 * kPartModeItems / 2 - 1) / (4 * kPartModeItems / 2));
         const int64_t pmax = std::min<int64_t>(kMaxParts, std::max<int64_t>(1, (per_item + T - 1) / T));
@@ -101,6 +104,10 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     off = align_up(off + size_t(p.acc0_elems) * sizeof(float), kWsAlign);
     p.off_acc1 = off;
     off = align_up(off + size_t(p.acc1_elems) * sizeof(float), kWsAlign);
+    // SPLIT_DS: a bf16 dS tile for every (b, h, query block, key block)
+    p.off_ds = off;
+    if (algo == ISATTN_ALGO_SPLIT_DS)
+        off = align_up(off + size_t(s.batch) * s.heads_q * p.n_qb * p.n_kb * kBlock * kBlock * 2, kWsAlign);
     p.total = off;
     *plan = p;
     return true;
@@ -125,7 +132,8 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         int64_t(s.batch) * s.heads_k * cdiv(s.seqlen_k, kBlock) >= (int64_t(1) << 31) - 8)
         return ISATTN_ERR_SHAPE;
     if (!supported_dims(s.dim_qk, s.dim_v)) return ISATTN_ERR_UNSUPPORTED;
-    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT)
+    if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT &&
+        algo != ISATTN_ALGO_SPLIT_DS)
         return ISATTN_ERR_UNSUPPORTED;
     if (!std::isfinite(softmax_scale)) return ISATTN_ERR_UNSUPPORTED;
 
@@ -141,7 +149,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     if ((st = check_view(dk, nk)) != ISATTN_OK) return st;
     if ((st = check_view(dv, nk)) != ISATTN_OK) return st;
     if (nq > 0 && lse == nullptr) return ISATTN_ERR_NULL;
-    if (algo == ISATTN_ALGO_SPLIT && nq > 0) {
+    if ((algo == ISATTN_ALGO_SPLIT || algo == ISATTN_ALGO_SPLIT_DS) && nq > 0) {
         // 32-bit byte offsets within one head: Q/dO rows (dK/dV pass), K/V rows (dQ pass)
         const int64_t lim = int64_t(1) << 31;
         const int64_t rq = int64_t(cdiv(s.seqlen_q, kBlock)) * kBlock;

@@ -21,7 +21,7 @@ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 struct BwdPlan {
     int32_t n_qb, n_kb, G, Hm, stat_ld;
-    size_t off_delta, off_lse2, off_order, off_units, off_info, off_partial, off_acc0, off_acc1, total;
+    size_t off_delta, off_lse2, off_order, off_units, off_info, off_partial, off_acc0, off_acc1, off_ds, total;
     int32_t kv_parts_T, kv_units_bound;
     int64_t acc0_elems, acc1_elems;
 };

@@ -67,6 +67,9 @@ def test_workspace_sizes(lib):
     # 512 or more dK/dV items: no part mode
     big = shape(B=1, Sq=128, Sk=128 * 256, Hq=2, Hk=2)
     assert ws_bytes(lib, big, 2) == 2 * al(2 * 128 * 4) + al((2 * 256 + 2 * 1) * 4)
+    # SPLIT_DS: SPLIT's parts plus a 128 x 128 bf16 dS tile per (b, h, query block, key block)
+    assert ws_bytes(lib, s, 3) == ws_bytes(lib, s, 2) + al(2 * 4 * 3 * 2 * 128 * 128 * 2)
+    assert ws_bytes(lib, big, 3) == ws_bytes(lib, big, 2) + al(1 * 2 * 1 * 256 * 128 * 128 * 2)
     assert ws_bytes(lib, s, 7) == 0
     assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
     # converter: presence B*H*nQB*nKB bytes + row and column counts
@@ -94,7 +97,7 @@ class Call:
         self.scale = 0.125
         self.algo = algo
         self.ws = FAKE
-        self.ws_bytes = ws_bytes(lib, self.shape, algo) if algo in (0, 1, 2) else 0
+        self.ws_bytes = ws_bytes(lib, self.shape, algo) if algo in (0, 1, 2, 3) else 0
 
     def __call__(self, shape_ptr=True):
         v = self.views
@@ -140,6 +143,10 @@ def test_bwd_validation_errors(lib):
     c = Call(lib, algo=2); c.views["v"].stride_s = 1 << 22; c.views["v"].stride_b = 256 << 22
     assert c() == STRIDE
     c = Call(lib, algo=2); c.ws_bytes -= 1; assert c() == WS
+    c = Call(lib, algo=3); c.views["k"].stride_s = 1 << 22; c.views["k"].stride_b = 256 << 22
+    assert c() == STRIDE
+    c = Call(lib, algo=3); c.ws_bytes -= 1; assert c() == WS
+    c = Call(lib, algo=3); c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, None, None); assert c() == NULL
 
 
 def test_fwd_validation_errors(lib):

@@ -44,7 +44,7 @@ def get_case(name):
     return _built[name]
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split", "split_ds"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_attn_bwd_parity(name, algo):
     c = get_case(name)
@@ -61,19 +61,19 @@ def test_attn_bwd_parity(name, algo):
 
 @pytest.mark.parametrize("name", ["causal_gqa_br_d128", "block_h1_gqa_causal", "index_gqa_d128", "causal_d192"])
 def test_loop_orders_agree(name):
-    """LoopK, LoopQ and the split passes agree within the tolerance (fp32
+    """LoopK, LoopQ and both split variants agree within the tolerance (fp32
     accumulation order differs between them)."""
     c = get_case(name)
     log(f"loopk vs loopq vs split {name}")
     mask = gpu_mask(c)
     a = run_gpu(c, "loopk", mask)
-    for other in ("loopq", "split"):
+    for other in ("loopq", "split", "split_ds"):
         b = run_gpu(c, other, mask)
         for n, x, y in zip(("dq", "dk", "dv"), a, b):
             assert_close(f"{n} loopk-vs-{other}", x, y)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split", "split_ds"])
 def test_dense_equals_all_kept_blocks(algo):
     """Dense mask and an all-kept block mask give the same gradients."""
     import torch
@@ -87,7 +87,7 @@ def test_dense_equals_all_kept_blocks(algo):
         assert_close(n + " dense-vs-allkept", x, y)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split", "split_ds"])
 def test_poisoned_workspace(algo):
     """A workspace full of NaN bytes on entry does not leak into the results."""
     c = get_case("causal_gqa_br_d128")
@@ -99,7 +99,20 @@ def test_poisoned_workspace(algo):
     assert_close("dv", dv, rv)
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
+@pytest.mark.parametrize("name", ["block_h1_gqa_causal", "index_gqa_d128", "block_d192"])
+def test_split_ds_poisoned_workspace_sparse(name):
+    """SPLIT_DS reads back only the dS tiles its dK/dV pass wrote: with a
+    NaN-filled workspace the tiles of dropped blocks must never be read."""
+    c = get_case(name)
+    log(f"poisoned workspace split_ds {name}")
+    dq, dk, dv = run_gpu(c, "split_ds", gpu_mask(c), workspace_fill=0xFF)
+    rq, rk, rv = oracle_grads(c)
+    assert_close("dq", dq, rq)
+    assert_close("dk", dk, rk)
+    assert_close("dv", dv, rv)
+
+
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split", "split_ds"])
 def test_empty_sequences(algo):
     """Sq = 0 gives zero dK/dV; Sk = 0 gives zero dQ; B = 0 is a no-op."""
     import torch
