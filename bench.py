@@ -1,12 +1,13 @@
 """Benchmark: attention-backward TFLOP/s on kept blocks, 8K block-sparse (keep 0.25).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--algo split|loopk|loopq] [--no-cpu-baseline] [--no-compare]
+                    [--algo split_ds|split|loopk|loopq] [--no-cpu-baseline] [--no-compare]
 
 One step = one pass of the whole hot path over one batch of synthetic input:
 block presence -> Q->K / K->Q CSR on the GPU, then the backward call (delta
 preprocess, the main kernel(s), and for LoopK/LoopQ the fp32 -> bf16
-postprocess).  Inputs are resident in HBM before the timed region.  FLOP are
+postprocess).  The default algorithm is SPLIT_DS (dK/dV pass storing dS,
+then dQ = dS K).  Inputs are resident in HBM before the timed region.  FLOP are
 counted over computed blocks only: 2 * (3*Dqk + 2*Dv) per (query, key) pair of
 every kept block, whatever the algorithm executes.
 
@@ -188,7 +189,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--algo", default="split", choices=["split", "split_ds", "loopk", "loopq"])
+    ap.add_argument("--algo", default="split_ds", choices=["split", "split_ds", "loopk", "loopq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other loop order")
     args = ap.parse_args()

@@ -97,19 +97,23 @@ class Timer:
 
 
 def attn_bwd_workspace_bytes(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v,
-                             algo="loopk") -> int:
+                             algo="split") -> int:
     shape = _abi.Shape(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v)
     return int(_abi.load().isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), ALGOS[algo]))
 
 
 def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = False,
-             softmax_scale: float | None = None, algo: str = "loopk", dq=None, dk=None, dv=None,
+             softmax_scale: float | None = None, algo: str = "split", dq=None, dk=None, dv=None,
              workspace: torch.Tensor | None = None, stream=None, timer: Timer | None = None):
     """Attention backward on the GPU.  Returns (dq, dk, dv) as bf16 tensors.
 
     q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv], o/do [B,Sq,Hq,Dv] bf16;
     lse fp32 [B,Hq,Sq] (natural log).  ``mask`` None = dense.  ``causal``
     adds the bottom-right causal term.  Outputs are allocated when not given.
+    ``algo``: "split" (default: two atomic-free passes, small workspace),
+    "split_ds" (the dK/dV pass stores dS for the dQ pass: faster, workspace of
+    B*Hq*ceil(Sq/128)*ceil(Sk/128)*32 KiB), "loopk" or "loopq" (the pages'
+    loop orders with fp32 atomics).
     """
     lib = _abi.load()
     B, Sq, Hq, Dqk = q.shape
