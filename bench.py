@@ -323,7 +323,7 @@ def main():
         if name == "k_bwd_dq_ds":                  # streams 2 bytes of stored dS per pair
             kern[-1]["ds_read_gbs"] = round(pairs * 2 / (ms * 1e-3) / 1e9, 1)
     dom = max(kern, key=lambda k: k["avg_launch_ms"])
-    traffic = load_traffic(f"{dom['kernel']}:{w.name}")
+    traffic = load_traffic(f"{dom['kernel']}:{args.algo}:{w.name}")
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -362,9 +362,9 @@ def main():
         post_bytes = rows_k * (w.dim_qk + w.dim_v) * (4 + 2)
     elif args.algo == "loopq":
         pre_bytes += rows_q * w.dim_qk * 4
+        post_bytes = rows_q * w.dim_qk * (4 + 2)
     elif args.algo == "split_ds":
         pre_bytes += rows_q * 4                    # lse * log2(e)
-        post_bytes = rows_q * w.dim_qk * (4 + 2)
     out["prepost_gbs"] = {"pre": round(pre_bytes / (r["stage_ms"][0] * 1e-3) / 1e9, 1),
                           "post": (round(post_bytes / (r["stage_ms"][3] * 1e-3) / 1e9, 1)
                                    if post_bytes else None),
