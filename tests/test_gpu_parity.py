@@ -132,3 +132,21 @@ def test_empty_sequences(algo):
         assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
     q = torch.randn(0, 16, 2, 64, **bf)
     isa.attn_bwd(q, q, q, q, q, torch.zeros(0, 2, 16, device="cuda"), algo=algo)
+
+
+@pytest.mark.parametrize("algo", ["split", "split_ds"])
+@pytest.mark.parametrize("name", ["block_h1_gqa_causal", "index_gqa_d128", "many_items_block_gqa", "causal_d192"])
+def test_split_is_bit_reproducible(name, algo):
+    """The atomic-free algorithms are deterministic: every reduction (dQ over
+    key blocks, dK/dV over query blocks and heads, part-mode partials) runs in
+    a fixed order, so repeated calls -- also with a NaN-filled workspace --
+    give bit-identical dQ, dK and dV.  (LoopK/LoopQ reduce with fp32 atomics
+    and are only reproducible up to rounding.)"""
+    c = get_case(name)
+    log(f"bit reproducibility {algo} {name}")
+    mask = gpu_mask(c)
+    first = run_gpu(c, algo, mask)
+    for fill in (None, 0xFF, None):
+        again = run_gpu(c, algo, mask, workspace_fill=fill)
+        for n, x, y in zip(("dq", "dk", "dv"), first, again):
+            assert np.array_equal(x, y), f"{algo} {name}: {n} differs between calls"
