@@ -186,6 +186,63 @@ isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t bat
                                              int64_t col_capacity, void* workspace,
                                              size_t workspace_bytes, void* stream);
 
+/* ---- Packed variable-length sequences ----------------------------------
+ * (the packed sequences of [P2]'s variable-length backward and of [P3]
+ * Background; [P1] Limitations leaves LoopK fixed-length only.)
+ * Sequence b of a batch of `batch` sequences is tokens [cu_seqlens_q[b],
+ * cu_seqlens_q[b+1]) of the query-side tensors (q, o, dO, dq) and
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of the key side (k, v, dk, dv); both
+ * arrays are int32 device [batch + 1], nondecreasing, starting at 0.  Tensor
+ * views address token t as ptr + t * stride_s + h * stride_h (stride_b is
+ * unused).  shape->seqlen_q / seqlen_k are the longest lengths: every
+ * sequence must fit them (a longer one is cut to them).  Attention, causal
+ * alignment (bottom-right, per sequence) and 128-row / 128-key blocks are
+ * those of each sequence on its own; mask rows and presence use the longest
+ * block counts, blocks past a sequence's end are ignored.  lse is fp32
+ * [batch, heads_q, seqlen_q] (entries past a sequence's length unused). */
+typedef struct isattn_varlen {
+    const int32_t* cu_seqlens_q;
+    const int32_t* cu_seqlens_k;
+} isattn_varlen_t;
+
+/* isattn_attn_bwd over packed sequences.  algo: ISATTN_ALGO_SPLIT or
+ * ISATTN_ALGO_SPLIT_DS (others: ISATTN_ERR_UNSUPPORTED); workspace as
+ * isattn_attn_bwd_workspace_bytes(shape, algo) with the longest lengths.
+ * NULL cu_seqlens with batch > 0: ISATTN_ERR_NULL. */
+isattn_status_t isattn_attn_bwd_varlen(const isattn_shape_t* shape, const isattn_varlen_t* varlen,
+                                       const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                       const isattn_tensor_t* v, const isattn_tensor_t* o,
+                                       const isattn_tensor_t* dO, const float* lse,
+                                       const isattn_mask_t* mask_desc, int32_t causal,
+                                       float softmax_scale, const isattn_tensor_t* dq,
+                                       const isattn_tensor_t* dk, const isattn_tensor_t* dv,
+                                       int32_t algo, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* isattn_attn_fwd over packed sequences (same conventions). */
+isattn_status_t isattn_attn_fwd_varlen(const isattn_shape_t* shape, const isattn_varlen_t* varlen,
+                                       const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                       const isattn_tensor_t* v, const isattn_mask_t* mask_desc,
+                                       int32_t causal, float softmax_scale,
+                                       const isattn_tensor_t* o, float* lse, void* stream);
+
+/* isattn_index_to_block_sparse over packed sequences: indices int32 device
+ * [cu_seqlens_q[batch], nhk, topk]; row r of sequence b (cu_seqlens_q[b] <=
+ * r < cu_seqlens_q[b+1]) is its query r - cu_seqlens_q[b] and its values are
+ * key positions in that sequence (outside [0, its key length): padding).
+ * Block counts, outputs, capacity and workspace are those of
+ * isattn_index_to_block_sparse with seqlen_q = max_seqlen_q and seqlen_k =
+ * max_seqlen_k. */
+isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int32_t batch,
+                                                    const int32_t* cu_seqlens_q,
+                                                    const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                                                    int32_t max_seqlen_k, int32_t nhk, int32_t topk,
+                                                    int32_t block_q, int32_t block_k,
+                                                    int32_t* q2k_row_ptr, int32_t* q2k_col,
+                                                    int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                                    int64_t col_capacity, void* workspace,
+                                                    size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace isattn_block_mask_to_csr needs. */
 size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,
                                                 int32_t n_kb);

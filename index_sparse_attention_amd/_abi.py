@@ -31,6 +31,10 @@ class Mask(ctypes.Structure):
                 ("k2q_row_ptr", c_void_p), ("k2q_col", c_void_p)]
 
 
+class Varlen(ctypes.Structure):
+    _fields_ = [("cu_seqlens_q", c_void_p), ("cu_seqlens_k", c_void_p)]
+
+
 _T = POINTER(Tensor)
 _BWD_ARGS = [POINTER(Shape), _T, _T, _T, _T, _T, c_void_p, POINTER(Mask), c_int32, c_float,
              _T, _T, _T, c_int32, c_void_p, c_size_t, c_void_p]
@@ -42,6 +46,13 @@ SIGNATURES = {
     "isattn_attn_bwd_timed": (c_int32, _BWD_ARGS + [c_void_p]),
     "isattn_attn_fwd": (c_int32, [POINTER(Shape), _T, _T, _T, POINTER(Mask), c_int32, c_float, _T, c_void_p,
                                   c_void_p]),
+    "isattn_attn_bwd_varlen": (c_int32, [POINTER(Shape), POINTER(Varlen)] + _BWD_ARGS[1:]),
+    "isattn_attn_fwd_varlen": (c_int32, [POINTER(Shape), POINTER(Varlen), _T, _T, _T, POINTER(Mask), c_int32,
+                                         c_float, _T, c_void_p, c_void_p]),
+    "isattn_index_to_block_sparse_varlen": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                                      c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                                      c_void_p, c_void_p, c_int64, c_void_p, c_size_t,
+                                                      c_void_p]),
     "isattn_index_to_block_sparse_workspace_bytes": (c_size_t, [c_int32] * 6),
     "isattn_index_to_block_sparse": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,

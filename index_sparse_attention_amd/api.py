@@ -24,6 +24,8 @@ def _stream_ptr(stream) -> int:
 
 
 def _view(t: torch.Tensor, name: str) -> _abi.Tensor:
+    if t.dim() == 3:                               # packed sequences: [total, heads, dim]
+        t = t.unsqueeze(0)
     if t.dim() != 4:
         raise ValueError(f"{name}: expected [batch, seq, heads, dim], got shape {tuple(t.shape)}")
     if t.dtype != torch.bfloat16:
@@ -33,6 +35,24 @@ def _view(t: torch.Tensor, name: str) -> _abi.Tensor:
     if t.stride(3) != 1:
         raise ValueError(f"{name}: last dimension must be contiguous")
     return _abi.Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _varlen(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
+    """Packed-sequence arguments: (batch, max_q, max_k, Varlen) or None."""
+    if cu_seqlens_q is None and cu_seqlens_k is None:
+        return None
+    for n, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if c is None or c.dtype != torch.int32 or c.dim() != 1 or not c.is_cuda or not c.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor [batch + 1]")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have batch + 1 entries")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        lq = (cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item() if cu_seqlens_q.numel() > 1 else 0
+        lk = (cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item() if cu_seqlens_k.numel() > 1 else 0
+        max_seqlen_q = int(lq) if max_seqlen_q is None else max_seqlen_q
+        max_seqlen_k = int(lk) if max_seqlen_k is None else max_seqlen_k
+    return (cu_seqlens_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k),
+            _abi.Varlen(cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()))
 
 
 @dataclass
@@ -102,9 +122,21 @@ def attn_bwd_workspace_bytes(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk
     return int(_abi.load().isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), ALGOS[algo]))
 
 
+def _dims(q, k, v, vl):
+    """(B, Sq, Sk, Hq, Hk, Dqk, Dv) of fixed-length [B,S,H,D] tensors or of
+    packed [total,H,D] tensors with their varlen tuple."""
+    if vl is None:
+        B, Sq, Hq, Dqk = q.shape
+        return B, Sq, k.shape[1], Hq, k.shape[2], Dqk, v.shape[3]
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed sequences take q, k, v as [total_tokens, heads, dim]")
+    return vl[0], vl[1], vl[2], q.shape[1], k.shape[1], q.shape[2], v.shape[2]
+
+
 def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = False,
              softmax_scale: float | None = None, algo: str = "split", dq=None, dk=None, dv=None,
-             workspace: torch.Tensor | None = None, stream=None, timer: Timer | None = None):
+             workspace: torch.Tensor | None = None, stream=None, timer: Timer | None = None,
+             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
     """Attention backward on the GPU.  Returns (dq, dk, dv) as bf16 tensors.
 
     q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv], o/do [B,Sq,Hq,Dv] bf16;
@@ -114,10 +146,14 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     "split_ds" (the dK/dV pass stores dS for the dQ pass: faster, workspace of
     B*Hq*ceil(Sq/128)*ceil(Sk/128)*32 KiB), "loopk" or "loopq" (the pages'
     loop orders with fp32 atomics).
+    Packed sequences: pass int32 ``cu_seqlens_q`` / ``cu_seqlens_k`` [B + 1]
+    and q, k, v, o, do as [total_tokens, heads, dim]; lse is then
+    [B, Hq, max_seqlen_q] (the longest lengths are computed when not given,
+    which synchronises); "split" and "split_ds" only.
     """
     lib = _abi.load()
-    B, Sq, Hq, Dqk = q.shape
-    Sk, Hk, Dv = k.shape[1], k.shape[2], v.shape[3]
+    vl = _varlen(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    B, Sq, Sk, Hq, Hk, Dqk, Dv = _dims(q, k, v, vl)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
@@ -133,38 +169,53 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     views = [_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
                                       (dq, "dq"), (dk, "dk"), (dv, "dv"))]
     m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
-    args = [ctypes.byref(shape)] + [ctypes.byref(x) for x in views[:5]] + [
+    args = [ctypes.byref(x) for x in views[:5]] + [
         lse.data_ptr(), ctypes.byref(m), int(bool(causal)), float(softmax_scale)] + [
         ctypes.byref(x) for x in views[5:]] + [a, workspace.data_ptr(), workspace.numel(),
                                                _stream_ptr(stream)]
-    if timer is None:
-        _abi.check(lib.isattn_attn_bwd(*args), "isattn_attn_bwd")
+    if vl is not None:
+        if timer is not None:
+            raise ValueError("stage timing is not available for packed sequences")
+        _abi.check(lib.isattn_attn_bwd_varlen(ctypes.byref(shape), ctypes.byref(vl[3]), *args),
+                   "isattn_attn_bwd_varlen")
+    elif timer is None:
+        _abi.check(lib.isattn_attn_bwd(ctypes.byref(shape), *args), "isattn_attn_bwd")
     else:
-        _abi.check(lib.isattn_attn_bwd_timed(*args, timer.handle), "isattn_attn_bwd_timed")
+        _abi.check(lib.isattn_attn_bwd_timed(ctypes.byref(shape), *args, timer.handle), "isattn_attn_bwd_timed")
     return dq, dk, dv
 
 
 def attn_fwd(q, k, v, mask: BlockMask | None = None, causal: bool = False, softmax_scale: float | None = None,
-             o=None, lse=None, stream=None):
+             o=None, lse=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+             max_seqlen_k=None):
     """Attention forward on the GPU.  Returns (o bf16 [B,Sq,Hq,Dv], lse fp32
-    [B,Hq,Sq], natural log, +inf for a row with no kept key).  Same mask and
-    causal conventions as ``attn_bwd``; outputs are allocated when not given.
+    [B,Hq,Sq], natural log, +inf for a row with no kept key).  Same mask,
+    causal and packed-sequence conventions as ``attn_bwd`` (packed: o is
+    [total_q, Hq, Dv]); outputs are allocated when not given.
     """
     lib = _abi.load()
-    B, Sq, Hq, Dqk = q.shape
-    Sk, Hk, Dv = k.shape[1], k.shape[2], v.shape[3]
+    vl = _varlen(cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    B, Sq, Sk, Hq, Hk, Dqk, Dv = _dims(q, k, v, vl)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(Dqk)
-    o = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device) if o is None else o
-    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o is None:
+        oshape = (B, Sq, Hq, Dv) if vl is None else (q.shape[0], Hq, Dv)
+        o = torch.empty(oshape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.full((B, Hq, Sq), float("inf"), dtype=torch.float32, device=q.device) if vl is not None \
+            else torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
         raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
     shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
     vq, vk, vv, vo = (_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")))
     m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
-    _abi.check(lib.isattn_attn_fwd(ctypes.byref(shape), ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv),
-                                   ctypes.byref(m), int(bool(causal)), float(softmax_scale), ctypes.byref(vo),
-                                   lse.data_ptr(), _stream_ptr(stream)), "isattn_attn_fwd")
+    args = [ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), ctypes.byref(m), int(bool(causal)),
+            float(softmax_scale), ctypes.byref(vo), lse.data_ptr(), _stream_ptr(stream)]
+    if vl is not None:
+        _abi.check(lib.isattn_attn_fwd_varlen(ctypes.byref(shape), ctypes.byref(vl[3]), *args),
+                   "isattn_attn_fwd_varlen")
+    else:
+        _abi.check(lib.isattn_attn_fwd(ctypes.byref(shape), *args), "isattn_attn_fwd")
     return o, lse
 
 
@@ -175,8 +226,12 @@ def _csr_buffers(rows_q, rows_k, nnz_max, device):
 
 
 def index_to_block_sparse(indices: torch.Tensor, batch: int, seqlen_q: int, seqlen_k: int,
-                          block_q: int = 128, block_k: int = 128, stream=None) -> BlockMask:
-    """int32 indices [batch*seqlen_q, nhk, topk] -> BlockMask with heads = nhk."""
+                          block_q: int = 128, block_k: int = 128, stream=None, cu_seqlens_q=None,
+                          cu_seqlens_k=None) -> BlockMask:
+    """int32 indices [batch*seqlen_q, nhk, topk] -> BlockMask with heads = nhk.
+    Packed sequences: give ``cu_seqlens_q`` / ``cu_seqlens_k`` (int32 [batch
+    + 1]); indices are then [total_q, nhk, topk] and seqlen_q / seqlen_k the
+    longest lengths."""
     lib = _abi.load()
     if indices.dtype != torch.int32 or indices.dim() != 3 or not indices.is_contiguous():
         raise ValueError("indices must be contiguous int32 [batch*seqlen_q, nhk, topk]")
@@ -189,10 +244,19 @@ def index_to_block_sparse(indices: torch.Tensor, batch: int, seqlen_q: int, seql
     ws_bytes = int(lib.isattn_index_to_block_sparse_workspace_bytes(batch, seqlen_q, seqlen_k, nhk,
                                                                     block_q, block_k))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=indices.device)
-    _abi.check(lib.isattn_index_to_block_sparse(
-        indices.data_ptr(), batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k,
-        qp.data_ptr(), qc.data_ptr(), kp.data_ptr(), kc.data_ptr(), qc.numel(),
-        ws.data_ptr(), ws.numel(), _stream_ptr(stream)), "isattn_index_to_block_sparse")
+    outs = (qp.data_ptr(), qc.data_ptr(), kp.data_ptr(), kc.data_ptr(), qc.numel(), ws.data_ptr(), ws.numel(),
+            _stream_ptr(stream))
+    if cu_seqlens_q is not None or cu_seqlens_k is not None:
+        vl = _varlen(cu_seqlens_q, cu_seqlens_k, seqlen_q, seqlen_k)
+        if vl[0] != batch:
+            raise ValueError("cu_seqlens must have batch + 1 entries")
+        _abi.check(lib.isattn_index_to_block_sparse_varlen(
+            indices.data_ptr(), batch, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), seqlen_q, seqlen_k,
+            nhk, topk, block_q, block_k, *outs), "isattn_index_to_block_sparse_varlen")
+    else:
+        _abi.check(lib.isattn_index_to_block_sparse(
+            indices.data_ptr(), batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k, *outs),
+            "isattn_index_to_block_sparse")
     return BlockMask(nhk, n_qb, n_kb, qp, qc, kp, kc, block_q, block_k)
 
 

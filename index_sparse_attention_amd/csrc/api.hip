@@ -35,11 +35,12 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
                               const isattn_mask_t* mask, int32_t causal, float softmax_scale,
                               const isattn_tensor_t* dq, const isattn_tensor_t* dk,
                               const isattn_tensor_t* dv, int32_t algo, void* workspace,
-                              size_t workspace_bytes, void* stream, isattn_timer_t* timer) {
+                              size_t workspace_bytes, void* stream, isattn_timer_t* timer,
+                              const isattn_varlen_t* varlen = nullptr) {
     BwdArgs a{};
     BwdPlan plan{};
     isattn_status_t st = validate_bwd(shape, q, k, v, o, dO, lse, mask, causal, softmax_scale, dq, dk,
-                                      dv, algo, workspace, workspace_bytes, &a, &plan);
+                                      dv, algo, workspace, workspace_bytes, &a, &plan, varlen);
     if (st != ISATTN_OK) return st;
     if (a.B == 0) return ISATTN_OK;
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
@@ -103,15 +104,47 @@ isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape, const isattn_tensor
                          workspace, workspace_bytes, stream, nullptr);
 }
 
+isattn_status_t isattn_attn_bwd_varlen(const isattn_shape_t* shape, const isattn_varlen_t* varlen,
+                                       const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                       const isattn_tensor_t* v, const isattn_tensor_t* o,
+                                       const isattn_tensor_t* dO, const float* lse,
+                                       const isattn_mask_t* mask_desc, int32_t causal,
+                                       float softmax_scale, const isattn_tensor_t* dq,
+                                       const isattn_tensor_t* dk, const isattn_tensor_t* dv,
+                                       int32_t algo, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+    if (varlen == nullptr) return ISATTN_ERR_NULL;
+    return attn_bwd_impl(shape, q, k, v, o, dO, lse, mask_desc, causal, softmax_scale, dq, dk, dv, algo,
+                         workspace, workspace_bytes, stream, nullptr, varlen);
+}
+
+static isattn_status_t attn_fwd_impl(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                                     const isattn_tensor_t* k, const isattn_tensor_t* v,
+                                     const isattn_mask_t* mask_desc, int32_t causal, float softmax_scale,
+                                     const isattn_tensor_t* o, float* lse, void* stream,
+                                     const isattn_varlen_t* varlen) {
+    FwdArgs a{};
+    const isattn_status_t st =
+        validate_fwd(shape, q, k, v, mask_desc, causal, softmax_scale, o, lse, &a, varlen);
+    if (st != ISATTN_OK) return st;
+    if (a.B == 0) return ISATTN_OK;
+    return launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
+}
+
 isattn_status_t isattn_attn_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
                                 const isattn_tensor_t* k, const isattn_tensor_t* v,
                                 const isattn_mask_t* mask_desc, int32_t causal, float softmax_scale,
                                 const isattn_tensor_t* o, float* lse, void* stream) {
-    FwdArgs a{};
-    const isattn_status_t st = validate_fwd(shape, q, k, v, mask_desc, causal, softmax_scale, o, lse, &a);
-    if (st != ISATTN_OK) return st;
-    if (a.B == 0) return ISATTN_OK;
-    return launch_attn_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
+    return attn_fwd_impl(shape, q, k, v, mask_desc, causal, softmax_scale, o, lse, stream, nullptr);
+}
+
+isattn_status_t isattn_attn_fwd_varlen(const isattn_shape_t* shape, const isattn_varlen_t* varlen,
+                                       const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                       const isattn_tensor_t* v, const isattn_mask_t* mask_desc,
+                                       int32_t causal, float softmax_scale,
+                                       const isattn_tensor_t* o, float* lse, void* stream) {
+    if (varlen == nullptr) return ISATTN_ERR_NULL;
+    return attn_fwd_impl(shape, q, k, v, mask_desc, causal, softmax_scale, o, lse, stream, varlen);
 }
 
 isattn_status_t isattn_attn_bwd_timed(const isattn_shape_t* shape, const isattn_tensor_t* q,
@@ -135,12 +168,13 @@ size_t isattn_index_to_block_sparse_workspace_bytes(int32_t batch, int32_t seqle
     return p.total;
 }
 
-isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t batch, int32_t seqlen_q,
-                                             int32_t seqlen_k, int32_t nhk, int32_t topk,
-                                             int32_t block_q, int32_t block_k, int32_t* q2k_row_ptr,
-                                             int32_t* q2k_col, int32_t* k2q_row_ptr, int32_t* k2q_col,
-                                             int64_t col_capacity, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
+static isattn_status_t index_to_block_sparse_impl(const int32_t* indices, int32_t batch,
+                                                  const int32_t* cu_q, const int32_t* cu_k, int32_t seqlen_q,
+                                                  int32_t seqlen_k, int32_t nhk, int32_t topk,
+                                                  int32_t block_q, int32_t block_k, int32_t* q2k_row_ptr,
+                                                  int32_t* q2k_col, int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                                  int64_t col_capacity, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
     CsrPlan p{};
     isattn_status_t st = validate_index(indices, batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k,
                                         q2k_row_ptr, q2k_col, k2q_row_ptr, k2q_col, col_capacity,
@@ -152,13 +186,39 @@ isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t bat
     uint8_t* presence = reinterpret_cast<uint8_t*>(ws_at(workspace, p.off_presence));
     int32_t* qcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_qcnt));
     int32_t* kcnt = reinterpret_cast<int32_t*>(ws_at(workspace, p.off_kcnt));
-    if (launch_index_presence(indices, batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k, n_qb, n_kb,
-                              presence, qcnt, s) != hipSuccess)
+    if (launch_index_presence(indices, cu_q, cu_k, batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k,
+                              n_qb, n_kb, presence, qcnt, s) != hipSuccess)
         return ISATTN_ERR_HIP;
     if (launch_presence_to_csr(presence, batch * nhk, n_qb, n_kb, true, qcnt, kcnt, q2k_row_ptr, q2k_col,
                                k2q_row_ptr, k2q_col, s) != hipSuccess)
         return ISATTN_ERR_HIP;
     return ISATTN_OK;
+}
+
+isattn_status_t isattn_index_to_block_sparse(const int32_t* indices, int32_t batch, int32_t seqlen_q,
+                                             int32_t seqlen_k, int32_t nhk, int32_t topk,
+                                             int32_t block_q, int32_t block_k, int32_t* q2k_row_ptr,
+                                             int32_t* q2k_col, int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                             int64_t col_capacity, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+    return index_to_block_sparse_impl(indices, batch, nullptr, nullptr, seqlen_q, seqlen_k, nhk, topk, block_q,
+                                      block_k, q2k_row_ptr, q2k_col, k2q_row_ptr, k2q_col, col_capacity,
+                                      workspace, workspace_bytes, stream);
+}
+
+isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int32_t batch,
+                                                    const int32_t* cu_seqlens_q,
+                                                    const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
+                                                    int32_t max_seqlen_k, int32_t nhk, int32_t topk,
+                                                    int32_t block_q, int32_t block_k,
+                                                    int32_t* q2k_row_ptr, int32_t* q2k_col,
+                                                    int32_t* k2q_row_ptr, int32_t* k2q_col,
+                                                    int64_t col_capacity, void* workspace,
+                                                    size_t workspace_bytes, void* stream) {
+    if (batch > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return ISATTN_ERR_NULL;
+    return index_to_block_sparse_impl(indices, batch, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                                      nhk, topk, block_q, block_k, q2k_row_ptr, q2k_col, k2q_row_ptr,
+                                      k2q_col, col_capacity, workspace, workspace_bytes, stream);
 }
 
 size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,

@@ -23,7 +23,7 @@ struct BwdArgs {
     uint16_t* dq; int64_t dq_sb, dq_ss, dq_sh;
     uint16_t* dk; int64_t dk_sb, dk_ss, dk_sh;
     uint16_t* dv; int64_t dv_sb, dv_ss, dv_sh;
-    const float* lse;     // [B, Hq, Sq] natural-log LSE
+    const float* lse;     // [B, Hq, lse_ld] natural-log LSE
     float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O)
     float* lse2;          // [B, Hq, stat_ld] workspace (SPLIT only): lse * log2(e); else null
     int32_t* order;       // SPLIT work order: B*Hk*n_kb dK/dV items, then B*Hq*n_qb dQ items; else null
@@ -42,8 +42,14 @@ struct BwdArgs {
     // block CSR (mask_kind == 1)
     const int32_t* q2k_ptr; const int32_t* q2k_col;
     const int32_t* k2q_ptr; const int32_t* k2q_col;
+    // packed variable-length sequences: sequence b is tokens [cu_q[b], cu_q[b+1])
+    // of the query-side tensors and [cu_k[b], cu_k[b+1]) of the key side; Sq
+    // and Sk hold the longest lengths (a kernel narrows them to its sequence
+    // with seq_view); null for fixed-length batches
+    const int32_t* cu_q; const int32_t* cu_k;
     int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
     int32_t Hm, n_qb, n_kb;
+    int32_t lse_ld;       // row stride of lse per (b, h): the (longest) Sq
     int32_t stat_ld;      // row stride of delta / lse2 per (b, h): Sq, or n_qb * 128 for SPLIT
                           // (rows Sq.. hold delta = 0, lse2 = +inf)
     int32_t mask_kind, causal;
@@ -57,12 +63,51 @@ struct FwdArgs {
     const uint16_t* k; int64_t k_sb, k_ss, k_sh;
     const uint16_t* v; int64_t v_sb, v_ss, v_sh;
     uint16_t* o; int64_t o_sb, o_ss, o_sh;
-    float* lse;           // [B, Hq, Sq] natural-log LSE (+inf for a row with no kept key)
+    float* lse;           // [B, Hq, lse_ld] natural-log LSE (+inf for a row with no kept key)
     const int32_t* q2k_ptr; const int32_t* q2k_col;   // block CSR (mask_kind == 1)
+    const int32_t* cu_q; const int32_t* cu_k;         // packed sequences, as in BwdArgs
     int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
     int32_t Hm, n_qb, n_kb;
+    int32_t lse_ld;
     int32_t mask_kind, causal;
     float scale_log2;     // softmax_scale * log2(e)
 };
+
+#if defined(__HIPCC__)
+// Narrow the arguments to packed sequence b: its lengths (clamped to the
+// longest, so tiles and statistics rows stay inside their allocations) and
+// tensor pointers moved so that the batch-b address arithmetic of the
+// kernels (base + b * stride_b + row * stride_s) lands on its first token.
+__device__ __forceinline__ int seq_len(const int32_t* cu, int b, int longest) {
+    const int n = cu[b + 1] - cu[b];
+    return n < 0 ? 0 : (n > longest ? longest : n);
+}
+template <class T>
+__device__ __forceinline__ void seq_shift(T*& p, int64_t first, int64_t ss, int64_t sb, int b) {
+    p += first * ss - int64_t(b) * sb;
+}
+__device__ __forceinline__ void seq_view(BwdArgs& a, int b) {
+    const int64_t q0 = a.cu_q[b], k0 = a.cu_k[b];
+    a.Sq = seq_len(a.cu_q, b, a.Sq);
+    a.Sk = seq_len(a.cu_k, b, a.Sk);
+    seq_shift(a.q, q0, a.q_ss, a.q_sb, b);
+    seq_shift(a.o, q0, a.o_ss, a.o_sb, b);
+    seq_shift(a.dO, q0, a.do_ss, a.do_sb, b);
+    seq_shift(a.dq, q0, a.dq_ss, a.dq_sb, b);
+    seq_shift(a.k, k0, a.k_ss, a.k_sb, b);
+    seq_shift(a.v, k0, a.v_ss, a.v_sb, b);
+    seq_shift(a.dk, k0, a.dk_ss, a.dk_sb, b);
+    seq_shift(a.dv, k0, a.dv_ss, a.dv_sb, b);
+}
+__device__ __forceinline__ void seq_view(FwdArgs& a, int b) {
+    const int64_t q0 = a.cu_q[b], k0 = a.cu_k[b];
+    a.Sq = seq_len(a.cu_q, b, a.Sq);
+    a.Sk = seq_len(a.cu_k, b, a.Sk);
+    seq_shift(a.q, q0, a.q_ss, a.q_sb, b);
+    seq_shift(a.o, q0, a.o_ss, a.o_sb, b);
+    seq_shift(a.k, k0, a.k_ss, a.k_sb, b);
+    seq_shift(a.v, k0, a.v_ss, a.v_sb, b);
+}
+#endif
 
 }  // namespace isattn

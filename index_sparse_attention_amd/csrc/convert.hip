@@ -48,9 +48,9 @@ __device__ __forceinline__ void mark_key(uint32_t* bits, int x, int Sk, int bk, 
 }
 
 __global__ __launch_bounds__(kPresThreads) void k_index_presence(
-    const int32_t* __restrict__ idx, int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq,
-    int32_t bk, int32_t bk_shift, int32_t n_qb, int32_t n_kb, int32_t vec4,
-    uint8_t* __restrict__ presence, int32_t* __restrict__ qcnt) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq, int32_t bk, int32_t bk_shift,
+    int32_t n_qb, int32_t n_kb, int32_t vec4, uint8_t* __restrict__ presence, int32_t* __restrict__ qcnt) {
     extern __shared__ uint32_t bits[];
     __shared__ int red[kPresThreads / 64];
     const int qb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -59,10 +59,18 @@ __global__ __launch_bounds__(kPresThreads) void k_index_presence(
     for (int w = tid; w < nwords; w += kPresThreads) bits[w] = 0;
     __syncthreads();
 
+    // sequence b: index rows [first, first + Sq) and keys [0, Sk); packed
+    // sequences (cu_q, cu_k) have their own lengths, at most the longest
+    int64_t first = int64_t(b) * Sq;
+    if (cu_q != nullptr) {
+        first = cu_q[b];
+        Sq = min(max(cu_q[b + 1] - cu_q[b], 0), Sq);
+        Sk = min(max(cu_k[b + 1] - cu_k[b], 0), Sk);
+    }
     const int r0 = qb * bq;
-    const int rows = min(bq, Sq - r0);
+    const int rows = max(0, min(bq, Sq - r0));
     const int64_t row_stride = int64_t(nhk) * topk;
-    const int32_t* base = idx + (int64_t(b) * Sq + r0) * row_stride + int64_t(hk) * topk;
+    const int32_t* base = idx + (first + r0) * row_stride + int64_t(hk) * topk;
     if (vec4) {
         const int per_row = topk >> 2;
         const int total = rows * per_row;
@@ -247,8 +255,8 @@ __global__ __launch_bounds__(256) void k_fill(const uint8_t* __restrict__ presen
 
 }  // namespace
 
-hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,
-                                 int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
+hipError_t launch_index_presence(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                                 int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
                                  int32_t n_qb, int32_t n_kb, uint8_t* presence, int32_t* qcnt,
                                  hipStream_t s) {
     if (B == 0 || nhk == 0 || n_qb == 0) return hipSuccess;
@@ -261,8 +269,8 @@ hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int3
         if (e != hipSuccess) return e;
     }
     dim3 grid(n_qb, nhk, B);
-    hipLaunchKernelGGL(k_index_presence, grid, dim3(kPresThreads), lds, s, idx, Sq, Sk, nhk, topk, bq,
-                       bk, bk_shift, n_qb, n_kb, vec4, presence, qcnt);
+    hipLaunchKernelGGL(k_index_presence, grid, dim3(kPresThreads), lds, s, idx, cu_q, cu_k, Sq, Sk, nhk, topk,
+                       bq, bk, bk_shift, n_qb, n_kb, vec4, presence, qcnt);
     return hipGetLastError();
 }
 

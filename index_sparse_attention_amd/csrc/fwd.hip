@@ -51,7 +51,7 @@ struct FwdCfg {
     static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool VL>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     using C = FwdCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -70,24 +70,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     const int h = bh - b * a.Hq;
     const int hk = h / a.G;
     const int m_base = qb * C::BM;
-    const int last_row = min(m_base + C::BM - 1, a.Sq - 1);
+    if constexpr (VL) {                            // packed sequences: narrow to sequence b
+        seq_view(a, b);
+        if (m_base >= a.Sq) return;                // a block past the end of the sequence
+    }
     const int shift = a.Sk - a.Sq;
 
     KeySteps steps;
-    steps.lane = lane;
-    steps.n_kb = a.n_kb;
-    const int diag = last_row + shift;
-    steps.last = a.causal ? min(diag, a.Sk - 1) : a.Sk - 1;
-    if (a.mask_kind == 1) {
-        const int hm = h * a.Hm / a.Hq;
-        const int r = (b * a.Hm + hm) * a.n_qb + qb;
-        const int beg = a.q2k_ptr[r];
-        steps.count = a.q2k_ptr[r + 1] - beg;
-        steps.list = a.q2k_col + beg;
-    } else {
-        steps.count = a.n_kb;
-        if (a.causal) steps.count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
-    }
+    init_key_steps(steps, a, b, h, qb, lane);
 
     // ---- resident operand: this wave's Q rows (B operand of S^T = K Q^T)
     const int qrow = m_base + 32 * w + l32;
@@ -261,31 +251,36 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
                 *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * g + 4 * h2) = pkd;
             }
         if (h2 == 0)
-            a.lse[(int64_t(b) * a.Hq + h) * a.Sq + qrow] =
+            a.lse[(int64_t(b) * a.Hq + h) * a.lse_ld + qrow] =
                 l_tot > 0.f ? kLn2 * (m_run + __builtin_amdgcn_logf(l_tot)) : __builtin_inff();
     }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool VL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     using C = FwdCfg<DQK, DV>;
     const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_fwd<DQK, DV>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_fwd<DQK, DV, VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_attn_fwd<DQK, DV>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_attn_fwd<DQK, DV, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
+    return a.cu_q != nullptr ? launch_fwd_t<DQK, DV, true>(a, s) : launch_fwd_t<DQK, DV, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s) {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_t<64, 64>(a, s);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_t<128, 128>(a, s);
-    if (a.Dqk == 192 && a.Dv == 128) return launch_fwd_t<192, 128>(a, s);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_fwd_d<64, 64>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_fwd_d<128, 128>(a, s);
+    if (a.Dqk == 192 && a.Dv == 128) return launch_fwd_d<192, 128>(a, s);
     return hipErrorInvalidValue;
 }
 

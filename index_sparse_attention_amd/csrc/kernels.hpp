@@ -25,8 +25,10 @@ hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
-hipError_t launch_index_presence(const int32_t* idx, int32_t B, int32_t Sq, int32_t Sk,
-                                 int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
+// Packed sequences: cu_q / cu_k (else null) give each sequence's rows and
+// length; Sq, Sk are then the longest lengths.
+hipError_t launch_index_presence(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                                 int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq, int32_t bk,
                                  int32_t n_qb, int32_t n_kb, uint8_t* presence, int32_t* qcnt,
                                  hipStream_t s);
 // Presence -> Q->K and K->Q CSR.  Row counts are computed here unless

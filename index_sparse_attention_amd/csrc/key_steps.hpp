@@ -47,4 +47,29 @@ struct KeySteps {
     }
 };
 
+// The steps of query block qb of (batch b, query head h): the kept key blocks
+// of its Q->K CSR row, or every key block of the sequence (dense), cut at
+// the bottom-right causal diagonal of its last row.  a.Sq and a.Sk are the
+// lengths of b's sequence; a.n_qb, a.n_kb the (longest) block counts the CSR
+// rows are laid out with.
+template <class Args>
+__device__ __forceinline__ void init_key_steps(KeySteps& st, const Args& a, int b, int h, int qb, int lane) {
+    st.lane = lane;
+    st.n_kb = a.n_kb;
+    const int last_row = min(qb * kBlock + kBlock - 1, a.Sq - 1);
+    const int diag = last_row + a.Sk - a.Sq;
+    st.last = a.causal ? min(diag, a.Sk - 1) : a.Sk - 1;
+    if (a.mask_kind == 1) {
+        const int hm = h * a.Hm / a.Hq;
+        const int r = (b * a.Hm + hm) * a.n_qb + qb;
+        const int beg = a.q2k_ptr[r];
+        st.count = a.q2k_ptr[r + 1] - beg;
+        st.list = a.q2k_col + beg;
+    } else {
+        const int nkb = (a.Sk + kBlock - 1) / kBlock;
+        st.count = nkb;
+        if (a.causal) st.count = diag < 0 ? 0 : min(nkb, diag / kBlock + 1);
+    }
+}
+
 }  // namespace isattn

@@ -41,6 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
         const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
         const int sub = threadIdx.x % L;
         int64_t row[R], stat[R], i[R];
+        bool in[R];
         u32x4_t o[R], g[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -52,9 +53,23 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
             stat[r] = (b * a.Hq + h) * a.stat_ld + i[r];
             o[r] = u32x4_t{0u, 0u, 0u, 0u};
             g[r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (row[r] < rows && i[r] < a.Sq) {
-                o[r] = gload128(a.o + b * a.o_sb + i[r] * a.o_ss + h * a.o_sh + 8 * sub);
-                g[r] = gload128(a.dO + b * a.do_sb + i[r] * a.do_ss + h * a.do_sh + 8 * sub);
+            in[r] = false;
+            if (row[r] < rows) {
+                // token row of (b, i): b * stride_b + i * stride_s, or for packed
+                // sequences cu_q[b] + i (rows past the sequence's length are padding)
+                int64_t ob = b * a.o_sb + i[r] * a.o_ss, db = b * a.do_sb + i[r] * a.do_ss;
+                int sq = a.Sq;
+                if (a.cu_q != nullptr) {
+                    const int64_t t = a.cu_q[b] + i[r];
+                    sq = seq_len(a.cu_q, int(b), a.Sq);
+                    ob = t * a.o_ss;
+                    db = t * a.do_ss;
+                }
+                in[r] = i[r] < sq;
+                if (in[r]) {
+                    o[r] = gload128(a.o + ob + h * a.o_sh + 8 * sub);
+                    g[r] = gload128(a.dO + db + h * a.do_sh + 8 * sub);
+                }
             }
         }
 #pragma unroll
@@ -71,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk
                 a.delta[stat[r]] = acc;
                 if (a.lse2 != nullptr) {
                     const int64_t bh = stat[r] / a.stat_ld;
-                    a.lse2[stat[r]] = i[r] < a.Sq ? a.lse[bh * a.Sq + i[r]] * kLog2e : __builtin_inff();
+                    a.lse2[stat[r]] = in[r] ? a.lse[bh * a.lse_ld + i[r]] * kLog2e : __builtin_inff();
                 }
             }
         }

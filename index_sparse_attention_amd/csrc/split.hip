@@ -52,11 +52,14 @@ constexpr int kSchedThreads = 1024;
 constexpr int kSchedKeys = 4096;
 
 // kept query blocks a dK/dV item (b, KV head, key block) visits, over its GQA group
-__device__ int item_work_kv(const BwdArgs& a, int item) {
+__device__ int item_work_kv(const BwdArgs& a0, int item) {
+    BwdArgs a = a0;
     const int bh = item / a.n_kb;
     const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
+    if (a.cu_q != nullptr) seq_view(a, b);
+    if (kb * kBlock >= a.Sk) return 0;             // past the end of b's keys
     if (a.mask_kind == 1) {
         int w = 0;
         for (int g = 0; g < a.G; ++g) {
@@ -68,21 +71,25 @@ __device__ int item_work_kv(const BwdArgs& a, int item) {
     }
     const int first_row = kb * kBlock - (a.Sk - a.Sq);
     const int first = a.causal && first_row > 0 ? first_row / kBlock : 0;
-    return a.G * max(0, a.n_qb - first);
+    return a.G * max(0, (a.Sq + kBlock - 1) / kBlock - first);
 }
 // kept key blocks a dQ item (b, query head, query block) visits
-__device__ int item_work_q(const BwdArgs& a, int item) {
+__device__ int item_work_q(const BwdArgs& a0, int item) {
+    BwdArgs a = a0;
     const int bh = item / a.n_qb;
     const int qb = item - bh * a.n_qb;
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
+    if (a.cu_q != nullptr) seq_view(a, b);
+    if (qb * kBlock >= a.Sq) return 0;             // past the end of b's queries
     if (a.mask_kind == 1) {
         const int r = (b * a.Hm + h * a.Hm / a.Hq) * a.n_qb + qb;
         return a.q2k_ptr[r + 1] - a.q2k_ptr[r];
     }
-    if (!a.causal) return a.n_kb;
+    const int nkb = (a.Sk + kBlock - 1) / kBlock;
+    if (!a.causal) return nkb;
     const int diag = min(qb * kBlock + kBlock - 1, a.Sq - 1) + (a.Sk - a.Sq);
-    return diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
+    return diag < 0 ? 0 : min(nkb, diag / kBlock + 1);
 }
 
 // Exclusive block-wide scan of one value per thread (kSchedThreads threads);
@@ -244,7 +251,7 @@ struct DqCfg {
     static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
 };
 
-template <int DQK, int DV, int WR>
+template <int DQK, int DV, int WR, bool VL>
 // two workgroups per CU (two waves per SIMD) where the registers allow
 __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(BwdArgs a) {
     using C = DqCfg<DQK, DV, WR>;
@@ -264,24 +271,14 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     const int h = bh - b * a.Hq;
     const int hk = h / a.G;
     const int m_base = qb * C::BM;
-    const int last_row = min(m_base + C::BM - 1, a.Sq - 1);
+    if constexpr (VL) {                            // packed sequences: narrow to sequence b
+        seq_view(a, b);
+        if (m_base >= a.Sq) return;                // a block past the end of the sequence
+    }
     const int shift = a.Sk - a.Sq;
 
     KeySteps steps;
-    steps.lane = lane;
-    steps.n_kb = a.n_kb;
-    const int diag = last_row + shift;
-    steps.last = a.causal ? min(diag, a.Sk - 1) : a.Sk - 1;
-    if (a.mask_kind == 1) {
-        const int hm = h * a.Hm / a.Hq;
-        const int r = (b * a.Hm + hm) * a.n_qb + qb;
-        const int beg = a.q2k_ptr[r];
-        steps.count = a.q2k_ptr[r + 1] - beg;
-        steps.list = a.q2k_col + beg;
-    } else {
-        steps.count = a.n_kb;
-        if (a.causal) steps.count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
-    }
+    init_key_steps(steps, a, b, h, qb, lane);
 
     // ---- resident operands: this wave's Q / dO rows (B operands), and the
     // rows' statistics, computed here and stored for the dK/dV pass (which
@@ -307,7 +304,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
             doB[qt][c] = in ? gload_operand(dr + 16 * c) : bf16x8_t{};
             ov[c] = in ? gload128(orow + 16 * c) : u32x4_t{0u, 0u, 0u, 0u};
         }
-        lse2[qt] = in ? a.lse[(int64_t(b) * a.Hq + h) * a.Sq + qrow] * kLog2e : __builtin_inff();
+        lse2[qt] = in ? a.lse[(int64_t(b) * a.Hq + h) * a.lse_ld + qrow] * kLog2e : __builtin_inff();
         float acc = 0.f;
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
@@ -659,7 +656,7 @@ struct DkvSteps {
                 const int first_row = n_base - shift;
                 first = first_row <= 0 ? 0 : first_row / kBlock;
             }
-            count = a.n_qb - first;
+            count = (a.Sq + kBlock - 1) / kBlock - first;
         }
     }
     __device__ int qb_at() {
@@ -684,7 +681,7 @@ struct DkvSteps {
             }
             if (cum + it >= hi) return false;
             const int qb = qb_at();
-            if (qb < 0 || qb >= a.n_qb) continue;  // malformed entry: nothing to do
+            if (qb < 0 || qb >= a.n_qb || qb * kBlock >= a.Sq) continue;  // malformed entry: nothing to do
             if (a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base) continue;
             part = 0;
             m = qb * kBlock;
@@ -1341,7 +1338,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     role.drain();
 }
 
-template <int DQK, int DV, bool DS>
+template <int DQK, int DV, bool DS, bool VL>
 __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     using C = DkvCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -1371,6 +1368,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
+    if constexpr (VL) {                            // packed sequences: narrow to sequence b
+        seq_view(a, b);
+        if (kb * C::BN >= a.Sk) return;            // a key block past the end of the sequence
+    }
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
     DkvSteps<C::BM> steps(a, b, hk, kb, lane);
     steps.lo = lo;
@@ -1386,17 +1387,17 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     }
 }
 
-template <int DQK, int DV, int WR>
+template <int DQK, int DV, int WR, bool VL>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
     using C = DqCfg<DQK, DV, WR>;
     const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq<DQK, DV, WR>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq<DQK, DV, WR, VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_bwd_dq<DQK, DV, WR>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dq<DQK, DV, WR, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -1415,6 +1416,7 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
     const int kb = item - bh * a.n_kb;
     const int b = bh / a.Hk;
     const int hk = bh - b * a.Hk;
+    if (a.cu_q != nullptr) seq_view(a, b);
     const int key0 = (blockIdx.x % (kBlock / 8)) * 8;
     for (int u = threadIdx.x; u < 8 * W / 4; u += 256) {
         const int r = key0 + (4 * u) / W;
@@ -1432,25 +1434,38 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
     }
 }
 
-template <int DQK, int DV, bool DS>
+template <int DQK, int DV, bool DS, bool VL>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<DQK, DV>;
     const int64_t items = int64_t(a.n_kb) * a.B * a.Hk;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV, DS>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV, DS, VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     if (a.kv_parts_T > 0) {                        // part mode: one workgroup per unit, then the reduction
-        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
+        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_dkdv_reduce<DQK, DV>), dim3(unsigned(items * (kBlock / 8))), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
+    const bool ds = a.ds != nullptr;               // SPLIT_DS: also store dS
+    if (a.cu_q != nullptr)                         // packed sequences
+        return ds ? launch_dkdv_t<DQK, DV, true, true>(a, s) : launch_dkdv_t<DQK, DV, false, true>(a, s);
+    return ds ? launch_dkdv_t<DQK, DV, true, false>(a, s) : launch_dkdv_t<DQK, DV, false, false>(a, s);
+}
+
+template <int DQK, int DV, int WR>
+hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
+    return a.cu_q != nullptr ? launch_dq_t<DQK, DV, WR, true>(a, s) : launch_dq_t<DQK, DV, WR, false>(a, s);
 }
 
 }  // namespace
@@ -1462,19 +1477,16 @@ hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s) {
-    const bool ds = a.ds != nullptr;               // SPLIT_DS: also store dS
-    if (a.Dqk == 64 && a.Dv == 64) return ds ? launch_dkdv_t<64, 64, true>(a, s) : launch_dkdv_t<64, 64, false>(a, s);
-    if (a.Dqk == 128 && a.Dv == 128)
-        return ds ? launch_dkdv_t<128, 128, true>(a, s) : launch_dkdv_t<128, 128, false>(a, s);
-    if (a.Dqk == 192 && a.Dv == 128)
-        return ds ? launch_dkdv_t<192, 128, true>(a, s) : launch_dkdv_t<192, 128, false>(a, s);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_dkdv_d<64, 64>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_dkdv_d<128, 128>(a, s);
+    if (a.Dqk == 192 && a.Dv == 128) return launch_dkdv_d<192, 128>(a, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s) {
-    if (a.Dqk == 64 && a.Dv == 64) return launch_dq_t<64, 64, 32>(a, s);
-    if (a.Dqk == 128 && a.Dv == 128) return launch_dq_t<128, 128, 32>(a, s);
-    if (a.Dqk == 192 && a.Dv == 128) return launch_dq_t<192, 128, 32>(a, s);
+    if (a.Dqk == 64 && a.Dv == 64) return launch_dq_d<64, 64, 32>(a, s);
+    if (a.Dqk == 128 && a.Dv == 128) return launch_dq_d<128, 128, 32>(a, s);
+    if (a.Dqk == 192 && a.Dv == 128) return launch_dq_d<192, 128, 32>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t ds_lds_off(int l, int cc, int j, int hf) {
     return uint32_t(1024 * cc + 16 * s + 8 * hf);
 }
 
-template <int DQK>
+template <int DQK, bool VL>
 __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a) {
     using C = DsqCfg<DQK>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -89,25 +89,14 @@ __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a)
     const int h = bh - b * a.Hq;
     const int hk = h / a.G;
     const int m_base = qb * C::BM;
-    const int last_row = min(m_base + C::BM - 1, a.Sq - 1);
-    const int shift = a.Sk - a.Sq;
+    if constexpr (VL) {                            // packed sequences: narrow to sequence b
+        seq_view(a, b);
+        if (m_base >= a.Sq) return;                // a block past the end of the sequence
+    }
 
     // the key blocks the dK/dV pass visited for this query block
     KeySteps steps;
-    steps.lane = lane;
-    steps.n_kb = a.n_kb;
-    const int diag = last_row + shift;
-    steps.last = a.causal ? min(diag, a.Sk - 1) : a.Sk - 1;
-    if (a.mask_kind == 1) {
-        const int hm = h * a.Hm / a.Hq;
-        const int r = (b * a.Hm + hm) * a.n_qb + qb;
-        const int beg = a.q2k_ptr[r];
-        steps.count = a.q2k_ptr[r + 1] - beg;
-        steps.list = a.q2k_col + beg;
-    } else {
-        steps.count = a.n_kb;
-        if (a.causal) steps.count = diag < 0 ? 0 : min(a.n_kb, diag / kBlock + 1);
-    }
+    init_key_steps(steps, a, b, h, qb, lane);
 
     f32x16_t dq[C::NDT];
 #pragma unroll
@@ -242,27 +231,28 @@ __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a)
         }
 }
 
-template <int DQK>
+template <int DQK, bool VL>
 hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     using C = DsqCfg<DQK>;
     const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq_ds<DQK>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq_ds<DQK, VL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_bwd_dq_ds<DQK>, dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dq_ds<DQK, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s) {
+    const bool vl = a.cu_q != nullptr;             // packed sequences
     switch (a.Dqk) {
-        case 64: return launch_t<64>(a, s);
-        case 128: return launch_t<128>(a, s);
-        case 192: return launch_t<192>(a, s);
+        case 64: return vl ? launch_t<64, true>(a, s) : launch_t<64, false>(a, s);
+        case 128: return vl ? launch_t<128, true>(a, s) : launch_t<128, false>(a, s);
+        case 192: return vl ? launch_t<192, true>(a, s) : launch_t<192, false>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

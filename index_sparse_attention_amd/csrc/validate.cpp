@@ -120,7 +120,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
                              float softmax_scale, const isattn_tensor_t* dq,
                              const isattn_tensor_t* dk, const isattn_tensor_t* dv, int32_t algo,
                              const void* workspace, size_t workspace_bytes, BwdArgs* args,
-                             BwdPlan* plan) {
+                             BwdPlan* plan, const isattn_varlen_t* varlen) {
     if (shape == nullptr) return ISATTN_ERR_NULL;
     const isattn_shape_t s = *shape;
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
@@ -179,6 +179,16 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         a.k2q_col = mask->k2q_col;
     }
 
+    if (varlen != nullptr) {
+        // packed sequences: the two-pass algorithms only (LoopK is fixed-length
+        // only, [P1] Limitations; LoopQ follows it)
+        if (algo != ISATTN_ALGO_SPLIT && algo != ISATTN_ALGO_SPLIT_DS) return ISATTN_ERR_UNSUPPORTED;
+        if (s.batch > 0 && (varlen->cu_seqlens_q == nullptr || varlen->cu_seqlens_k == nullptr))
+            return ISATTN_ERR_NULL;
+        a.cu_q = varlen->cu_seqlens_q;
+        a.cu_k = varlen->cu_seqlens_k;
+    }
+
     BwdPlan p{};
     if (!plan_bwd_workspace(s, algo, &p)) return ISATTN_ERR_SHAPE;
     if (workspace_bytes < p.total) return ISATTN_ERR_WORKSPACE;
@@ -204,6 +214,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     a.Dv = s.dim_v;
     a.n_qb = p.n_qb;
     a.n_kb = p.n_kb;
+    a.lse_ld = s.seqlen_q;
     a.stat_ld = p.stat_ld;
     a.causal = causal != 0;
     a.scale = softmax_scale;
@@ -250,7 +261,8 @@ static isattn_status_t check_csr_outputs(int64_t rows_q_total, int64_t nnz_max,
 isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
                              const isattn_tensor_t* k, const isattn_tensor_t* v,
                              const isattn_mask_t* mask, int32_t causal, float softmax_scale,
-                             const isattn_tensor_t* o, const float* lse, FwdArgs* args) {
+                             const isattn_tensor_t* o, const float* lse, FwdArgs* args,
+                             const isattn_varlen_t* varlen) {
     if (shape == nullptr) return ISATTN_ERR_NULL;
     const isattn_shape_t s = *shape;
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
@@ -288,6 +300,12 @@ isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t*
         a.q2k_ptr = mask->q2k_row_ptr;
         a.q2k_col = mask->q2k_col;
     }
+    if (varlen != nullptr) {
+        if (s.batch > 0 && (varlen->cu_seqlens_q == nullptr || varlen->cu_seqlens_k == nullptr))
+            return ISATTN_ERR_NULL;
+        a.cu_q = varlen->cu_seqlens_q;
+        a.cu_k = varlen->cu_seqlens_k;
+    }
     copy_view(q, &a.q, &a.q_sb, &a.q_ss, &a.q_sh);
     copy_view(k, &a.k, &a.k_sb, &a.k_ss, &a.k_sh);
     copy_view(v, &a.v, &a.v_sb, &a.v_ss, &a.v_sh);
@@ -303,6 +321,7 @@ isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t*
     a.Dv = s.dim_v;
     a.n_qb = cdiv(s.seqlen_q, kBlock);
     a.n_kb = cdiv(s.seqlen_k, kBlock);
+    a.lse_ld = s.seqlen_q;
     a.causal = causal != 0;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     *args = a;

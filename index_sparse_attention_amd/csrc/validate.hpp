@@ -38,13 +38,14 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
                              float softmax_scale, const isattn_tensor_t* dq,
                              const isattn_tensor_t* dk, const isattn_tensor_t* dv, int32_t algo,
                              const void* workspace, size_t workspace_bytes, BwdArgs* args,
-                             BwdPlan* plan);
+                             BwdPlan* plan, const isattn_varlen_t* varlen = nullptr);
 
 // Argument check of the forward; on success fills `args`.
 isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,
                              const isattn_tensor_t* k, const isattn_tensor_t* v,
                              const isattn_mask_t* mask, int32_t causal, float softmax_scale,
-                             const isattn_tensor_t* o, const float* lse, FwdArgs* args);
+                             const isattn_tensor_t* o, const float* lse, FwdArgs* args,
+                             const isattn_varlen_t* varlen = nullptr);
 
 struct CsrPlan {
     int32_t rows_q, rows_k;       // B*H*n_qb, B*H*n_kb

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
@@ -199,3 +199,35 @@ def test_block_mask_validation_errors(lib):
     assert call(H=-2) == SHAPE
     assert call(cap=10) == CAP
     assert call(wsb=0) == WS
+
+
+def test_varlen_validation_errors(lib):
+    """Packed sequences: the varlen descriptor and its arrays are required,
+    and only the two-pass algorithms take them (checked before any launch)."""
+    vl = _abi.Varlen(FAKE, FAKE)
+
+    def bwd(algo, varlen):
+        c = Call(lib, algo=algo)
+        ref = lambda t: ctypes.byref(t) if t is not None else None
+        v = c.views
+        return lib.isattn_attn_bwd_varlen(ctypes.byref(c.shape), ctypes.byref(varlen) if varlen is not None else None,
+                                          ref(v["q"]), ref(v["k"]), ref(v["v"]), ref(v["o"]), ref(v["do"]),
+                                          c.lse, None, 0, 0.125, ref(v["dq"]), ref(v["dk"]), ref(v["dv"]), algo,
+                                          c.ws, c.ws_bytes, None)
+    assert bwd(2, None) == NULL
+    assert bwd(0, vl) == UNSUP
+    assert bwd(1, vl) == UNSUP
+    assert bwd(2, _abi.Varlen(None, FAKE)) == NULL
+    assert bwd(3, _abi.Varlen(FAKE, None)) == NULL
+    s = shape()
+    t = _abi.Tensor(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    assert lib.isattn_attn_fwd_varlen(ctypes.byref(s), None, ctypes.byref(t), ctypes.byref(t), ctypes.byref(t),
+                                      None, 0, 0.125, ctypes.byref(t), FAKE, None) == NULL
+    assert lib.isattn_attn_fwd_varlen(ctypes.byref(s), ctypes.byref(_abi.Varlen(FAKE, None)), ctypes.byref(t),
+                                      ctypes.byref(t), ctypes.byref(t), None, 0, 0.125, ctypes.byref(t), FAKE,
+                                      None) == NULL
+    wsb = lib.isattn_index_to_block_sparse_workspace_bytes(1, 256, 256, 2, 128, 128)
+    assert lib.isattn_index_to_block_sparse_varlen(FAKE, 1, None, FAKE, 256, 256, 2, 64, 128, 128, FAKE, FAKE,
+                                                   FAKE, FAKE, 8, FAKE, wsb, None) == NULL
+    assert lib.isattn_index_to_block_sparse_varlen(FAKE, 1, FAKE, FAKE, 256, 256, 2, 64, 128, 128, FAKE, FAKE,
+                                                   FAKE, FAKE, 3, FAKE, wsb, None) == CAP
