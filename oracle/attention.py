@@ -81,7 +81,7 @@ def attn_fwd(q, k, v, mask: MaskSpec, causal: bool, scale: float, heads=None):
                 cols = _key_positions(_m.q2k_row(mask, b, hm, qb, n_qb, n_kb), bk, Sk)
                 if len(cols) == 0:
                     continue
-                em = _m.element_mask(rows, cols, Sq, Sk, causal)
+                em = _m.element_mask(rows, cols, Sq, Sk, causal) & _m.token_term(mask, b, hm, rows, cols)
                 S = s * (q[b, rows, h, :] @ k[b, cols, hk, :].T)
                 S = np.where(em, S, -np.inf)
                 m = S.max(axis=1)
@@ -151,7 +151,7 @@ def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, or
                     cols = _key_positions(_m.q2k_row(mask, b, hm, qb, n_qb, n_kb), bk, Sk)
                     if len(cols) == 0:
                         continue
-                    em = _m.element_mask(rows, cols, Sq, Sk, causal)
+                    em = _m.element_mask(rows, cols, Sq, Sk, causal) & _m.token_term(mask, b, hm, rows, cols)
                     qr, dor = q[b, rows, h, :], do[b, rows, h, :]
                     kc, vc = k[b, cols, hk, :], v[b, cols, hk, :]
                     P, dS = tile_grads(qr, dor, lse[b, h, rows], D[b, h, rows], kc, vc, em, s)
@@ -163,18 +163,20 @@ def attn_bwd(q, k, v, o, do, lse, mask: MaskSpec, causal: bool, scale: float, or
             for hk in range(Hk):
                 for kb in range(n_kb):
                     cols = np.arange(kb * bk, min((kb + 1) * bk, Sk))
-                    hrow, qrow = [], []
+                    hrow, qrow, mrow = [], [], []
                     for h in [h for h in range(Hq) if _m.kv_head(h, Hq, Hk) == hk and h in hset]:
                         hm = _m.mask_head(h, Hq, mask) if mask.kind == "block" else 0
                         for qb in _m.k2q_row(mask, b, hm, kb, n_qb, n_kb):
                             r = np.arange(qb * bq, min((qb + 1) * bq, Sq))
                             hrow.append(np.full(len(r), h))
+                            mrow.append(np.full(len(r), hm))
                             qrow.append(r)
                     if not qrow:
                         continue
                     hs = np.concatenate(hrow)
                     rs = np.concatenate(qrow)
-                    em = _m.element_mask(rs, cols, Sq, Sk, causal)
+                    em = _m.element_mask(rs, cols, Sq, Sk, causal) & _m.token_term(mask, b, np.concatenate(mrow),
+                                                                                   rs, cols)
                     qr, dor = q[b, rs, hs, :], do[b, rs, hs, :]
                     kc, vc = k[b, cols, hk, :], v[b, cols, hk, :]
                     P, dS = tile_grads(qr, dor, lse[b, hs, rs], D[b, hs, rs], kc, vc, em, s)

@@ -48,6 +48,23 @@ def indices_to_presence(indices, batch: int, seqlen_q: int, seqlen_k: int,
     return pres
 
 
+def indices_to_token_mask(indices, batch: int, seqlen_q: int, seqlen_k: int) -> np.ndarray:
+    """bool [B, NHK, Sq, Sk]: query i of sequence b attends key j for KV head
+    hk iff j appears in its index row (the token-exact reading; same padding
+    rules as indices_to_presence)."""
+    idx = np.asarray(indices)
+    assert idx.ndim == 3 and idx.shape[0] == batch * seqlen_q
+    nhk = idx.shape[1]
+    tok = np.zeros((batch, nhk, seqlen_q, seqlen_k), dtype=bool)
+    for b in range(batch):
+        rows = idx[b * seqlen_q:(b + 1) * seqlen_q].astype(np.int64)    # [Sq, NHK, topk]
+        valid = (rows >= 0) & (rows < seqlen_k)
+        i = np.broadcast_to(np.arange(seqlen_q)[:, None, None], rows.shape)[valid]
+        hk = np.broadcast_to(np.arange(nhk)[None, :, None], rows.shape)[valid]
+        tok[b, hk, i, rows[valid]] = True
+    return tok
+
+
 def presence_to_csr(presence):
     """(q2k_row_ptr, q2k_col, k2q_row_ptr, k2q_col), all int32.
 

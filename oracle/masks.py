@@ -21,7 +21,11 @@ Readings where the pages are silent:
 * GQA: query head h reads KV head ``h // (Hq // Hk)`` (consecutive query
   heads share a KV head).
 * inside a kept block every pair is attended (the index path is block-granular:
-  PR #334 routes index sparsity through the block-sparse machinery).
+  PR #334 routes index sparsity through the block-sparse machinery) -- unless
+  the mask carries a token mask: then a fourth term ANDs in token[b, hm, i, j],
+  query i attending exactly the keys its index row selected (the token-exact
+  reading of DSA sparsity, xtuner PR #2096 Background: each query keeps its
+  top-k key positions).
 """
 from __future__ import annotations
 
@@ -41,6 +45,7 @@ class MaskSpec:
     q2k_col: Optional[np.ndarray] = None        # int [nnz], ascending per row
     k2q_row_ptr: Optional[np.ndarray] = None    # int [B*Hm*nKB + 1]
     k2q_col: Optional[np.ndarray] = None        # int [nnz], ascending per row
+    token: Optional[np.ndarray] = None          # bool [B, Hm, Sq, Sk]: token-exact term, or None
 
 
 def dense_mask() -> MaskSpec:
@@ -48,8 +53,9 @@ def dense_mask() -> MaskSpec:
 
 
 def block_mask_from_csr(heads: int, q2k_row_ptr, q2k_col, k2q_row_ptr=None, k2q_col=None,
-                        block_q: int = 128, block_k: int = 128) -> MaskSpec:
+                        block_q: int = 128, block_k: int = 128, token=None) -> MaskSpec:
     return MaskSpec(kind="block", heads=heads, block_q=block_q, block_k=block_k,
+                    token=None if token is None else np.asarray(token, dtype=bool),
                     q2k_row_ptr=np.asarray(q2k_row_ptr, dtype=np.int64),
                     q2k_col=np.asarray(q2k_col, dtype=np.int64),
                     k2q_row_ptr=None if k2q_row_ptr is None else np.asarray(k2q_row_ptr, dtype=np.int64),
@@ -95,6 +101,18 @@ def element_mask(rows: np.ndarray, cols: np.ndarray, seqlen_q: int, seqlen_k: in
     return m
 
 
+def token_term(mask: MaskSpec, b: int, hm, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """The token-exact term for query positions ``rows`` (with mask heads
+    ``hm``, a scalar or one per row) and key positions ``cols``: all True
+    when the mask has no token mask."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    if mask.token is None:
+        return np.ones((len(rows), len(cols)), dtype=bool)
+    hm = np.broadcast_to(np.asarray(hm), rows.shape)
+    return mask.token[b, hm[:, None], rows[:, None], cols[None, :]]
+
+
 def full_mask(mask: MaskSpec, b: int, h: int, heads_q: int, seqlen_q: int, seqlen_k: int,
               causal: bool) -> np.ndarray:
     """Boolean [Sq, Sk] mask of (b, h): all three terms.  For tiny shapes and tests."""
@@ -107,4 +125,5 @@ def full_mask(mask: MaskSpec, b: int, h: int, heads_q: int, seqlen_q: int, seqle
     for qb in range(n_qb):
         for kb in q2k_row(mask, b, hm, qb, n_qb, n_kb):
             kind[qb * bq:(qb + 1) * bq, kb * bk:(kb + 1) * bk] = True
-    return kind & element_mask(np.arange(seqlen_q), np.arange(seqlen_k), seqlen_q, seqlen_k, causal)
+    r, c = np.arange(seqlen_q), np.arange(seqlen_k)
+    return kind & element_mask(r, c, seqlen_q, seqlen_k, causal) & token_term(mask, b, hm, r, c)
