@@ -65,8 +65,15 @@ enum { ISATTN_MASK_DENSE = 0, ISATTN_MASK_BLOCK_CSR = 1 };
  * block); columns ascend within a row; row_ptr[0] == 0.  LoopK reads only
  * q2k_*, LoopQ only k2q_*, SPLIT and SPLIT_DS both (and need the two forms
  * to hold the same pairs); a pair not read may be NULL.  Inside a kept block
- * every pair is attended.  block_q = block_k = 128; heads is 1, heads_k or
- * heads_q. */
+ * every pair is attended, unless token_bits is given: then pair (i, j) of a
+ * kept block is attended iff its bit is set (token-exact index sparsity: each
+ * query keeps exactly its selected keys; isattn_index_to_token_bits builds
+ * it).  token_bits: uint32 device, one slot of 1024 words per (b, hm, qb, kb)
+ * at ((b * heads + hm) * n_qb + qb) * n_kb + kb (every block, kept or not):
+ * words [0, 512) row-major -- bit j % 32 of word 4 r + j / 32 is row r, key j
+ * of the block -- and words [512, 1024) the same bits key-major -- bit r % 32
+ * of word 512 + 4 j + r / 32.  SPLIT, SPLIT_DS and the forward only.
+ * block_q = block_k = 128; heads is 1, heads_k or heads_q. */
 typedef struct isattn_mask {
     int32_t kind;
     int32_t block_q, block_k;
@@ -75,6 +82,7 @@ typedef struct isattn_mask {
     const int32_t* q2k_col;       /* [nnz] device                   */
     const int32_t* k2q_row_ptr;   /* [batch*heads*n_kb + 1] device */
     const int32_t* k2q_col;       /* [nnz] device                   */
+    const uint32_t* token_bits;   /* NULL, or [batch*heads*n_qb*n_kb][1024] device */
 } isattn_mask_t;
 
 /* Loop orders of [P1] Summary.  LOOPK: outer loop over 128-row query tiles,
@@ -242,6 +250,18 @@ isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int3
                                                     int32_t* k2q_row_ptr, int32_t* k2q_col,
                                                     int64_t col_capacity, void* workspace,
                                                     size_t workspace_bytes, void* stream);
+
+/* Token-exact bits of an index tensor (the per-block bitmaps of
+ * isattn_mask_t.token_bits, heads = nhk, 128 x 128 blocks): indices as for
+ * isattn_index_to_block_sparse, or packed sequences when cu_seqlens_q and
+ * cu_seqlens_k are given (then seqlen_q / seqlen_k are the longest lengths);
+ * bit (i, j) is set iff query i's row selects key j.  bits: uint32 device of
+ * at least bits_words = batch*nhk*ceil(seqlen_q/128)*ceil(seqlen_k/128)*1024
+ * words, fully overwritten. */
+isattn_status_t isattn_index_to_token_bits(const int32_t* indices, int32_t batch, int32_t seqlen_q,
+                                           int32_t seqlen_k, int32_t nhk, int32_t topk,
+                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                           uint32_t* bits, int64_t bits_words, void* stream);
 
 /* Bytes of device workspace isattn_block_mask_to_csr needs. */
 size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,

@@ -28,7 +28,7 @@ class Tensor(ctypes.Structure):
 class Mask(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("block_q", c_int32), ("block_k", c_int32), ("heads", c_int32),
                 ("q2k_row_ptr", c_void_p), ("q2k_col", c_void_p),
-                ("k2q_row_ptr", c_void_p), ("k2q_col", c_void_p)]
+                ("k2q_row_ptr", c_void_p), ("k2q_col", c_void_p), ("token_bits", c_void_p)]
 
 
 class Varlen(ctypes.Structure):
@@ -57,6 +57,8 @@ SIGNATURES = {
     "isattn_index_to_block_sparse": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "isattn_index_to_token_bits": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                             c_void_p, c_void_p, c_int64, c_void_p]),
     "isattn_block_mask_to_csr_workspace_bytes": (c_size_t, [c_int32] * 4),
     "isattn_block_mask_to_csr": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                            c_void_p, c_void_p, c_void_p, c_int64, c_void_p,

@@ -60,7 +60,10 @@ class BlockMask:
     """Block-sparse mask as device CSR arrays (int32), 128x128 blocks.
 
     q2k: per (batch, mask head, query block) the ascending key blocks;
-    k2q: per (batch, mask head, key block) the ascending query blocks."""
+    k2q: per (batch, mask head, key block) the ascending query blocks;
+    token_bits: optional token-exact bits (int32 [batch*heads*n_qb*n_kb*1024],
+    the layout of isattn_mask_t.token_bits): inside a kept block a pair is
+    attended only if its bit is set."""
     heads: int
     n_qb: int
     n_kb: int
@@ -70,6 +73,7 @@ class BlockMask:
     k2q_col: torch.Tensor
     block_q: int = 128
     block_k: int = 128
+    token_bits: torch.Tensor | None = None
 
     def nnz(self) -> int:
         """Number of kept blocks (reads the last row pointer: synchronises)."""
@@ -78,7 +82,8 @@ class BlockMask:
     def _abi(self) -> _abi.Mask:
         return _abi.Mask(_abi.MASK_BLOCK_CSR, self.block_q, self.block_k, self.heads,
                          self.q2k_row_ptr.data_ptr(), self.q2k_col.data_ptr(),
-                         self.k2q_row_ptr.data_ptr(), self.k2q_col.data_ptr())
+                         self.k2q_row_ptr.data_ptr(), self.k2q_col.data_ptr(),
+                         self.token_bits.data_ptr() if self.token_bits is not None else None)
 
 
 class Timer:
@@ -227,11 +232,12 @@ def _csr_buffers(rows_q, rows_k, nnz_max, device):
 
 def index_to_block_sparse(indices: torch.Tensor, batch: int, seqlen_q: int, seqlen_k: int,
                           block_q: int = 128, block_k: int = 128, stream=None, cu_seqlens_q=None,
-                          cu_seqlens_k=None) -> BlockMask:
+                          cu_seqlens_k=None, token_exact: bool = False) -> BlockMask:
     """int32 indices [batch*seqlen_q, nhk, topk] -> BlockMask with heads = nhk.
     Packed sequences: give ``cu_seqlens_q`` / ``cu_seqlens_k`` (int32 [batch
     + 1]); indices are then [total_q, nhk, topk] and seqlen_q / seqlen_k the
-    longest lengths."""
+    longest lengths.  ``token_exact``: also build the token bits, so that each
+    query attends exactly its selected keys (else every pair of a kept block)."""
     lib = _abi.load()
     if indices.dtype != torch.int32 or indices.dim() != 3 or not indices.is_contiguous():
         raise ValueError("indices must be contiguous int32 [batch*seqlen_q, nhk, topk]")
@@ -257,7 +263,17 @@ def index_to_block_sparse(indices: torch.Tensor, batch: int, seqlen_q: int, seql
         _abi.check(lib.isattn_index_to_block_sparse(
             indices.data_ptr(), batch, seqlen_q, seqlen_k, nhk, topk, block_q, block_k, *outs),
             "isattn_index_to_block_sparse")
-    return BlockMask(nhk, n_qb, n_kb, qp, qc, kp, kc, block_q, block_k)
+    bits = None
+    if token_exact:
+        if block_q != 128 or block_k != 128:
+            raise ValueError("token-exact bits use 128 x 128 blocks")
+        bits = torch.empty(max(batch * nhk * n_qb * n_kb * 1024, 4), dtype=torch.int32, device=indices.device)
+        _abi.check(lib.isattn_index_to_token_bits(
+            indices.data_ptr(), batch, seqlen_q, seqlen_k, nhk, topk,
+            cu_seqlens_q.data_ptr() if cu_seqlens_q is not None else None,
+            cu_seqlens_k.data_ptr() if cu_seqlens_k is not None else None,
+            bits.data_ptr(), bits.numel(), _stream_ptr(stream)), "isattn_index_to_token_bits")
+    return BlockMask(nhk, n_qb, n_kb, qp, qc, kp, kc, block_q, block_k, bits)
 
 
 def block_mask_to_csr(presence: torch.Tensor, block_q: int = 128, block_k: int = 128,

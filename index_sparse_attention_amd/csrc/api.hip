@@ -221,6 +221,26 @@ isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int3
                                       k2q_col, col_capacity, workspace, workspace_bytes, stream);
 }
 
+isattn_status_t isattn_index_to_token_bits(const int32_t* indices, int32_t batch, int32_t seqlen_q,
+                                           int32_t seqlen_k, int32_t nhk, int32_t topk,
+                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                           uint32_t* bits, int64_t bits_words, void* stream) {
+    if (batch < 0 || seqlen_q < 0 || seqlen_k < 0 || nhk < 0 || topk < 0) return ISATTN_ERR_SHAPE;
+    if (seqlen_q >= (1 << 30) || seqlen_k >= (1 << 30)) return ISATTN_ERR_SHAPE;
+    if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr)) return ISATTN_ERR_NULL;
+    const int32_t n_qb = cdiv(seqlen_q, kBlock), n_kb = cdiv(seqlen_k, kBlock);
+    const int64_t need = int64_t(batch) * nhk * n_qb * n_kb * 1024;
+    if (need == 0) return ISATTN_OK;
+    if (nhk > 65535 || batch > 65535) return ISATTN_ERR_SHAPE;   // grid (n_qb, nhk, batch)
+    if (bits == nullptr || (seqlen_q > 0 && topk > 0 && indices == nullptr)) return ISATTN_ERR_NULL;
+    if (bits_words < need) return ISATTN_ERR_CAPACITY;
+    if ((reinterpret_cast<uintptr_t>(bits) & 15u) != 0) return ISATTN_ERR_STRIDE_ALIGN;
+    return launch_index_token_bits(indices, cu_seqlens_q, cu_seqlens_k, batch, seqlen_q, seqlen_k, nhk, topk,
+                                   n_qb, n_kb, bits, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ISATTN_OK
+               : ISATTN_ERR_HIP;
+}
+
 size_t isattn_block_mask_to_csr_workspace_bytes(int32_t batch, int32_t heads, int32_t n_qb,
                                                 int32_t n_kb) {
     CsrPlan p{};

@@ -42,6 +42,9 @@ struct BwdArgs {
     // block CSR (mask_kind == 1)
     const int32_t* q2k_ptr; const int32_t* q2k_col;
     const int32_t* k2q_ptr; const int32_t* k2q_col;
+    // token-exact bits per (b, mask head, qb, kb) slot of 1024 words
+    // (row-major words [0, 512), key-major [512, 1024)); null: block-granular
+    const uint32_t* tok;
     // packed variable-length sequences: sequence b is tokens [cu_q[b], cu_q[b+1])
     // of the query-side tensors and [cu_k[b], cu_k[b+1]) of the key side; Sq
     // and Sk hold the longest lengths (a kernel narrows them to its sequence
@@ -65,6 +68,7 @@ struct FwdArgs {
     uint16_t* o; int64_t o_sb, o_ss, o_sh;
     float* lse;           // [B, Hq, lse_ld] natural-log LSE (+inf for a row with no kept key)
     const int32_t* q2k_ptr; const int32_t* q2k_col;   // block CSR (mask_kind == 1)
+    const uint32_t* tok;                              // token-exact bits, as in BwdArgs
     const int32_t* cu_q; const int32_t* cu_k;         // packed sequences, as in BwdArgs
     int32_t B, Sq, Sk, Hq, Hk, G, Dqk, Dv;
     int32_t Hm, n_qb, n_kb;

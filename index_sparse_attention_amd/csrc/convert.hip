@@ -253,7 +253,59 @@ __global__ __launch_bounds__(256) void k_fill(const uint8_t* __restrict__ presen
     }
 }
 
+// Token bits: every slot cleared, then one workgroup per (qb, hk, b) sets the
+// bits of its rows' selected keys in both layouts (row-major and key-major)
+// with relaxed 32-bit atomic ORs (rows of one block hit the same words).
+__global__ __launch_bounds__(256) void k_tok_clear(uint32_t* __restrict__ bits, int64_t n4) {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < n4; u += stride)
+        reinterpret_cast<u32x4_t*>(bits)[u] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+__global__ __launch_bounds__(256) void k_tok_set(const int32_t* __restrict__ idx, const int32_t* __restrict__ cu_q,
+                                                 const int32_t* __restrict__ cu_k, int32_t Sq, int32_t Sk,
+                                                 int32_t nhk, int32_t topk, int32_t n_qb, int32_t n_kb,
+                                                 uint32_t* __restrict__ bits) {
+    const int qb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    int64_t first = int64_t(b) * Sq;
+    if (cu_q != nullptr) {
+        first = cu_q[b];
+        Sq = min(max(cu_q[b + 1] - cu_q[b], 0), Sq);
+        Sk = min(max(cu_k[b + 1] - cu_k[b], 0), Sk);
+    }
+    const int r0 = qb * kBlock;
+    const int rows = max(0, min(kBlock, Sq - r0));
+    const int64_t row_stride = int64_t(nhk) * topk;
+    const int32_t* base = idx + (first + r0) * row_stride + int64_t(hk) * topk;
+    uint32_t* slots = bits + ((int64_t(b) * nhk + hk) * n_qb + qb) * int64_t(n_kb) * 1024;
+    const int total = rows * topk;
+    for (int u = threadIdx.x; u < total; u += 256) {
+        const int r = u / topk;
+        const int j = base[int64_t(r) * row_stride + (u - r * topk)];
+        if (static_cast<unsigned>(j) >= static_cast<unsigned>(Sk)) continue;   // padding
+        uint32_t* slot = slots + int64_t(j / kBlock) * 1024;
+        const int jj = j % kBlock;
+        __hip_atomic_fetch_or(slot + 4 * r + jj / 32, 1u << (jj & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(slot + 512 + 4 * jj + r / 32, 1u << (r & 31), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_index_token_bits(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                                   int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t n_qb,
+                                   int32_t n_kb, uint32_t* bits, hipStream_t s) {
+    const int64_t n4 = int64_t(B) * nhk * n_qb * n_kb * 256;
+    if (n4 == 0) return hipSuccess;
+    const int64_t nb = (n4 + 255) / 256;
+    hipLaunchKernelGGL(k_tok_clear, dim3(unsigned(nb < 16384 ? nb : 16384)), dim3(256), 0, s, bits, n4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tok_set, dim3(n_qb, nhk, B), dim3(256), 0, s, idx, cu_q, cu_k, Sq, Sk, nhk, topk, n_qb,
+                       n_kb, bits);
+    return hipGetLastError();
+}
 
 hipError_t launch_index_presence(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
                                  int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t bq, int32_t bk,

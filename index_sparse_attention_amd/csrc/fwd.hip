@@ -31,7 +31,7 @@ namespace {
 constexpr float kRescale = 8.f;   // log2 headroom of the running maximum
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool TOK>
 struct FwdCfg {
     static constexpr int BM = 128;                 // query rows per workgroup
     static constexpr int BN = 32;                  // keys per step
@@ -39,21 +39,25 @@ struct FwdCfg {
     static constexpr int NT = 64 * NW;
     static constexpr int K_BYTES = BN * DQK * 2;
     static constexpr int V_BYTES = BN * DV * 2;
-    static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+    static constexpr int TILE_BYTES = K_BYTES + V_BYTES;
+    // token-exact masks: each wave's 32 rows' bit words of the step (64 lanes x 4 B)
+    static constexpr int TK_BYTES = TOK ? NW * 256 : 0;
+    static constexpr int STAGE_BYTES = TILE_BYTES + TK_BYTES;
     static constexpr int NS = 4;                   // LDS ring stages (loads run two steps ahead)
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
     static constexpr int NKI = K_BYTES / 1024;     // 1 KiB loads per K tile
-    static constexpr int NI = STAGE_BYTES / 1024;  // 1 KiB loads per step
-    static constexpr int KMAX = NI / NW;           // loads per wave per step
+    static constexpr int NI = TILE_BYTES / 1024;   // 1 KiB loads per step
+    static constexpr int KMAX = NI / NW;           // tile loads per wave per step
+    static constexpr int NL = KMAX + (TOK ? 1 : 0);   // loads per wave per step
     static constexpr int NCQ = DQK / 16;
     static constexpr int NDT = DV / 32;            // O^T row tiles (32 columns of O each)
     static_assert(NI % NW == 0 && K_BYTES % 1024 == 0, "tiles split into whole wave loads");
-    static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
+    static_assert(NL <= NCQ, "loads must fit between the S MFMAs");
 };
 
-template <int DQK, int DV, bool VL>
+template <int DQK, int DV, bool VL, bool TOK>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
-    using C = FwdCfg<DQK, DV>;
+    using C = FwdCfg<DQK, DV, TOK>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -114,9 +118,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     struct Dma {
         uint32_t sb;
         uint32_t off[C::KMAX];
+        const uint32_t* tk;                        // token words of the step's key group (TOK)
     } d;
+    // token-exact bits: slot (b, mask head, qb, kb) row-major words; lane L
+    // loads its row's word (rows 32 w + L % 32) for the step's 32 keys
+    const uint32_t* tslots = nullptr;
+    const uint32_t tk_off = uint32_t(16 * (32 * w + l32));
+    if constexpr (TOK) tslots = a.tok + ((int64_t(b) * a.Hm + h * a.Hm / a.Hq) * a.n_qb + qb) * int64_t(a.n_kb) * 1024;
     auto plan = [&](int n0, int s) {
         d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        if constexpr (TOK) d.tk = tslots + int64_t(n0 / kBlock) * 1024 + (n0 % kBlock) / 32;
         if (n0 + C::BN <= a.Sk) {
             const uint32_t mk = uint32_t(n0) * uint32_t(a.k_ss * 2), mv = uint32_t(n0) * uint32_t(a.v_ss * 2);
 #pragma unroll
@@ -131,6 +142,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     };
     auto restage = [&](int s) { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); };
     auto fire = [&](int k) {
+        if (TOK && k == C::KMAX) {                 // this wave's rows' token words
+            dma4(d.tk, tk_off, d.sb + uint32_t(C::TILE_BYTES + 256 * w));
+            return;
+        }
         const int j = w + C::NW * k;
         const bool is_k = j < C::NKI;
         dma16(is_k ? static_cast<const void*>(gk) : static_cast<const void*>(gv), d.off[k],
@@ -142,6 +157,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     auto step = [&](int s, int n0) {
         const uint16_t* sK = lds + s * (C::STAGE_BYTES / 2);
         const uint16_t* sV = sK + C::K_BYTES / 2;
+        uint32_t tw = ~0u;
+        if constexpr (TOK) tw = *reinterpret_cast<const uint32_t*>(sK + (C::TILE_BYTES + 256 * w + 4 * l32) / 2);
         f32x16_t st = f32x16_t{};
         {
             constexpr int PF = 2;                  // K rows read this many chunks ahead
@@ -152,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             for (int c = 0; c < C::NCQ; ++c) {
                 if (c + PF < C::NCQ) ka[(c + PF) % (PF + 1)] = row_operand_swz<DQK>(sK, l32, 16 * (c + PF) + 8 * h2);
                 st = mfma32(ka[c % (PF + 1)], qB[c], st);
-                if (c < C::KMAX) fire(c);
+                if (c < C::NL) fire(c);
             }
         }
         // scores in log2 units; keys past Sk or (causal) past the row's last
@@ -164,6 +181,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             const int rel = min(a.Sk - 1, a.causal ? qrow + shift : a.Sk - 1) - n0 - 8 * h2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sv[i] = 16 * (i >> 3) + (i & 7) <= rel ? sv[i] : -__builtin_inff();
+        }
+        if constexpr (TOK) {                       // keys the row did not select
+            const uint32_t mine = tw >> (8 * h2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (((mine >> (16 * (i >> 3) + (i & 7))) & 1u) == 0) sv[i] = -__builtin_inff();
         }
         float mx = sv[0];
 #pragma unroll
@@ -202,16 +225,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
         int n0 = steps.n0;                         // step t
         plan(n0, 0);
 #pragma unroll
-        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        for (int k = 0; k < C::NL; ++k) fire(k);
         bool have1 = steps.next();                 // step t + 1
         int n1 = steps.n0;
         if (have1) plan(n1, 1);
         else restage(1);
 #pragma unroll
-        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        for (int k = 0; k < C::NL; ++k) fire(k);
         bool have2 = have1 && steps.next();        // step t + 2
         int n2 = steps.n0;
-        wait_vmcnt<C::KMAX>();                     // this wave's loads of step t landed
+        wait_vmcnt<C::NL>();                       // this wave's loads of step t landed
         __syncthreads();
         if (have2) plan(n2, 2);
         else restage(2);
@@ -222,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
             n0 = n1;
             const bool have3 = have2 && steps.next();
             const int n3 = steps.n0;
-            wait_vmcnt<C::KMAX>();
+            wait_vmcnt<C::NL>();
             __syncthreads();
             if (have3) plan(n3, (t + 2) % C::NS);
             else restage((t + 2) % C::NS);
@@ -256,23 +279,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdArgs a) {
     }
 }
 
-template <int DQK, int DV, bool VL>
+template <int DQK, int DV, bool VL, bool TOK>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-    using C = FwdCfg<DQK, DV>;
+    using C = FwdCfg<DQK, DV, TOK>;
     const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_fwd<DQK, DV, VL>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_fwd<DQK, DV, VL, TOK>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_attn_fwd<DQK, DV, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_attn_fwd<DQK, DV, VL, TOK>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
 template <int DQK, int DV>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t s) {
-    return a.cu_q != nullptr ? launch_fwd_t<DQK, DV, true>(a, s) : launch_fwd_t<DQK, DV, false>(a, s);
+    if (a.tok != nullptr)
+        return a.cu_q != nullptr ? launch_fwd_t<DQK, DV, true, true>(a, s) : launch_fwd_t<DQK, DV, false, true>(a, s);
+    return a.cu_q != nullptr ? launch_fwd_t<DQK, DV, true, false>(a, s) : launch_fwd_t<DQK, DV, false, false>(a, s);
 }
 
 }  // namespace

@@ -25,6 +25,11 @@ hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
+// Token-exact bits of the index rows (slots of 1024 words per block, see the
+// token_bits layout of the C ABI); cu_q / cu_k as below.
+hipError_t launch_index_token_bits(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,
+                                   int32_t Sq, int32_t Sk, int32_t nhk, int32_t topk, int32_t n_qb,
+                                   int32_t n_kb, uint32_t* bits, hipStream_t s);
 // Packed sequences: cu_q / cu_k (else null) give each sequence's rows and
 // length; Sq, Sk are then the longest lengths.
 hipError_t launch_index_presence(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
 // go through a 4-stage LDS ring filled by direct global->LDS loads issued two
 // steps ahead from inside the MFMA stream.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int WR>
+template <int DQK, int DV, int WR, bool TOK>
 struct DqCfg {
     static constexpr int BM = 128;                 // query rows per workgroup
     static constexpr int BN = 32;                  // keys per step
@@ -238,23 +238,28 @@ struct DqCfg {
     static constexpr int QT = WR / 32;             // 32-row query tiles per wave
     static constexpr int K_BYTES = BN * DQK * 2;
     static constexpr int V_BYTES = BN * DV * 2;
-    static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+    static constexpr int TILE_BYTES = K_BYTES + V_BYTES;
+    // token-exact masks: each wave's rows' bit words of the step (64 lanes x 4 B)
+    static constexpr int TK_BYTES = TOK ? NW * 256 : 0;
+    static constexpr int STAGE_BYTES = TILE_BYTES + TK_BYTES;
     static constexpr int NS = 4;                   // LDS ring stages (loads run two steps ahead)
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
     static constexpr int NKI = K_BYTES / 1024;     // 1 KiB loads per K tile
-    static constexpr int NI = STAGE_BYTES / 1024;  // 1 KiB loads per step
-    static constexpr int KMAX = NI / NW;           // loads per wave per step
+    static constexpr int NI = TILE_BYTES / 1024;   // 1 KiB loads per step
+    static constexpr int KMAX = NI / NW;           // tile loads per wave per step
+    static constexpr int NL = KMAX + (TOK ? 1 : 0);   // loads per wave per step
     static constexpr int NCQ = DQK / 16;
     static constexpr int NCV = DV / 16;
     static constexpr int NDT = DQK / 32;
     static_assert(NI % NW == 0 && K_BYTES % 1024 == 0, "tiles split into whole wave loads");
-    static_assert(KMAX <= NCQ, "loads must fit between the S MFMAs");
+    static_assert(NL <= NCQ, "loads must fit between the S MFMAs");
+    static_assert(!TOK || QT == 1, "token words: one query row per lane");
 };
 
-template <int DQK, int DV, int WR, bool VL>
+template <int DQK, int DV, int WR, bool VL, bool TOK>
 // two workgroups per CU (two waves per SIMD) where the registers allow
 __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(BwdArgs a) {
-    using C = DqCfg<DQK, DV, WR>;
+    using C = DqCfg<DQK, DV, WR, TOK>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -349,9 +354,16 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     struct Dma {
         uint32_t sb;
         uint32_t off[C::KMAX];
+        const uint32_t* tk;                        // token words of the step's key group (TOK)
     } d;
+    // token-exact bits: slot (b, mask head, qb, kb) row-major words; lane L
+    // loads its row's word (row wrow + L % 32) for the step's 32 keys
+    const uint32_t* tslots = nullptr;
+    const uint32_t tk_off = uint32_t(16 * (w * WR + l32));
+    if constexpr (TOK) tslots = a.tok + ((int64_t(b) * a.Hm + h * a.Hm / a.Hq) * a.n_qb + qb) * int64_t(a.n_kb) * 1024;
     auto plan = [&](int n0, int s) {
         d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
+        if constexpr (TOK) d.tk = tslots + int64_t(n0 / kBlock) * 1024 + (n0 % kBlock) / 32;
         if (n0 + C::BN <= a.Sk) {
             const uint32_t mk = uint32_t(n0) * uint32_t(a.k_ss * 2), mv = uint32_t(n0) * uint32_t(a.v_ss * 2);
 #pragma unroll
@@ -366,6 +378,10 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     };
     auto restage = [&](int s) { d.sb = lds_base + uint32_t(s * C::STAGE_BYTES); };
     auto fire = [&](int k) {
+        if (TOK && k == C::KMAX) {                 // this wave's rows' token words
+            dma4(d.tk, tk_off, d.sb + uint32_t(C::TILE_BYTES + 256 * w));
+            return;
+        }
         const int j = w + C::NW * k;
         const bool is_k = j < C::NKI;
         dma16(is_k ? static_cast<const void*>(gk) : static_cast<const void*>(gv), d.off[k],
@@ -403,8 +419,14 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
 #pragma unroll
                 for (int qt = 0; qt < C::QT; ++qt) dpt[qt] = mfma32(va[c % (PF + 1)], doB[qt][c], dpt[qt]);
             }
-            if (c < C::KMAX) fire(c);
+            if (c < C::NL) fire(c);
         }
+    };
+    // this wave's token word of the step in stage s (TOK)
+    auto tok_word = [&](int s) -> uint32_t {
+        if constexpr (TOK)
+            return *reinterpret_cast<const uint32_t*>(lds + (s * C::STAGE_BYTES + C::TILE_BYTES + 256 * w + 4 * l32) / 2);
+        return ~0u;
     };
     // P and dS of a step (packed into dsn, accumulator register i holding key
     // n0 + 16*(i/8) + 8*h2 + i%8) with, when PREV, the dQ += dS K MFMAs of the
@@ -412,7 +434,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     // arithmetic.  Masked steps clear the packed pairs afterwards.
     bf16x8_t dsp[C::QT][2];
     auto ds_step = [&](auto prev, int sp, const f32x16_t (&st)[C::QT], const f32x16_t (&dpt)[C::QT], int n0,
-                       bf16x8_t (&dsn)[C::QT][2]) {
+                       bf16x8_t (&dsn)[C::QT][2], uint32_t tw) {
         constexpr bool PREV = decltype(prev)::value;
         constexpr int NF = 2 * C::NDT;             // dQ B fragments, f = cc * NDT + dt
         constexpr int PF = NF < 3 ? NF : 3;        // prefetch depth
@@ -460,6 +482,16 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
                     }
             }
         }
+        if constexpr (TOK) {                       // keys the row did not select
+            const uint32_t mine = tw >> (8 * h2);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int o = 16 * cc + 2 * jj;
+                    pk[0][cc][jj] &= (((mine >> o) & 1u) ? 0x0000ffffu : 0u) | (((mine >> (o + 1)) & 1u) ? 0xffff0000u : 0u);
+                }
+        }
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt)
 #pragma unroll
@@ -480,23 +512,23 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         int n0 = steps.n0;                         // step t
         plan(n0, 0);
 #pragma unroll
-        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        for (int k = 0; k < C::NL; ++k) fire(k);
         bool have1 = steps.next();                 // step t + 1
         int n1 = steps.n0;
         if (have1) plan(n1, 1);
         else restage(1);
 #pragma unroll
-        for (int k = 0; k < C::KMAX; ++k) fire(k);
+        for (int k = 0; k < C::NL; ++k) fire(k);
         bool have2 = have1 && steps.next();        // step t + 2
         int n2 = steps.n0;
-        wait_vmcnt<C::KMAX>();                     // this wave's loads of step t landed
+        wait_vmcnt<C::NL>();                       // this wave's loads of step t landed
         __syncthreads();
         if (have2) plan(n2, 2);
         else restage(2);
         f32x16_t st[C::QT], dpt[C::QT];
         bf16x8_t dsn[C::QT][2];
         sdp(0, st, dpt);
-        ds_step(std::false_type{}, 0, st, dpt, n0, dsn);
+        ds_step(std::false_type{}, 0, st, dpt, n0, dsn, tok_word(0));
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt) {
             dsp[qt][0] = dsn[qt][0];
@@ -508,12 +540,12 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
             n0 = n1;
             const bool have3 = have2 && steps.next();
             const int n3 = steps.n0;
-            wait_vmcnt<C::KMAX>();
+            wait_vmcnt<C::NL>();
             __syncthreads();
             if (have3) plan(n3, (t + 2) % C::NS);
             else restage((t + 2) % C::NS);
             sdp(t % C::NS, st, dpt);
-            ds_step(std::true_type{}, (t + C::NS - 1) % C::NS, st, dpt, n0, dsn);
+            ds_step(std::true_type{}, (t + C::NS - 1) % C::NS, st, dpt, n0, dsn, tok_word(t % C::NS));
 #pragma unroll
             for (int qt = 0; qt < C::QT; ++qt) {
                 dsp[qt][0] = dsn[qt][0];
@@ -576,7 +608,11 @@ struct DkvCfg {
     static constexpr int O_OFF = Q_OFF + NS * Q_BYTES;
     static constexpr int S_OFF = O_OFF + NS * O_BYTES;
     static constexpr int X_OFF = S_OFF + NS * ST_BYTES;
-    static constexpr int LDS_BYTES = X_OFF + 2 * XBUF_BYTES;
+    // token-exact masks: each P wave's 32 keys' bit words of the step's 64
+    // rows (64 lanes x 4 B), per stage
+    static constexpr int TK_STAGE = NR * 256;
+    static constexpr int T_OFF = X_OFF + 2 * XBUF_BYTES;
+    static constexpr int LDS_BYTES = T_OFF + NS * TK_STAGE;
     static constexpr int HQ = 32 * DQK * 2;                 // bytes of 32 Q rows
     static constexpr int HO = 32 * DV * 2;
     static constexpr int NQI = Q_BYTES / 1024;              // 1 KiB loads per Q tile
@@ -598,7 +634,7 @@ struct DkvCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((NH - 1) * HQ + 48 * DQK * 2 < 65536 && (NH - 1) * HO + 48 * DV * 2 < 65536,
                   "row-group offsets fit the LDS instruction offset field");
-    static_assert(NDMA_P <= NH * NCQ && NDMA_S <= NCV, "loads must fit between the MFMAs");
+    static_assert(NDMA_P + 1 <= NH * NCQ && NDMA_S <= NCV, "loads must fit between the MFMAs");
 };
 
 // Step sequence of one workgroup: every BM-row part of every kept query
@@ -739,7 +775,8 @@ struct DkvShared {
         const uint16_t* q;
         const uint16_t* o;
         const float* st;
-        uint32_t lq, lo, ls;
+        const uint32_t* tk;                         // token words of the step (P waves, token masks)
+        uint32_t lq, lo, ls, lt;
         uint32_t off[C::KMAX];
         uint32_t soff;
     };
@@ -773,11 +810,17 @@ struct DkvShared {
     }
 
     // Plan the loads of the steps' current step into stage s.
+    template <bool TOK>
     __device__ void plan(Dma& d, const DkvSteps<C::BM>& st, int s) const {
         const int m = st.m;
         restage(d, s);
         d.q = st.qh;
         d.o = st.oh;
+        if constexpr (TOK) {                        // key-major words of slot (b, mask head, qb, kb), rows m..m+63
+            const int h = st.hq();
+            d.tk = a.tok + ((int64_t(b) * a.Hm + h * a.Hm / a.Hq) * a.n_qb + m / kBlock) * int64_t(a.n_kb) * 1024 +
+                   int64_t(n_base / kBlock) * 1024 + 512 + (m % kBlock) / 32;
+        }
         d.st = (w & 1) == 0 ? st.lh : st.dh;
         d.soff = soff + uint32_t(4 * m);
         if (m + C::BM <= a.Sq) {
@@ -799,18 +842,24 @@ struct DkvShared {
         d.lq = lds_base + uint32_t(C::Q_OFF + s * C::Q_BYTES);
         d.lo = lds_base + uint32_t(C::O_OFF + s * C::O_BYTES);
         d.ls = lds_base + uint32_t(C::S_OFF + s * C::ST_BYTES);
+        d.lt = lds_base + uint32_t(C::T_OFF + s * C::TK_STAGE);
     }
 
     // Load k of this wave (k < KMAX: tile part; k == KMAX: the step's 64
     // statistics values, by the P waves or the dS waves -- lse2 by even
     // waves, delta by odd ones).
+    // With token masks a P wave's last load (k == KMAX + 1 where the P waves
+    // load the statistics, else KMAX) is its keys' token words: lane L takes
+    // word L / 32 of key 32 w + L % 32.
     __device__ void fire(const Dma& d, int k) const {
         if (k < C::KMAX) {
             const int j = load_index(w, k);
             const bool is_q = j < C::NQI;
             dma16(is_q ? d.q : d.o, d.off[k], is_q ? d.lq + uint32_t(1024 * j) : d.lo + uint32_t(1024 * (j - C::NQI)));
-        } else {
+        } else if (k == C::KMAX && (C::P_LOADS || w >= C::NR)) {
             dma4(d.st, d.soff, d.ls + uint32_t((w & 1) * 256));
+        } else {
+            dma4(d.tk, uint32_t(4 * (4 * (32 * w + l32) + h2)), d.lt + uint32_t(256 * w));
         }
     }
 };
@@ -818,10 +867,12 @@ struct DkvShared {
 // P wave: S, P, dV for 32 keys.  Reads: Q rows of the step's stage (S),
 // dO^T of the previous step's stage (dV), lse2 of the step; writes P to the
 // step's P buffer.
-template <int DQK, int DV>
+template <int DQK, int DV, bool TOK>
 struct DkvPWave {
     static constexpr bool kLoads = true;            // issues the step's tile and statistics loads
+    static constexpr bool kTok = TOK;               // and its keys' token words
     using C = DkvCfg<DQK, DV>;
+    static constexpr int NDMA = C::NDMA_P + (TOK ? 1 : 0);
     using Dma = typename DkvShared<DQK, DV>::Dma;
     static constexpr int NF = 2 * C::NDV;           // dO^T fragments (cc, j) of one half
     const DkvShared<DQK, DV>& sh;
@@ -837,6 +888,7 @@ struct DkvPWave {
     const lds_char* ot_at[C::NDV][2];
     const lds_char* l_at;
     const lds_char* x_at;
+    const lds_char* t_at;                           // token words of this lane's key at stage qs (TOK)
     RingPos<C::NS> qs{0}, os{C::NS - 1};
     int par = 0;
 
@@ -859,11 +911,13 @@ struct DkvPWave {
             for (int hi = 0; hi < 2; ++hi) ot_at[j][hi] = o0 + tr_read_off<DV>(sh.lane, j, hi);
         l_at = sh.lp + C::S_OFF + 16 * sh.h2;
         x_at = sh.lp + C::X_OFF + wr * C::NH * 2 * 1024 + 16 * sh.lane;
+        t_at = sh.lp + C::T_OFF + wr * 256 + 4 * sh.l32;
     }
 
     // next step: every read moves one stage on, the P buffer flips
     __device__ void advance() {
         const int kq = qs.advance(), ko = os.advance();
+        t_at += kq * C::TK_STAGE;
 #pragma unroll
         for (int c = 0; c < C::NCQ; ++c) qa_at[c] += kq * C::Q_BYTES;
 #pragma unroll
@@ -913,7 +967,7 @@ struct DkvPWave {
                 for (int c = 0; c < C::NCQ; ++c) {
                     st = mfma32(qa[c % PF], kB[c], st);
                     if (c + PF < C::NCQ) qa[c % PF] = q_row(hh, c + PF);
-                    if (hh * C::NCQ + c < C::NDMA_P) sh.fire(d, hh * C::NCQ + c);
+                    if (hh * C::NCQ + c < NDMA) sh.fire(d, hh * C::NCQ + c);
                 }
             }
             f32x4_t l4[4];
@@ -950,8 +1004,14 @@ struct DkvPWave {
             }
         }
         if (mask) {
-            // pairs whose row is below the lane key's first visible row (causal)
-            // or whose key is past Sk: clear the bf16 halves and rewrite
+            // pairs whose row is below the lane key's first visible row (causal),
+            // whose key is past Sk, or (token masks) whose row did not select the
+            // key: clear the bf16 halves and rewrite
+            uint32_t tw[C::NH] = {~0u, ~0u};
+            if constexpr (TOK) {
+                tw[0] = *(const __attribute__((address_space(3))) uint32_t*)(t_at) >> (8 * sh.h2);
+                tw[1] = *(const __attribute__((address_space(3))) uint32_t*)(t_at + 128) >> (8 * sh.h2);
+            }
 #pragma unroll
             for (int hh = 0; hh < C::NH; ++hh) {
                 const int tau = qmin - m - 32 * hh - 8 * sh.h2;   // first visible row offset of this lane
@@ -960,7 +1020,9 @@ struct DkvPWave {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int o = 16 * cc + 2 * jj;
-                        const uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
+                        uint32_t keep = (o >= tau ? 0x0000ffffu : 0u) | (o + 1 >= tau ? 0xffff0000u : 0u);
+                        if constexpr (TOK)
+                            keep &= (((tw[hh] >> o) & 1u) ? 0x0000ffffu : 0u) | (((tw[hh] >> (o + 1)) & 1u) ? 0xffff0000u : 0u);
                         pn[hh][cc][jj] &= keep;
                     }
                     lds_st128(x_at + (hh * 2 + cc) * 1024, pn[hh][cc]);
@@ -978,7 +1040,7 @@ struct DkvPWave {
     __device__ void step(int m, bool mask, const Dma& d, int64_t) { body<true>(m, mask, d); }
     __device__ void fire_all(const Dma& d) const {
 #pragma unroll
-        for (int k = 0; k < C::NDMA_P; ++k) sh.fire(d, k);
+        for (int k = 0; k < NDMA; ++k) sh.fire(d, k);
     }
     // dV update of the last step (its dO^T reads at the stage advance() moved to)
     __device__ void drain() {
@@ -1015,6 +1077,7 @@ struct DkvPWave {
 template <int DQK, int DV, bool DS>
 struct DkvSWave {
     static constexpr bool kLoads = DkvCfg<DQK, DV>::NDMA_S > 0;
+    static constexpr bool kTok = false;
     using C = DkvCfg<DQK, DV>;
     using Dma = typename DkvShared<DQK, DV>::Dma;
     const DkvShared<DQK, DV>& sh;
@@ -1302,18 +1365,20 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     const bool ragged_keys = sh.n_base + C::BN > a.Sk;
     const int shift = a.Sk - a.Sq;
     // some pair of step m is masked (rows past Sq need no mask: their lse2 is +inf)
-    auto need_mask = [&](int m) { return ragged_keys || (a.causal && sh.n_base + C::BN - 1 > m + shift); };
+    auto need_mask = [&](int m) {
+        return Role::kTok || ragged_keys || (a.causal && sh.n_base + C::BN - 1 > m + shift);
+    };
     if (!steps.start()) return;
     typename DkvShared<DQK, DV>::Dma d;
     int m = steps.m;                                // step t
     int64_t dso = steps.ds_off();
-    sh.plan(d, steps, 0);
+    sh.template plan<Role::kTok>(d, steps, 0);
     role.fire_all(d);
     bool have1 = steps.next();                      // step t + 1
     int m1 = steps.m;
     int64_t dso1 = steps.ds_off();
     step_barrier<Role::kLoads>();
-    if (have1) sh.plan(d, steps, 1);
+    if (have1) sh.template plan<Role::kTok>(d, steps, 1);
     else sh.restage(d, 1);
     role.first(m, need_mask(m), d, dso);
     int t = 0;
@@ -1325,7 +1390,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
         const int m2 = steps.m;
         const int64_t dso2 = steps.ds_off();
         step_barrier<Role::kLoads>();               // the loads of step t landed
-        if (have2) sh.plan(d, steps, (t + 1) % C::NS);
+        if (have2) sh.template plan<Role::kTok>(d, steps, (t + 1) % C::NS);
         else sh.restage(d, (t + 1) % C::NS);
         role.advance();
         role.step(m, need_mask(m), d, dso);
@@ -1338,7 +1403,7 @@ __device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<
     role.drain();
 }
 
-template <int DQK, int DV, bool DS, bool VL>
+template <int DQK, int DV, bool DS, bool VL, bool TOK>
 __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     using C = DkvCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -1377,7 +1442,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     steps.lo = lo;
     steps.hi = hi;
     if (w < C::NR) {
-        DkvPWave<DQK, DV> role(sh, w);
+        DkvPWave<DQK, DV, TOK> role(sh, w);
         dkdv_run<DQK, DV>(sh, steps, role);
         role.store(partial);
     } else {
@@ -1387,17 +1452,17 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
     }
 }
 
-template <int DQK, int DV, int WR, bool VL>
+template <int DQK, int DV, int WR, bool VL, bool TOK>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
-    using C = DqCfg<DQK, DV, WR>;
+    using C = DqCfg<DQK, DV, WR, TOK>;
     const int64_t items = int64_t(a.n_qb) * a.B * a.Hq;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq<DQK, DV, WR, VL>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dq<DQK, DV, WR, VL, TOK>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_bwd_dq<DQK, DV, WR, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dq<DQK, DV, WR, VL, TOK>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
@@ -1434,38 +1499,45 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
     }
 }
 
-template <int DQK, int DV, bool DS, bool VL>
+template <int DQK, int DV, bool DS, bool VL, bool TOK>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
     using C = DkvCfg<DQK, DV>;
     const int64_t items = int64_t(a.n_kb) * a.B * a.Hk;
     if (items == 0) return hipSuccess;
     const int64_t grid = int64_t(kXcds) * xcd_items_per(int(items));
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV, DS, VL>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bwd_dkdv<DQK, DV, DS, VL, TOK>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     if (a.kv_parts_T > 0) {                        // part mode: one workgroup per unit, then the reduction
-        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
+        hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL, TOK>), dim3(unsigned(a.kv_units_bound)), dim3(C::NT), C::LDS_BYTES, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((k_dkdv_reduce<DQK, DV>), dim3(unsigned(items * (kBlock / 8))), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((k_bwd_dkdv<DQK, DV, DS, VL, TOK>), dim3(unsigned(grid)), dim3(C::NT), C::LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+template <int DQK, int DV, bool TOK>
+hipError_t launch_dkdv_v(const BwdArgs& a, hipStream_t s) {
+    const bool ds = a.ds != nullptr;               // SPLIT_DS: also store dS
+    if (a.cu_q != nullptr)                         // packed sequences
+        return ds ? launch_dkdv_t<DQK, DV, true, true, TOK>(a, s) : launch_dkdv_t<DQK, DV, false, true, TOK>(a, s);
+    return ds ? launch_dkdv_t<DQK, DV, true, false, TOK>(a, s) : launch_dkdv_t<DQK, DV, false, false, TOK>(a, s);
 }
 
 template <int DQK, int DV>
 hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t s) {
-    const bool ds = a.ds != nullptr;               // SPLIT_DS: also store dS
-    if (a.cu_q != nullptr)                         // packed sequences
-        return ds ? launch_dkdv_t<DQK, DV, true, true>(a, s) : launch_dkdv_t<DQK, DV, false, true>(a, s);
-    return ds ? launch_dkdv_t<DQK, DV, true, false>(a, s) : launch_dkdv_t<DQK, DV, false, false>(a, s);
+    return a.tok != nullptr ? launch_dkdv_v<DQK, DV, true>(a, s) : launch_dkdv_v<DQK, DV, false>(a, s);
 }
 
 template <int DQK, int DV, int WR>
 hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
-    return a.cu_q != nullptr ? launch_dq_t<DQK, DV, WR, true>(a, s) : launch_dq_t<DQK, DV, WR, false>(a, s);
+    if (a.tok != nullptr)
+        return a.cu_q != nullptr ? launch_dq_t<DQK, DV, WR, true, true>(a, s) : launch_dq_t<DQK, DV, WR, false, true>(a, s);
+    return a.cu_q != nullptr ? launch_dq_t<DQK, DV, WR, true, false>(a, s) : launch_dq_t<DQK, DV, WR, false, false>(a, s);
 }
 
 }  // namespace

@@ -177,6 +177,12 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         a.q2k_col = mask->q2k_col;
         a.k2q_ptr = mask->k2q_row_ptr;
         a.k2q_col = mask->k2q_col;
+        if (mask->token_bits != nullptr) {
+            // token-exact masks: the two-pass algorithms only
+            if (algo != ISATTN_ALGO_SPLIT && algo != ISATTN_ALGO_SPLIT_DS) return ISATTN_ERR_UNSUPPORTED;
+            if ((reinterpret_cast<uintptr_t>(mask->token_bits) & 15u) != 0) return ISATTN_ERR_STRIDE_ALIGN;
+            a.tok = mask->token_bits;
+        }
     }
 
     if (varlen != nullptr) {
@@ -299,6 +305,10 @@ isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t*
         a.Hm = mask->heads;
         a.q2k_ptr = mask->q2k_row_ptr;
         a.q2k_col = mask->q2k_col;
+        if (mask->token_bits != nullptr) {
+            if ((reinterpret_cast<uintptr_t>(mask->token_bits) & 15u) != 0) return ISATTN_ERR_STRIDE_ALIGN;
+            a.tok = mask->token_bits;
+        }
     }
     if (varlen != nullptr) {
         if (s.batch > 0 && (varlen->cu_seqlens_q == nullptr || varlen->cu_seqlens_k == nullptr))

@@ -63,6 +63,7 @@ class Case:
     topk: int = 64
     seed: int = 0
     heads: list | None = None    # query heads with real O/LSE (others: LSE = +inf)
+    token: bool = False          # index masks: token-exact (each query attends only its selected keys)
     data: dict = field(default_factory=dict)
 
     @property
@@ -71,7 +72,7 @@ class Case:
 
     def label(self):
         return (f"B{self.B} Sq{self.Sq} Sk{self.Sk} Hq{self.Hq} Hk{self.Hk} D{self.Dqk}/{self.Dv} "
-                f"{'causal ' if self.causal else ''}{self.mask} seed{self.seed}")
+                f"{'causal ' if self.causal else ''}{self.mask}{' token' if self.token else ''} seed{self.seed}")
 
 
 def build_case(c: Case) -> Case:
@@ -92,7 +93,8 @@ def build_case(c: Case) -> Case:
         d["indices"] = synth.topk_indices(g[5], c.B, c.Sq, c.Sk, c.Hk, c.topk, causal=True)
         d["presence"] = oracle.indices_to_presence(d["indices"], c.B, c.Sq, c.Sk)
         d["csr"] = oracle.presence_to_csr(d["presence"])
-        d["omask"] = oracle.block_mask_from_csr(c.Hk, *d["csr"])
+        tok = oracle.indices_to_token_mask(d["indices"], c.B, c.Sq, c.Sk) if c.token else None
+        d["omask"] = oracle.block_mask_from_csr(c.Hk, *d["csr"], token=tok)
     else:
         d["omask"] = oracle.dense_mask()
     f = {k: oracle.bf16_to_f64(d[k]) for k in ("q", "k", "v", "do")}
@@ -117,7 +119,7 @@ def gpu_mask(c: Case):
     if c.mask == "block":
         return isa.block_mask_to_csr(torch.from_numpy(d["presence"]).cuda())
     if c.mask == "index":
-        return isa.index_to_block_sparse(torch.from_numpy(d["indices"]).cuda(), c.B, c.Sq, c.Sk)
+        return isa.index_to_block_sparse(torch.from_numpy(d["indices"]).cuda(), c.B, c.Sq, c.Sk, token_exact=c.token)
     return None
 
 

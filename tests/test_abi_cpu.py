@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
@@ -231,3 +231,21 @@ def test_varlen_validation_errors(lib):
                                                    FAKE, FAKE, 8, FAKE, wsb, None) == NULL
     assert lib.isattn_index_to_block_sparse_varlen(FAKE, 1, FAKE, FAKE, 256, 256, 2, 64, 128, 128, FAKE, FAKE,
                                                    FAKE, FAKE, 3, FAKE, wsb, None) == CAP
+
+
+def test_token_bits_validation_errors(lib):
+    """Token-exact masks: the two-pass algorithms only, 16-byte aligned bits;
+    the bits converter checks its buffer, pointers and sizes."""
+    tok = lambda p: _abi.Mask(1, 128, 128, 2, FAKE, FAKE, FAKE, FAKE, p)
+    for algo in (0, 1):
+        c = Call(lib, algo=algo); c.mask = tok(FAKE); assert c() == UNSUP
+    c = Call(lib, algo=2); c.mask = tok(FAKE + 4); assert c() == STRIDE
+    need = 1 * 2 * 2 * 2 * 1024
+    call = lambda idx=FAKE, bits=FAKE, words=need, cq=None, ck=None, B=1: lib.isattn_index_to_token_bits(
+        idx, B, 256, 256, 2, 64, cq, ck, bits, words, None)
+    assert call(words=need - 1) == CAP
+    assert call(bits=None) == NULL
+    assert call(idx=None) == NULL
+    assert call(cq=FAKE) == NULL
+    assert call(B=-1) == SHAPE
+    assert call(bits=FAKE + 4) == STRIDE
