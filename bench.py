@@ -17,6 +17,8 @@ mask, run once before timing.
 Printed on stdout: one JSON line.  Progress goes to stderr.  Besides the
 contract fields it carries the per-step median / min / P90, the mask
 conversion alone as GB/s (`converter`), the forward alone (`forward`), the
+index producer alone (`indexer_topk`: top-k of a 16K packed-causal score
+matrix), the
 pre/postprocess GB/s, the main kernels' TFLOP/s and, unless --no-compare, the
 other algorithms' step times.
 """
@@ -310,6 +312,30 @@ def main():
         return {"ms": round(ms, 4), "bytes_read": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "what": "presence -> CSR" if w.mask == "block" else "indices -> presence -> CSR"}
 
+    def time_topk(pack=16384, nseq=4, k=2048, reps=5):
+        """The index producer alone (not part of the backward step): top-k of a
+        packed-causal fp32 score matrix (pack x pack, nseq sequences, each row
+        limited to its causal range in its sequence), k positions per row."""
+        g = torch.Generator(device=dev).manual_seed(7)
+        x = torch.randn(pack, pack, device=dev, dtype=torch.float32, generator=g)
+        seg = pack // nseq
+        st = torch.tensor(np.repeat(np.arange(nseq) * seg, seg), dtype=torch.int32, device=dev)
+        en = torch.tensor(np.concatenate([np.arange(seg) + 1 + i * seg for i in range(nseq)]), dtype=torch.int32,
+                          device=dev)
+        out = isa.topk_select(x, k, st, en)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            isa.topk_select(x, k, st, en, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        valid = int((en - st).sum().item())
+        del x
+        return {"ms": round(ms, 4), "pack": pack, "sequences": nseq, "topk": k,
+                "valid_score_gbs": round(valid * 4 / (ms * 1e-3) / 1e9, 1)}
+
     log(f"timing {args.algo}: {args.warmup} warmup + {args.steps} steps")
     r = run(args.algo, args.steps, args.warmup)
     pairs = kept * 128 * 128
@@ -352,6 +378,7 @@ def main():
         "step_ms": {k: round(v, 4) for k, v in r["step_ms"].items()},
         "converter": time_converter(),
         "forward": time_forward(),
+        "indexer_topk": time_topk(),
     }
     rows_q = w.batch * w.seqlen_q * w.heads_q
     rows_k = w.batch * w.seqlen_k * w.heads_k

@@ -251,6 +251,18 @@ isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int3
                                                     int64_t col_capacity, void* workspace,
                                                     size_t workspace_bytes, void* stream);
 
+/* Top-k selection (the indexer step before the converter; xtuner PR #2096,
+ * Main Changes item 1).  scores: fp32 device [rows, ld] (row r at scores +
+ * r * ld, ld >= n); starts / ends: int32 device [rows] -- row r selects
+ * among positions [starts[r], ends[r]) clipped to [0, n) -- or both NULL for
+ * whole rows.  out: int32 device [rows, topk]: the selected positions ordered
+ * by score, highest first (equal scores: smaller position first), then -1
+ * where the row has fewer valid positions than topk.  0 <= topk <= 8192.
+ * Scores must not be NaN. */
+isattn_status_t isattn_topk_select(const float* scores, int64_t ld, int32_t rows, int32_t n,
+                                   const int32_t* starts, const int32_t* ends, int32_t topk,
+                                   int32_t* out, void* stream);
+
 /* Token-exact bits of an index tensor (the per-block bitmaps of
  * isattn_mask_t.token_bits, heads = nhk, 128 x 128 blocks): indices as for
  * isattn_index_to_block_sparse, or packed sequences when cu_seqlens_q and

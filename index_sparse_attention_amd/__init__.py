@@ -7,6 +7,7 @@ Entry points (thin wrappers over the C ABI in include/isattn.h):
                                GQA, 128x128 block-sparse); SPLIT, LoopK or LoopQ.
 * ``index_to_block_sparse`` -- int32 top-k token indices -> BlockMask (CSR).
 * ``block_mask_to_csr``     -- uint8 block presence -> BlockMask (CSR).
+* ``topk_select``           -- fp32 score rows -> int32 top-k positions.
 """
 from ._abi import LibraryMissing, IsattnError, load as load_library  # noqa: F401
 from .api import (  # noqa: F401
@@ -17,6 +18,7 @@ from .api import (  # noqa: F401
     attn_bwd_workspace_bytes,
     block_mask_to_csr,
     index_to_block_sparse,
+    topk_select,
 )
 
 __version__ = "0.1.0"

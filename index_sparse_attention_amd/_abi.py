@@ -57,6 +57,8 @@ SIGNATURES = {
     "isattn_index_to_block_sparse": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_void_p, c_int64, c_void_p, c_size_t, c_void_p]),
+    "isattn_topk_select": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                                     c_void_p]),
     "isattn_index_to_token_bits": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                              c_void_p, c_void_p, c_int64, c_void_p]),
     "isattn_block_mask_to_csr_workspace_bytes": (c_size_t, [c_int32] * 4),

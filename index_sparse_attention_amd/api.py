@@ -224,6 +224,30 @@ def attn_fwd(q, k, v, mask: BlockMask | None = None, causal: bool = False, softm
     return o, lse
 
 
+def topk_select(scores: torch.Tensor, topk: int, starts: torch.Tensor | None = None,
+                ends: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Top-k positions of each fp32 score row (GPU): int32 [rows, topk],
+    highest score first (ties: smaller position first), -1 padded.  Rows may
+    be limited to [starts[r], ends[r]) (int32 [rows] each)."""
+    lib = _abi.load()
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1 or not scores.is_cuda:
+        raise ValueError("scores must be a float32 GPU tensor [rows, n] with contiguous rows")
+    rows, n = scores.shape
+    if (starts is None) != (ends is None):
+        raise ValueError("give both starts and ends, or neither")
+    for t in (starts, ends):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != rows or not t.is_contiguous() or not t.is_cuda):
+            raise ValueError("starts / ends must be contiguous int32 GPU tensors [rows]")
+    out = torch.empty((rows, topk), dtype=torch.int32, device=scores.device) if out is None else out
+    if out.dtype != torch.int32 or tuple(out.shape) != (rows, topk) or not out.is_contiguous():
+        raise ValueError("out must be contiguous int32 [rows, topk]")
+    _abi.check(lib.isattn_topk_select(scores.data_ptr(), scores.stride(0), rows, n,
+                                      starts.data_ptr() if starts is not None else None,
+                                      ends.data_ptr() if ends is not None else None, topk, out.data_ptr(),
+                                      _stream_ptr(stream)), "isattn_topk_select")
+    return out
+
+
 def _csr_buffers(rows_q, rows_k, nnz_max, device):
     i32 = dict(dtype=torch.int32, device=device)
     return (torch.empty(rows_q + 1, **i32), torch.empty(max(nnz_max, 1), **i32),

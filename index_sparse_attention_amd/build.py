@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libisattn.so")
 
-HIP_SOURCES = ["api.hip", "convert.hip", "prepost.hip", "loopk.hip", "loopq.hip", "split.hip", "split_ds.hip", "fwd.hip"]
+HIP_SOURCES = ["api.hip", "convert.hip", "prepost.hip", "loopk.hip", "loopq.hip", "split.hip", "split_ds.hip", "fwd.hip", "topk.hip"]
 CPP_SOURCES = ["validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -221,6 +221,19 @@ isattn_status_t isattn_index_to_block_sparse_varlen(const int32_t* indices, int3
                                       k2q_col, col_capacity, workspace, workspace_bytes, stream);
 }
 
+isattn_status_t isattn_topk_select(const float* scores, int64_t ld, int32_t rows, int32_t n,
+                                   const int32_t* starts, const int32_t* ends, int32_t topk,
+                                   int32_t* out, void* stream) {
+    if (rows < 0 || n < 0 || topk < 0 || ld < n) return ISATTN_ERR_SHAPE;
+    if (topk > 8192) return ISATTN_ERR_UNSUPPORTED;
+    if ((starts == nullptr) != (ends == nullptr)) return ISATTN_ERR_NULL;
+    if (rows == 0 || topk == 0) return ISATTN_OK;
+    if (out == nullptr || (n > 0 && scores == nullptr)) return ISATTN_ERR_NULL;
+    return launch_topk(scores, ld, rows, n, starts, ends, topk, out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ISATTN_OK
+               : ISATTN_ERR_HIP;
+}
+
 isattn_status_t isattn_index_to_token_bits(const int32_t* indices, int32_t batch, int32_t seqlen_q,
                                            int32_t seqlen_k, int32_t nhk, int32_t topk,
                                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

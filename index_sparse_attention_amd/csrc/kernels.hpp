@@ -25,6 +25,10 @@ hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
+// Top-k positions per score row within [starts[r], ends[r]) (full rows when
+// null), ordered by score (ties: smaller position first), -1 padded.
+hipError_t launch_topk(const float* scores, int64_t ld, int32_t rows, int32_t n, const int32_t* starts,
+                       const int32_t* ends, int32_t topk, int32_t* out, hipStream_t s);
 // Token-exact bits of the index rows (slots of 1024 words per block, see the
 // token_bits layout of the C ABI); cu_q / cu_k as below.
 hipError_t launch_index_token_bits(const int32_t* idx, const int32_t* cu_q, const int32_t* cu_k, int32_t B,

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
