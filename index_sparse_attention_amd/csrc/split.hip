@@ -1114,6 +1114,11 @@ struct DkvSWave {
         const uint16_t* vr = a.v + sh.b * a.v_sb + sh.hk * a.v_sh + int64_t(in ? key : 0) * a.v_ss + 8 * sh.h2;
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) vB[c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
+        // the V rows land before the step loop: a wave that issues no loads in
+        // the loop (but may store dS) then never waits on the memory counter
+        // inside it (the compiler would otherwise guard the first use of vB in
+        // the loop body, and that wait would also cover the dS stores)
+        wait_vmcnt<0>();
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) dk[j] = f32x16_t{};
         const lds_char* o0 = sh.lp + C::O_OFF + (C::NS - 1) * C::O_BYTES;
