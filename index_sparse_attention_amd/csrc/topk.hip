@@ -13,8 +13,11 @@
 //      and how many keys equal to T are still needed are known;
 //   3. one collection pass takes every key > T and, in position order, the
 //      first keys equal to T (ties resolve to the smaller position);
-//   4. a bitonic sort in LDS orders the selection by (key descending,
-//      position ascending) and the row is written, padded with -1.
+//   4. a bitonic sort orders the selection by (key descending, position
+//      ascending) and the row is written, padded with -1.  The sort keeps
+//      E = CAP / 512 entries per thread in registers: exchanges between a
+//      thread's own entries happen in registers, exchanges within a wave by
+//      lane shuffles, and only partners in other waves go through LDS.
 // Rows with no more valid positions than topk skip the radix passes.  The
 // row is re-read from global memory by every pass (L2-resident after the
 // first); scores are only read, never modified.
@@ -51,11 +54,75 @@ __device__ __forceinline__ int block_rank(bool flag, int* wcnt, int* total) {
     return before + __popcll(m & ((uint64_t(1) << lane) - 1));
 }
 
+// one compare-exchange result: the entry this side keeps
+__device__ __forceinline__ uint64_t bitonic_keep(uint64_t mine, uint64_t other, bool lower, bool desc) {
+    const bool take_max = lower == desc;
+    return take_max ? (mine > other ? mine : other) : (mine < other ? mine : other);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), m, 64));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), m, 64));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+// Sort the first `size` (a power of two, at most 512 E) entries of sel
+// descending; returns with thread t holding entries t E .. t E + E - 1 of the
+// sorted order in v (entries past `size` stay in place: the network never
+// pairs them with the first `size`).
+template <int E>
+__device__ __forceinline__ void bitonic_sort(uint64_t* sel, uint64_t (&v)[E], int size) {
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = sel[t * E + e];
+    for (int k = 2; k <= size; k <<= 1) {
+        // partners in other threads (j >= E), largest distance first
+        for (int j = k >> 1; j >= E; j >>= 1) {
+            if (j < 64 * E) {                               // partner in another lane of this wave
+                const int m = j / E;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = t * E + e;
+                    v[e] = bitonic_keep(v[e], shfl_xor64(v[e], m), (lane & m) == 0, (i & k) == 0);
+                }
+            } else {                                        // partner in another wave: through LDS
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e) sel[t * E + e] = v[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = t * E + e;
+                    v[e] = bitonic_keep(v[e], sel[i ^ j], (i & j) == 0, (i & k) == 0);
+                }
+            }
+        }
+        // partners in this thread's registers (j < E): compile-time indices
+#pragma unroll
+        for (int j = E / 2; j > 0; j >>= 1) {
+            if (j < k) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if ((e & j) == 0) {
+                        const bool desc = ((t * E + e) & k) == 0;
+                        const uint64_t a = v[e], b = v[e | j];
+                        v[e] = bitonic_keep(a, b, true, desc);
+                        v[e | j] = bitonic_keep(b, a, false, desc);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int E>
 __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ scores, int64_t ld, int32_t n,
                                                        const int32_t* __restrict__ starts,
                                                        const int32_t* __restrict__ ends, int32_t topk,
-                                                       int32_t cap, int32_t* __restrict__ out) {
-    extern __shared__ uint64_t sel[];                 // cap (key << 32 | ~position) entries
+                                                       int32_t* __restrict__ out) {
+    constexpr int CAP = kTopkThreads * E;
+    extern __shared__ uint64_t sel[];                 // CAP (key << 32 | ~position) entries
     __shared__ int hist[256];
     __shared__ int wcnt[kTopkThreads / 64];
     __shared__ int s_digit, s_above;
@@ -155,32 +222,34 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
             eq_seen += n_eq;
         }
     }
-    // pad to the sort size (the selection's power of two, at most cap) with
-    // entries that sort last
+    // pad to the sort size with entries that sort last (a real entry is
+    // never 0: its low word is a bit-inverted position below 2^31)
+    for (int i = take + tid; i < CAP; i += kTopkThreads) sel[i] = 0;
+    __syncthreads();
     int size = 1;
     while (size < take) size <<= 1;
-    for (int i = take + tid; i < size; i += kTopkThreads) sel[i] = 0;
-    __syncthreads();
-
-    // bitonic sort, descending
-    for (int k = 2; k <= size; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < size; i += kTopkThreads) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const uint64_t a = sel[i], b = sel[p];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? a < b : a > b) {
-                        sel[i] = b;
-                        sel[p] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    uint64_t v[E];
+    bitonic_sort<E>(sel, v, size);
     int32_t* o = out + row * int64_t(topk);
-    for (int i = tid; i < topk; i += kTopkThreads) o[i] = i < take ? int32_t(~uint32_t(sel[i])) : -1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = tid * E + e;
+        if (i < topk) o[i] = i < take ? int32_t(~uint32_t(v[e])) : -1;
+    }
+}
+
+template <int E>
+hipError_t launch_topk_e(const float* scores, int64_t ld, int32_t rows, int32_t n, const int32_t* starts,
+                         const int32_t* ends, int32_t topk, int32_t* out, hipStream_t s) {
+    const size_t lds = size_t(kTopkThreads) * E * sizeof(uint64_t);
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk<E>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_topk<E>, dim3(unsigned(rows)), dim3(kTopkThreads), lds, s, scores, ld, n, starts, ends,
+                       topk, out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -188,17 +257,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 hipError_t launch_topk(const float* scores, int64_t ld, int32_t rows, int32_t n, const int32_t* starts,
                        const int32_t* ends, int32_t topk, int32_t* out, hipStream_t s) {
     if (rows == 0 || topk == 0) return hipSuccess;
-    int cap = 1;
-    while (cap < topk) cap <<= 1;
-    const size_t lds = size_t(cap) * sizeof(uint64_t);
-    if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k_topk, dim3(unsigned(rows)), dim3(kTopkThreads), lds, s, scores, ld, n, starts, ends, topk,
-                       cap, out);
-    return hipGetLastError();
+    // sort size: 512 x E entries, E the smallest power of two with 512 E >= topk
+    if (topk <= 512) return launch_topk_e<1>(scores, ld, rows, n, starts, ends, topk, out, s);
+    if (topk <= 1024) return launch_topk_e<2>(scores, ld, rows, n, starts, ends, topk, out, s);
+    if (topk <= 2048) return launch_topk_e<4>(scores, ld, rows, n, starts, ends, topk, out, s);
+    if (topk <= 4096) return launch_topk_e<8>(scores, ld, rows, n, starts, ends, topk, out, s);
+    return launch_topk_e<16>(scores, ld, rows, n, starts, ends, topk, out, s);
 }
 
 }  // namespace isattn
