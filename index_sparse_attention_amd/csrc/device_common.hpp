@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <utility>
 
 namespace isattn {
 
@@ -266,6 +267,15 @@ __device__ __forceinline__ void dma16_nt(const void* base, uint32_t off, uint32_
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base))
                  : "memory");
+}
+// dma16 to LDS address lds + IMM, the sum formed in m0 next to the load: a
+// run of loads into one tile then keeps only lds live in a scalar register
+template <int IMM>
+__device__ __forceinline__ void dma16_imm(const void* base, uint32_t off, uint32_t lds) {
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(scalar_ptr(base)), "i"(IMM)
+                 : "memory", "scc");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"

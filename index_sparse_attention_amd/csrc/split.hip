@@ -851,8 +851,23 @@ struct DkvShared {
     // With token masks a P wave's last load (k == KMAX + 1 where the P waves
     // load the statistics, else KMAX) is its keys' token words: lane L takes
     // word L / 32 of key 32 w + L % 32.
+    // Tile load K where every loading wave's loads split evenly between the
+    // Q and dO tiles: wave w's piece K lands 1 KiB x (w + NLW K) into its
+    // tile, the wave part added at run time, the rest an immediate.
+    template <int K>
+    __device__ void fire_tile(const Dma& d) const {
+        constexpr bool is_q = C::NLW * K < C::NQI;
+        constexpr int imm = 1024 * (is_q ? C::NLW * K : C::NLW * K - C::NQI);
+        dma16_imm<imm>(is_q ? d.q : d.o, d.off[K], (is_q ? d.lq : d.lo) + uint32_t(1024 * w));
+    }
+    template <int... Ks>
+    __device__ void fire_tiles(const Dma& d, int k, std::integer_sequence<int, Ks...>) const {
+        ((k == Ks ? fire_tile<Ks>(d) : void()), ...);   // k is a constant at every call site
+    }
     __device__ void fire(const Dma& d, int k) const {
-        if (k < C::KMAX) {
+        if (k < C::KMAX && C::NQI % C::NLW == 0 && C::NI % C::NLW == 0) {
+            fire_tiles(d, k, std::make_integer_sequence<int, C::KMAX>{});
+        } else if (k < C::KMAX) {
             const int j = load_index(w, k);
             const bool is_q = j < C::NQI;
             dma16(is_q ? d.q : d.o, d.off[k], is_q ? d.lq + uint32_t(1024 * j) : d.lo + uint32_t(1024 * (j - C::NQI)));

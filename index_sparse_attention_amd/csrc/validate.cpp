@@ -72,14 +72,17 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
         off = align_up(off + size_t(items) * sizeof(int32_t), kWsAlign);
     }
     // SPLIT part mode: few dK/dV items, each cut into parts of about T
-    // query blocks (T spreads the dense-equivalent work over ~4 parts per CU)
+    // query blocks.  A part costs a fixed amount (its pipeline start and
+    // drain, its fp32 partial written and reduced) and the last parts leave
+    // CUs idle for about T / 2 blocks, so T grows with the square root of
+    // the work per CU (dense-equivalent work over the 256 CUs)
     p.kv_parts_T = 0;
     p.kv_units_bound = 0;
     p.off_units = p.off_info = p.off_partial = off;
     const int64_t n_kv = int64_t(s.batch) * s.heads_k * p.n_kb;
     if (split && n_kv > 0 && n_kv < kPartModeItems) {
         const int64_t per_item = int64_t(p.G) * p.n_qb;      // query blocks of an item, dense
-        const int64_t T = std::max<int64_t>(1, (per_item * n_kv + 4 * kPartModeItems / 2 - 1) / (4 * kPartModeItems / 2));
+        const int64_t T = std::max<int64_t>(1, int64_t(std::ceil(std::sqrt(16.0 * double(per_item * n_kv) / 256.0))));
         const int64_t pmax = std::min<int64_t>(kMaxParts, std::max<int64_t>(1, (per_item + T - 1) / T));
         p.kv_parts_T = int32_t(T);
         p.kv_units_bound = int32_t(n_kv * pmax);

@@ -60,9 +60,10 @@ def test_workspace_sizes(lib):
     # SPLIT: delta and lse*log2(e), each padded per (batch, head) to whole 128-row blocks, then the
     # work order of the two passes (B*Hk*n_kb + B*Hq*n_qb int32); with fewer than 512 dK/dV items the
     # part mode adds units, per-item info and fp32 partial slots: items 8, dense query blocks per item
-    # G*n_qb = 6, target part T = ceil(6*8/1024) = 1, at most 6 parts per item -> 48 slots of 128 x 256
+    # G*n_qb = 6, target part T = ceil(sqrt(16 * 6*8 / 256)) = 2, at most 3 parts per item -> 24 slots
+    # of 128 x 256
     stats = al(2 * 4 * 384 * 4)
-    part_mode = al((48 + 1) * 4) + al(3 * 8 * 4) + al(48 * 128 * (128 + 128) * 4)
+    part_mode = al((24 + 1) * 4) + al(3 * 8 * 4) + al(24 * 128 * (128 + 128) * 4)
     assert ws_bytes(lib, s, 2) == 2 * stats + al((2 * 2 * 2 + 2 * 4 * 3) * 4) + part_mode
     # 512 or more dK/dV items: no part mode
     big = shape(B=1, Sq=128, Sk=128 * 256, Hq=2, Hk=2)
