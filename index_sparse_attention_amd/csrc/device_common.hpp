@@ -291,6 +291,7 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 // list, which share their operand tiles in that XCD's L2.  The grid has
 // 8 * per workgroups; -1 marks the padding ones past the last item.
 constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
 __host__ __device__ inline int xcd_items_per(int n_items) { return (n_items + kXcds - 1) / kXcds; }
 __device__ __forceinline__ int xcd_item(int id, int n_items) {
     const int w = (id % kXcds) * xcd_items_per(n_items) + id / kXcds;

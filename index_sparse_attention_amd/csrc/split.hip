@@ -182,8 +182,16 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
     const int hi = min(n, lo + per);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    // dK/dV items with at least 8 per CU of the XCD: grouped by (batch, KV
+    // head), longest first inside a group, so the workgroups an XCD runs at
+    // once share one head's Q and dO rows in its L2 (with fewer items per CU
+    // the late start of a group's longest items would lengthen the tail)
+    const int wmax = a.G * a.n_qb;
+    const int ngrp = (hi - lo + a.n_kb - 1) / a.n_kb + 1;
+    const bool grouped = pass == 0 && hi - lo >= 8 * kCusPerXcd && int64_t(ngrp) * (wmax + 1) <= kSchedKeys;
     auto key = [&](int i) {
         const int wk = pass == 0 ? item_work_kv(a, i) : item_work_q(a, i);
+        if (grouped) return (i / a.n_kb - lo / a.n_kb) * (wmax + 1) + (wmax - min(wk, wmax));
         return kSchedKeys - 1 - min(wk, kSchedKeys - 1);
     };
     for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
