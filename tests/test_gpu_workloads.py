@@ -68,7 +68,7 @@ def gpu_mask(w, d):
     return None
 
 
-@pytest.mark.parametrize("algo", ["loopk", "loopq", "split"])
+@pytest.mark.parametrize("algo", ["loopk", "loopq", "split", "split_ds"])
 @pytest.mark.parametrize("name", list(CHECKED))
 def test_workload_full_size(name, algo):
     import index_sparse_attention_amd as isa
