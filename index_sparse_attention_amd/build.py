@@ -39,10 +39,11 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE]
 # Per-source additions.  split.hip: MFMA results go to VGPRs, so a kernel that
 # needs no AGPRs gets the whole 256-register budget of two waves per SIMD as
 # VGPRs (the default halves it between VGPRs and AGPRs) and its VALU reads the
-# accumulators without v_accvgpr copies; the memory-clause scheduling strategy
-# issues the LDS operand reads in groups ahead of their MFMAs (measured 3-5%
-# faster dK/dV pass than the default strategy).
-SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+# accumulators without v_accvgpr copies.  The default scheduling strategy:
+# the memory-clause strategy (LDS operand reads grouped ahead of their MFMAs)
+# was faster for earlier versions of the kernels, and is now 1-2% slower on
+# the block-sparse dK/dV pass and 10% slower on the 32K causal d192 one.
+SOURCE_FLAGS = {"split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
