@@ -99,7 +99,8 @@ def test_index_converter_full_workload():
     assert int(got[0][-1]) == 2 * 128 * 129 // 2      # the full lower block triangle per KV head
 
 
-@pytest.mark.parametrize("shape", [(2, 16, 64, 64), (1, 3, 5, 9), (3, 1, 70, 1), (1, 2, 1, 130)])
+@pytest.mark.parametrize("shape", [(2, 16, 64, 64), (1, 3, 5, 9), (3, 1, 70, 1), (1, 2, 1, 130), (1, 4, 128, 128),
+                                   (4, 16, 64, 64), (2, 3, 100, 77), (1, 1, 129, 2)])
 def test_block_mask_to_csr(shape):
     import index_sparse_attention_amd as isa
     rng = np.random.default_rng(sum(shape))
