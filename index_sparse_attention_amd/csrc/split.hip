@@ -185,18 +185,49 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
     // dK/dV items with at least 8 per CU of the XCD: grouped by (batch, KV
     // head), longest first inside a group, so the workgroups an XCD runs at
     // once share one head's Q and dO rows in its L2 (with fewer items per CU
-    // the late start of a group's longest items would lengthen the tail)
+    // the late start of a group's longest items would lengthen the tail).
+    // Items with more than twice the range's mean work still go first, ahead
+    // of every group, for the same reason.
     const int wmax = a.G * a.n_qb;
     const int ngrp = (hi - lo + a.n_kb - 1) / a.n_kb + 1;
-    const bool grouped = pass == 0 && hi - lo >= 8 * kCusPerXcd && int64_t(ngrp) * (wmax + 1) <= kSchedKeys;
-    auto key = [&](int i) {
-        const int wk = pass == 0 ? item_work_kv(a, i) : item_work_q(a, i);
-        if (grouped) return (i / a.n_kb - lo / a.n_kb) * (wmax + 1) + (wmax - min(wk, wmax));
+    const bool grouped = pass == 0 && hi - lo >= 8 * kCusPerXcd && int64_t(ngrp + 1) * (wmax + 1) <= kSchedKeys;
+    // the work of a thread's first kCache items, computed once
+    constexpr int kCache = 4;
+    auto work_of = [&](int i) { return pass == 0 ? item_work_kv(a, i) : item_work_q(a, i); };
+    int wc[kCache];
+#pragma unroll
+    for (int j = 0; j < kCache; ++j) {
+        const int i = lo + tid + j * kSchedThreads;
+        wc[j] = i < hi ? work_of(i) : 0;
+    }
+    const int i_rest = lo + tid + kCache * kSchedThreads;
+    __shared__ int s_total;
+    for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
+    if (tid == 0) s_total = 0;
+    __syncthreads();
+    int big = INT_MAX;
+    if (grouped) {
+        int part = 0;
+#pragma unroll
+        for (int j = 0; j < kCache; ++j) part += wc[j];
+        for (int i = i_rest; i < hi; i += kSchedThreads) part += work_of(i);
+        atomicAdd(&s_total, part);
+        __syncthreads();
+        big = int(2.f * float(s_total) / float(hi - lo));
+    }
+    auto key = [&](int i, int wk) {
+        if (grouped) {
+            const int lead = wmax - min(wk, wmax);
+            return wk > big ? lead : (1 + i / a.n_kb - lo / a.n_kb) * (wmax + 1) + lead;
+        }
         return kSchedKeys - 1 - min(wk, kSchedKeys - 1);
     };
-    for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
-    __syncthreads();
-    for (int i = lo + tid; i < hi; i += kSchedThreads) atomicAdd(&cnt[key(i)], 1);
+#pragma unroll
+    for (int j = 0; j < kCache; ++j) {
+        const int i = lo + tid + j * kSchedThreads;
+        if (i < hi) atomicAdd(&cnt[key(i, wc[j])], 1);
+    }
+    for (int i = i_rest; i < hi; i += kSchedThreads) atomicAdd(&cnt[key(i, work_of(i))], 1);
     __syncthreads();
     // exclusive scan of the counts: thread t owns keys PER * t .. PER * t + PER - 1
     constexpr int PER = kSchedKeys / kSchedThreads;
@@ -223,7 +254,12 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
         run += v[j];
     }
     __syncthreads();
-    for (int i = lo + tid; i < hi; i += kSchedThreads) out[lo + atomicAdd(&cnt[key(i)], 1)] = i;
+#pragma unroll
+    for (int j = 0; j < kCache; ++j) {
+        const int i = lo + tid + j * kSchedThreads;
+        if (i < hi) out[lo + atomicAdd(&cnt[key(i, wc[j])], 1)] = i;
+    }
+    for (int i = i_rest; i < hi; i += kSchedThreads) out[lo + atomicAdd(&cnt[key(i, work_of(i))], 1)] = i;
 }
 
 // ---------------------------------------------------------------------------
