@@ -211,7 +211,9 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < kCache; ++j) part += wc[j];
         for (int i = i_rest; i < hi; i += kSchedThreads) part += work_of(i);
-        atomicAdd(&s_total, part);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (lane == 0) atomicAdd(&s_total, part);   // one LDS atomic per wave
         __syncthreads();
         big = int(2.f * float(s_total) / float(hi - lo));
     }
