@@ -119,11 +119,12 @@ def cpu_baseline(w, data, budget_s=20.0, max_slices=64):
     whole (batch b, query head h) slices, in order, added until about budget_s
     of CPU time (or max_slices)."""
     import oracle
+    cores = len(os.sched_getaffinity(0))            # host cores this process may run on
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        threads = cores
     total_flop, total_s, slices = 0, 0.0, []
     for b in range(w.batch):
         q = oracle.bf16_to_f64(data["q"][b:b + 1])
@@ -156,7 +157,9 @@ def cpu_baseline(w, data, budget_s=20.0, max_slices=64):
     return {
         "value": total_flop / total_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(min(cores, threads)),
+        "affinity_cores": int(cores),
+        "blas_threads": int(threads),
         "kind": "oracle",
         "sample": (f"fp64 NumPy oracle backward (K order) of {len(slices)} whole (batch, query head) "
                    f"slices of {w.name}, first {slices[0]} .. last {slices[-1]}: "
@@ -229,6 +232,7 @@ def main():
     else:
         mk = lambda: None
     m0 = mk()
+    nnz0 = m0.nnz() if m0 is not None else None    # kept mask blocks (one read; every step's mask has the same)
     if w.mask == "index":
         qp = m0.q2k_row_ptr.cpu().numpy()
         qc = m0.q2k_col[:int(qp[-1])].cpu().numpy()
@@ -261,13 +265,17 @@ def main():
                 "flop": fwd_flop}
 
     def run(algo, steps, warmup):
+        # the workspace holds SPLIT_DS's dS tiles for the kept blocks only
         ws = torch.empty(isa.attn_bwd_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_k,
-                                                      w.dim_qk, w.dim_v, algo), dtype=torch.uint8, device=dev)
+                                                      w.dim_qk, w.dim_v, algo, mask=m0, causal=w.causal),
+                         dtype=torch.uint8, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         timer = isa.Timer(capacity=max(steps, 1))
 
         def step(tm):
             m = mk()
+            if m is not None:
+                m.nnz_host = nnz0
             isa.attn_bwd(q, k, v, o, do, lse, mask=m, causal=w.causal, softmax_scale=w.scale, algo=algo,
                          dq=dq, dk=dk, dv=dv, workspace=ws, timer=tm)
 
@@ -336,6 +344,10 @@ def main():
         return {"ms": round(ms, 4), "pack": pack, "sequences": nseq, "topk": k,
                 "valid_score_gbs": round(valid * 4 / (ms * 1e-3) / 1e9, 1)}
 
+    if args.algo == "split_ds" and isa.choose_algo(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_k, w.dim_qk,
+                                                   w.dim_v, mask=m0, causal=w.causal, device=dev) != "split_ds":
+        log("split_ds: the dS store does not fit the free device memory; timing split instead")
+        args.algo = "split"
     log(f"timing {args.algo}: {args.warmup} warmup + {args.steps} steps")
     r = run(args.algo, args.steps, args.warmup)
     pairs = kept * 128 * 128
@@ -403,7 +415,8 @@ def main():
             r2 = run(other, max(10, args.steps // 2), 3)
             out["compare"].append({"algo": other, "ms_per_step": round(r2["ms_per_step"], 4),
                                    "value": round(flop / (r2["ms_per_step"] * 1e-3) / 1e12, 3),
-                                   "stages_ms": [round(x, 4) for x in r2["stage_ms"]]})
+                                   "stages_ms": [round(x, 4) for x in r2["stage_ms"]],
+                                   "step_ms": {k: round(v, 4) for k, v in r2["step_ms"].items()}})
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, data)

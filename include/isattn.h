@@ -34,7 +34,7 @@ typedef enum isattn_status {
     ISATTN_ERR_UNSUPPORTED = 4,   /* outside the supported set (head dims, block, algo) */
     ISATTN_ERR_MASK = 5,          /* malformed mask descriptor                          */
     ISATTN_ERR_WORKSPACE = 6,     /* workspace missing, too small or misaligned         */
-    ISATTN_ERR_CAPACITY = 7,      /* CSR column capacity below the worst case           */
+    ISATTN_ERR_CAPACITY = 7,      /* CSR column or dS tile capacity below what is needed */
     ISATTN_ERR_HIP = 8            /* a HIP runtime call or kernel launch failed         */
 } isattn_status_t;
 
@@ -73,7 +73,12 @@ enum { ISATTN_MASK_DENSE = 0, ISATTN_MASK_BLOCK_CSR = 1 };
  * words [0, 512) row-major -- bit j % 32 of word 4 r + j / 32 is row r, key j
  * of the block -- and words [512, 1024) the same bits key-major -- bit r % 32
  * of word 512 + 4 j + r / 32.  SPLIT, SPLIT_DS and the forward only.
- * block_q = block_k = 128; heads is 1, heads_k or heads_q. */
+ * block_q = block_k = 128; heads is 1, heads_k or heads_q.
+ * nnz: host-side count of the CSR's blocks (q2k_row_ptr[last]) when the
+ * caller knows it, else any negative value.  Only SPLIT_DS reads it, to size
+ * its dS store by the kept blocks; a count below the true one makes results
+ * undefined (dS stores past the workspace are dropped, never written out of
+ * bounds). */
 typedef struct isattn_mask {
     int32_t kind;
     int32_t block_q, block_k;
@@ -83,6 +88,7 @@ typedef struct isattn_mask {
     const int32_t* k2q_row_ptr;   /* [batch*heads*n_kb + 1] device */
     const int32_t* k2q_col;       /* [nnz] device                   */
     const uint32_t* token_bits;   /* NULL, or [batch*heads*n_qb*n_kb][1024] device */
+    int64_t nnz;                  /* host: blocks in the CSR, or < 0 if unknown */
 } isattn_mask_t;
 
 /* Loop orders of [P1] Summary.  LOOPK: outer loop over 128-row query tiles,
@@ -100,8 +106,12 @@ typedef struct isattn_mask {
  * delta) and also stores every dS tile it forms (bf16) in the workspace; a
  * LOOPK pass then accumulates dQ = dS K from them, streaming 32 KiB of dS per
  * kept block instead of recomputing S and dP.  Same results as SPLIT up to
- * rounding order, for a workspace of B*Hq*ceil(Sq/128)*ceil(Sk/128)*32 KiB
- * (every block slot, kept or not). */
+ * rounding order.  Its workspace holds one 32 KiB dS tile per kept block
+ * of each query head: (heads_q / mask heads) * nnz tiles for a block CSR,
+ * batch * heads_q * (visible 128 x 128 blocks of one head) for a dense or
+ * causal mask, batch * heads_q * ceil(Sq/128) * ceil(Sk/128) for a dense
+ * mask over packed sequences; a block CSR whose nnz the caller does not give
+ * is sized for every block of every mask head. */
 enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2, ISATTN_ALGO_SPLIT_DS = 3 };
 
 /* Bytes of device workspace isattn_attn_bwd needs for this shape and algo
@@ -110,10 +120,24 @@ enum { ISATTN_ALGO_LOOPK = 0, ISATTN_ALGO_LOOPQ = 1, ISATTN_ALGO_SPLIT = 2, ISAT
  * lse * log2(e), each [B,Hq,ceil(Sq/128)*128], the int32 work order of its
  * two passes, and -- when there are fewer than 512 (b, KV head, 128-key
  * block) items -- the schedule and fp32 partial dK|dV of the items cut into
- * parts; for SPLIT_DS the same plus the bf16 dS tiles,
- * [B,Hq,ceil(Sq/128),ceil(Sk/128)] x 128 x 128; each part 256-byte
- * aligned).  Returns 0 for a NULL shape or unknown algo. */
+ * parts; for SPLIT_DS the same plus, for block CSR masks, the int32 K->Q
+ * position of every Q->K entry and then the bf16 dS tiles of 128 x 128;
+ * each part 256-byte aligned).  This form assumes nothing about the mask:
+ * its SPLIT_DS size holds a dS tile for every (b, h, query block, key
+ * block).  Returns 0 for a NULL shape or unknown algo. */
 size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo);
+
+/* The same for a given mask (NULL = dense), causal flag and layout (varlen
+ * nonzero: packed sequences, the shape holding the longest lengths): SPLIT_DS
+ * gets exactly the dS tiles of the kept blocks (see ISATTN_ALGO_SPLIT_DS),
+ * reading mask->nnz for a block CSR.  isattn_attn_bwd derives the dS
+ * capacity from workspace_bytes and returns ISATTN_ERR_CAPACITY, before any
+ * launch, when it holds fewer tiles than the mask needs (an nnz below 0
+ * needs the every-block size).  The other algorithms' sizes do not depend on
+ * the mask. */
+size_t isattn_attn_bwd_workspace_bytes_mask(const isattn_shape_t* shape, int32_t algo,
+                                            const isattn_mask_t* mask, int32_t causal,
+                                            int32_t varlen);
 
 /* Attention backward ([P1] Summary and Core changes 1-3): recompute
  * P = exp(softmax_scale * Q K^T - LSE) on the kept pairs, then

@@ -28,7 +28,13 @@ class Tensor(ctypes.Structure):
 class Mask(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("block_q", c_int32), ("block_k", c_int32), ("heads", c_int32),
                 ("q2k_row_ptr", c_void_p), ("q2k_col", c_void_p),
-                ("k2q_row_ptr", c_void_p), ("k2q_col", c_void_p), ("token_bits", c_void_p)]
+                ("k2q_row_ptr", c_void_p), ("k2q_col", c_void_p), ("token_bits", c_void_p),
+                ("nnz", c_int64)]
+
+    def __init__(self, *args, **kw):
+        if len(args) < len(self._fields_) and "nnz" not in kw:
+            kw["nnz"] = -1                         # block count unknown unless given
+        super().__init__(*args, **kw)
 
 
 class Varlen(ctypes.Structure):
@@ -42,6 +48,7 @@ _BWD_ARGS = [POINTER(Shape), _T, _T, _T, _T, _T, c_void_p, POINTER(Mask), c_int3
 # name -> (restype, argtypes); every function declared in include/isattn.h
 SIGNATURES = {
     "isattn_attn_bwd_workspace_bytes": (c_size_t, [POINTER(Shape), c_int32]),
+    "isattn_attn_bwd_workspace_bytes_mask": (c_size_t, [POINTER(Shape), c_int32, POINTER(Mask), c_int32, c_int32]),
     "isattn_attn_bwd": (c_int32, _BWD_ARGS),
     "isattn_attn_bwd_timed": (c_int32, _BWD_ARGS + [c_void_p]),
     "isattn_attn_fwd": (c_int32, [POINTER(Shape), _T, _T, _T, POINTER(Mask), c_int32, c_float, _T, c_void_p,

@@ -16,6 +16,8 @@ from . import _abi
 
 ALGOS = {"loopk": _abi.ALGO_LOOPK, "loopq": _abi.ALGO_LOOPQ, "split": _abi.ALGO_SPLIT,
          "split_ds": _abi.ALGO_SPLIT_DS}
+# "auto" takes SPLIT_DS when its dS store fits this fraction of the free device memory, else SPLIT
+AUTO_FREE_FRACTION = 0.8
 
 
 def _stream_ptr(stream) -> int:
@@ -63,7 +65,9 @@ class BlockMask:
     k2q: per (batch, mask head, key block) the ascending query blocks;
     token_bits: optional token-exact bits (int32 [batch*heads*n_qb*n_kb*1024],
     the layout of isattn_mask_t.token_bits): inside a kept block a pair is
-    attended only if its bit is set."""
+    attended only if its bit is set.
+    nnz_host: the number of kept blocks when known on the host (SPLIT_DS
+    sizes its dS store by it); None until ``nnz()`` reads it."""
     heads: int
     n_qb: int
     n_kb: int
@@ -74,16 +78,23 @@ class BlockMask:
     block_q: int = 128
     block_k: int = 128
     token_bits: torch.Tensor | None = None
+    nnz_host: int | None = None
 
     def nnz(self) -> int:
-        """Number of kept blocks (reads the last row pointer: synchronises)."""
-        return int(self.q2k_row_ptr[-1].item())
+        """Number of kept blocks (reads the last row pointer once: synchronises)."""
+        if self.nnz_host is None:
+            self.nnz_host = int(self.q2k_row_ptr[-1].item())
+        return self.nnz_host
 
     def _abi(self) -> _abi.Mask:
         return _abi.Mask(_abi.MASK_BLOCK_CSR, self.block_q, self.block_k, self.heads,
                          self.q2k_row_ptr.data_ptr(), self.q2k_col.data_ptr(),
                          self.k2q_row_ptr.data_ptr(), self.k2q_col.data_ptr(),
-                         self.token_bits.data_ptr() if self.token_bits is not None else None)
+                         self.token_bits.data_ptr() if self.token_bits is not None else None,
+                         -1 if self.nnz_host is None else int(self.nnz_host))
+
+
+_DENSE = lambda: _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None, None, -1)
 
 
 class Timer:
@@ -122,9 +133,33 @@ class Timer:
 
 
 def attn_bwd_workspace_bytes(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v,
-                             algo="split") -> int:
+                             algo="split", mask: "BlockMask | None | str" = "any", causal: bool = False,
+                             varlen: bool = False) -> int:
+    """Workspace bytes of ``attn_bwd``.  ``mask="any"`` (default) sizes for
+    any mask (SPLIT_DS: a dS tile for every block); None (dense) or a
+    BlockMask sizes SPLIT_DS's dS store by the kept blocks (a BlockMask's
+    ``nnz_host`` if set, else every block of every mask head)."""
     shape = _abi.Shape(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v)
-    return int(_abi.load().isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), ALGOS[algo]))
+    lib = _abi.load()
+    if isinstance(mask, str):
+        return int(lib.isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), ALGOS[algo]))
+    m = mask._abi() if mask is not None else _DENSE()
+    return int(lib.isattn_attn_bwd_workspace_bytes_mask(ctypes.byref(shape), ALGOS[algo], ctypes.byref(m),
+                                                       int(bool(causal)), int(bool(varlen))))
+
+
+def choose_algo(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v, mask=None, causal=False,
+                varlen=False, device=None) -> str:
+    """SPLIT_DS (faster) when its workspace, with the dS store sized by the
+    kept blocks, fits AUTO_FREE_FRACTION of the free device memory; SPLIT
+    (a workspace of a few MiB) otherwise.  Reads a BlockMask's block count
+    (one synchronisation) if it is not known yet."""
+    if mask is not None:
+        mask.nnz()
+    need = attn_bwd_workspace_bytes(batch, seqlen_q, seqlen_k, heads_q, heads_k, dim_qk, dim_v, "split_ds",
+                                    mask=mask, causal=causal, varlen=varlen)
+    free, _ = torch.cuda.mem_get_info(device)
+    return "split_ds" if need <= AUTO_FREE_FRACTION * free else "split"
 
 
 def _dims(q, k, v, vl):
@@ -139,7 +174,7 @@ def _dims(q, k, v, vl):
 
 
 def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = False,
-             softmax_scale: float | None = None, algo: str = "split", dq=None, dk=None, dv=None,
+             softmax_scale: float | None = None, algo: str = "auto", dq=None, dk=None, dv=None,
              workspace: torch.Tensor | None = None, stream=None, timer: Timer | None = None,
              cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
     """Attention backward on the GPU.  Returns (dq, dk, dv) as bf16 tensors.
@@ -147,10 +182,13 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     q [B,Sq,Hq,Dqk], k [B,Sk,Hk,Dqk], v [B,Sk,Hk,Dv], o/do [B,Sq,Hq,Dv] bf16;
     lse fp32 [B,Hq,Sq] (natural log).  ``mask`` None = dense.  ``causal``
     adds the bottom-right causal term.  Outputs are allocated when not given.
-    ``algo``: "split" (default: two atomic-free passes, small workspace),
-    "split_ds" (the dK/dV pass stores dS for the dQ pass: faster, workspace of
-    B*Hq*ceil(Sq/128)*ceil(Sk/128)*32 KiB), "loopk" or "loopq" (the pages'
-    loop orders with fp32 atomics).
+    ``algo``: "auto" (default: "split_ds" when its workspace fits the free
+    device memory, else "split"), "split" (two atomic-free passes, a
+    workspace of a few MiB), "split_ds" (the dK/dV pass stores dS for the dQ
+    pass: faster, 32 KiB of workspace per kept block and query head), "loopk"
+    or "loopq" (the pages' loop orders with fp32 atomics).  A workspace
+    allocated here for "split_ds" is sized by the mask's kept blocks (a
+    BlockMask's count is read once if not known: one synchronisation).
     Packed sequences: pass int32 ``cu_seqlens_q`` / ``cu_seqlens_k`` [B + 1]
     and q, k, v, o, do as [total_tokens, heads, dim]; lse is then
     [B, Hq, max_seqlen_q] (the longest lengths are computed when not given,
@@ -167,13 +205,19 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
+    if algo == "auto":
+        algo = choose_algo(B, Sq, Sk, Hq, Hk, Dqk, Dv, mask=mask, causal=causal, varlen=vl is not None,
+                           device=q.device)
     a = ALGOS[algo]
-    need = int(lib.isattn_attn_bwd_workspace_bytes(ctypes.byref(shape), a))
     if workspace is None:
+        if algo == "split_ds" and mask is not None:
+            mask.nnz()
+        need = attn_bwd_workspace_bytes(B, Sq, Sk, Hq, Hk, Dqk, Dv, algo, mask=mask, causal=causal,
+                                        varlen=vl is not None)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     views = [_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
                                       (dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
+    m = mask._abi() if mask is not None else _DENSE()
     args = [ctypes.byref(x) for x in views[:5]] + [
         lse.data_ptr(), ctypes.byref(m), int(bool(causal)), float(softmax_scale)] + [
         ctypes.byref(x) for x in views[5:]] + [a, workspace.data_ptr(), workspace.numel(),
@@ -213,7 +257,7 @@ def attn_fwd(q, k, v, mask: BlockMask | None = None, causal: bool = False, softm
         raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
     shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
     vq, vk, vv, vo = (_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")))
-    m = mask._abi() if mask is not None else _abi.Mask(_abi.MASK_DENSE, 128, 128, 0, None, None, None, None)
+    m = mask._abi() if mask is not None else _DENSE()
     args = [ctypes.byref(vq), ctypes.byref(vk), ctypes.byref(vv), ctypes.byref(m), int(bool(causal)),
             float(softmax_scale), ctypes.byref(vo), lse.data_ptr(), _stream_ptr(stream)]
     if vl is not None:

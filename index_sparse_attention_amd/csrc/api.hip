@@ -48,6 +48,10 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     a.lse2 = split ? reinterpret_cast<float*>(ws_at(workspace, plan.off_lse2)) : nullptr;
     a.order = split ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_order)) : nullptr;
     a.ds = algo == ISATTN_ALGO_SPLIT_DS ? reinterpret_cast<uint16_t*>(ws_at(workspace, plan.off_ds)) : nullptr;
+    if (algo == ISATTN_ALGO_SPLIT_DS && a.mask_kind == ISATTN_MASK_BLOCK_CSR) {
+        a.ds_map = reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_dsmap));
+        a.ds_flag = a.ds_map + plan.ds_map_len;
+    }
     a.kv_parts_T = plan.kv_parts_T;
     a.kv_units_bound = plan.kv_units_bound;
     a.units = plan.kv_parts_T > 0 ? reinterpret_cast<int32_t*>(ws_at(workspace, plan.off_units)) : nullptr;
@@ -64,6 +68,7 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     // computes delta and lse2 for the dK/dV pass
     if (algo != ISATTN_ALGO_SPLIT && launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
     if (split && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (algo == ISATTN_ALGO_SPLIT_DS && launch_ds_map(a, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
     hipError_t e;
     if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);
@@ -90,6 +95,26 @@ size_t isattn_attn_bwd_workspace_bytes(const isattn_shape_t* shape, int32_t algo
     if (shape == nullptr) return 0;
     BwdPlan p{};
     if (!plan_bwd_workspace(*shape, algo, &p)) return 0;
+    return p.total;
+}
+
+size_t isattn_attn_bwd_workspace_bytes_mask(const isattn_shape_t* shape, int32_t algo, const isattn_mask_t* mask,
+                                            int32_t causal, int32_t varlen) {
+    if (shape == nullptr) return 0;
+    MaskInfo mi;
+    mi.kind = ISATTN_MASK_DENSE;
+    if (mask != nullptr && mask->kind == ISATTN_MASK_BLOCK_CSR) {
+        mi.kind = ISATTN_MASK_BLOCK_CSR;
+        mi.heads = mask->heads;
+        mi.nnz = mask->nnz;
+    } else if (mask != nullptr && mask->kind != ISATTN_MASK_DENSE) {
+        return 0;
+    }
+    if (mi.kind == ISATTN_MASK_BLOCK_CSR && (mi.heads < 1 || shape->heads_q % mi.heads != 0)) return 0;
+    mi.causal = causal != 0;
+    mi.varlen = varlen != 0;
+    BwdPlan p{};
+    if (!plan_bwd_workspace(*shape, algo, &p, mi)) return 0;
     return p.total;
 }
 
@@ -289,13 +314,13 @@ const char* isattn_status_string(isattn_status_t status) {
         case ISATTN_ERR_UNSUPPORTED: return "outside the supported set";
         case ISATTN_ERR_MASK: return "malformed mask descriptor";
         case ISATTN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
-        case ISATTN_ERR_CAPACITY: return "CSR column capacity too small";
+        case ISATTN_ERR_CAPACITY: return "CSR column or dS tile capacity too small";
         case ISATTN_ERR_HIP: return "HIP runtime error";
     }
     return "unknown status";
 }
 
-const char* isattn_version(void) { return "0.1.0"; }
+const char* isattn_version(void) { return "0.2.0"; }
 
 isattn_status_t isattn_timer_create(int32_t capacity, isattn_timer_t** out) {
     if (out == nullptr) return ISATTN_ERR_NULL;

@@ -35,7 +35,18 @@ struct BwdArgs {
     int32_t* units;
     int32_t* item_info;
     float* partial;
-    uint16_t* ds;         // SPLIT_DS: bf16 dS tiles [B, Hq, n_qb, n_kb][128 x 128]; else null
+    // SPLIT_DS: bf16 dS tiles of 128 x 128, one per kept (b, h, qb, kb) block
+    // (dS tile slots below); else null.  ds_cap: tiles the workspace holds
+    // (fewer than 2^31), ds_T: tiles per (b, h) of a dense mask.  Block CSR
+    // masks: ds_map[p] is the K->Q position of Q->K entry p (ds_map_len
+    // entries; -1 where the two forms disagree), and *ds_flag is set when the
+    // CSR's true block count needs more than ds_cap tiles (both passes then
+    // compute nothing; reads of a tile are clamped into [0, ds_cap) anyway).
+    uint16_t* ds;
+    int32_t ds_cap, ds_T;
+    int32_t* ds_map;
+    int32_t* ds_flag;
+    int64_t ds_map_len;
     float* acc0;          // LoopK: dK accumulator [B,Hk,Sk,Dqk]; LoopQ: dQ accumulator [B,Hq,Sq,Dqk]
     float* acc1;          // LoopK: dV accumulator [B,Hk,Sk,Dv]; LoopQ: unused
     int64_t acc0_elems, acc1_elems;
@@ -76,6 +87,47 @@ struct FwdArgs {
     int32_t mask_kind, causal;
     float scale_log2;     // softmax_scale * log2(e)
 };
+
+#if defined(__HIPCC__)
+#define ISATTN_HD __host__ __device__
+#else
+#define ISATTN_HD
+#endif
+
+// ---- dS tile slots of SPLIT_DS ---------------------------------------------
+// Block CSR mask: the slot of (b, h, qb, kb) is R * p + (h - hm * R), with p
+// the position of the block in the K->Q lists, R = Hq / Hm query heads per
+// mask head and hm = h * Hm / Hq: R * nnz slots in all.  Dense masks at fixed
+// lengths: (b * Hq + h) * T + (visible blocks of the query blocks before qb)
+// + kb, T the visible blocks of one head (bottom-right causal cut, or all
+// n_qb * n_kb without it).  Packed sequences with a dense mask: every
+// (qb, kb) of the longest lengths, T = n_qb * n_kb (a sequence's causal cut
+// differs from that of the longest lengths).
+ISATTN_HD inline int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+// key blocks visible to query block qb: rows up to min(128 qb + 127, Sq - 1)
+// see keys up to that row + Sk - Sq (all n_kb without the causal term)
+ISATTN_HD inline int64_t visible_kb(int64_t qb, int64_t Sq, int64_t Sk, int64_t n_kb, bool causal) {
+    if (!causal) return n_kb;
+    const int64_t last_row = 128 * qb + 127 < Sq - 1 ? 128 * qb + 127 : Sq - 1;
+    const int64_t last_key = last_row + Sk - Sq;
+    if (last_key < 0) return 0;
+    const int64_t n = last_key / 128 + 1;
+    return n < n_kb ? n : n_kb;
+}
+// sum of clamp(x, 0, N) over the integers x < y
+ISATTN_HD inline int64_t clamp_prefix(int64_t y, int64_t N) {
+    if (y <= 0) return 0;
+    if (y <= N + 1) return y * (y - 1) / 2;
+    return N * (N + 1) / 2 + (y - N - 1) * N;
+}
+// visible key blocks of the query blocks before qb (qb <= n_qb - 1): blocks
+// qb' < n_qb - 1 are whole, so visible_kb(qb') = clamp(qb' + c0, 0, n_kb)
+// with c0 = 1 + floor((127 + Sk - Sq) / 128)
+ISATTN_HD inline int64_t visible_before(int64_t qb, int64_t Sq, int64_t Sk, int64_t n_kb, bool causal) {
+    if (!causal) return qb * n_kb;
+    const int64_t c0 = 1 + floor_div(127 + Sk - Sq, 128);
+    return clamp_prefix(c0 + qb, n_kb) - clamp_prefix(c0, n_kb);
+}
 
 #if defined(__HIPCC__)
 // Narrow the arguments to packed sequence b: its lengths (clamped to the

@@ -23,6 +23,8 @@ hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 // SPLIT_DS second pass: dQ from the dS tiles the dK/dV pass stored.
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
+// SPLIT_DS with a block CSR: the K->Q position of every Q->K entry (a.ds_map).
+hipError_t launch_ds_map(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
 // Top-k positions per score row within [starts[r], ends[r]) (full rows when

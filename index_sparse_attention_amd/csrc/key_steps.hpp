@@ -17,6 +17,11 @@ struct KeySteps {
     int it = -1, sub = 0, count = 0, n0 = 0, n_kb = 0, last = 0, lane = 0;
     const int32_t* list = nullptr;
     int chunk = 0, chunk_base = -1;
+    int beg = 0;                                    // Q->K position of the row's first entry
+    // optional per-entry values read along with the list (aux[i] for entry
+    // i, i < aux_n; -1 past it): aux_at() gives the current entry's
+    const int32_t* aux = nullptr;
+    int aux_n = 0, achunk = -1;
 
     __device__ int kb_at() {
         if (list == nullptr) return it;
@@ -24,9 +29,11 @@ struct KeySteps {
         if (base != chunk_base) {
             chunk_base = base;
             chunk = base + lane < count ? list[base + lane] : -1;
+            if (aux != nullptr) achunk = base + lane < aux_n ? aux[base + lane] : -1;
         }
         return __builtin_amdgcn_readlane(chunk, it & 63);
     }
+    __device__ int aux_at() const { return __builtin_amdgcn_readlane(achunk, it & 63); }
     __device__ bool next_block() {
         for (;;) {
             if (++it >= count) return false;
@@ -65,6 +72,7 @@ __device__ __forceinline__ void init_key_steps(KeySteps& st, const Args& a, int 
         const int beg = a.q2k_ptr[r];
         st.count = a.q2k_ptr[r + 1] - beg;
         st.list = a.q2k_col + beg;
+        st.beg = beg;
     } else {
         const int nkb = (a.Sk + kBlock - 1) / kBlock;
         st.count = nkb;

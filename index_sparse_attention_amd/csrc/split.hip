@@ -689,7 +689,7 @@ struct DkvCfg {
 // row of sees, or that lie past Sq, are still stepped through: their P is
 // masked to zero or their rows' lse2 is +inf.  The kept query blocks of a
 // head are read 64 at a time into a register (one per lane).
-template <int BM>
+template <int BM, bool DS>
 struct DkvSteps {
     static constexpr int PARTS = kBlock / BM;
     const BwdArgs& a;
@@ -699,6 +699,12 @@ struct DkvSteps {
     int cum = 0;                                    // blocks in the group's earlier heads
     int lo = 0, hi = INT_MAX;                       // range of the group's concatenated block lists
     const int32_t* list = nullptr;
+    // DS (SPLIT_DS): the dS tile slot (dS tile slots in bwd_args.hpp) of the
+    // current block, and the current head's slot of its first list entry
+    // (block CSR: R * the K->Q position + the head's place among the R query
+    // heads of its mask head; the next entry is R slots on) or of (qb = 0,
+    // kb) (dense)
+    int tile = 0, tile0 = 0;
     int chunk = 0, chunk_base = -1;
     // the current head's Q, dO and statistics rows
     const uint16_t* qh = nullptr;
@@ -711,11 +717,9 @@ struct DkvSteps {
 
     __device__ int hq() const { return hk * a.G + gi; }
     // element offset of the current step's part of its dS tile (SPLIT_DS):
-    // tile (b, h, qb, kb) of 128 x 128 bf16, the step's 64 rows its half p
-    __device__ int64_t ds_off() const {
-        return (((int64_t(b) * a.Hq + hq()) * a.n_qb + m / kBlock) * a.n_kb + kb) * (kBlock * kBlock) +
-               (m % kBlock) * kBlock;
-    }
+    // the 128 x 128 bf16 tile of the block's slot, the step's 64 rows its
+    // half m % 128 / 64 (only the dS waves of SPLIT_DS use it)
+    __device__ int64_t ds_off() const { return int64_t(tile) * (kBlock * kBlock) + (m % kBlock) * kBlock; }
 
     __device__ void load_head() {
         const int h = hq();
@@ -733,12 +737,17 @@ struct DkvSteps {
             const int beg = a.k2q_ptr[r];
             count = a.k2q_ptr[r + 1] - beg;
             list = a.k2q_col + beg;
+            if constexpr (DS) {
+                const int R = a.Hq / a.Hm;
+                tile0 = R * beg + (h - hm * R);
+            }
         } else {
             if (a.causal) {
                 const int first_row = n_base - shift;
                 first = first_row <= 0 ? 0 : first_row / kBlock;
             }
             count = (a.Sq + kBlock - 1) / kBlock - first;
+            if constexpr (DS) tile0 = (b * a.Hq + h) * a.ds_T + kb;
         }
     }
     __device__ int qb_at() {
@@ -767,6 +776,11 @@ struct DkvSteps {
             if (a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base) continue;
             part = 0;
             m = qb * kBlock;
+            if constexpr (DS) {
+                if (list != nullptr) tile = tile0 + (a.Hq / a.Hm) * it;
+                else tile = tile0 + (a.cu_q != nullptr ? qb * a.n_kb
+                                                       : int(visible_before(qb, a.Sq, a.Sk, a.n_kb, a.causal != 0)));
+            }
             return true;
         }
     }
@@ -856,8 +870,8 @@ struct DkvShared {
     }
 
     // Plan the loads of the steps' current step into stage s.
-    template <bool TOK>
-    __device__ void plan(Dma& d, const DkvSteps<C::BM>& st, int s) const {
+    template <bool TOK, bool DS>
+    __device__ void plan(Dma& d, const DkvSteps<C::BM, DS>& st, int s) const {
         const int m = st.m;
         restage(d, s);
         d.q = st.qh;
@@ -1423,8 +1437,8 @@ __device__ __forceinline__ void step_barrier() {
 // free of branches.  The loop body is one straight-line block per role (masking is a
 // fix-up on the packed P, outside the MFMA block) so the accumulators stay
 // put in registers.
-template <int DQK, int DV, class Role>
-__device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM>& steps,
+template <int DQK, int DV, bool DS, class Role>
+__device__ __forceinline__ void dkdv_run(const DkvShared<DQK, DV>& sh, DkvSteps<DkvCfg<DQK, DV>::BM, DS>& steps,
                                          Role& role) {
     using C = DkvCfg<DQK, DV>;
     const BwdArgs& a = sh.a;
@@ -1504,16 +1518,22 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
         if (kb * C::BN >= a.Sk) return;            // a key block past the end of the sequence
     }
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
-    DkvSteps<C::BM> steps(a, b, hk, kb, lane);
+    if constexpr (DS) {
+        // a block CSR whose true block count needs more dS tiles than the
+        // workspace holds (flagged by the position-map kernel): nothing is
+        // computed rather than anything written past the workspace
+        if (a.ds_flag != nullptr && *a.ds_flag != 0) return;
+    }
+    DkvSteps<C::BM, DS> steps(a, b, hk, kb, lane);
     steps.lo = lo;
     steps.hi = hi;
     if (w < C::NR) {
         DkvPWave<DQK, DV, TOK> role(sh, w);
-        dkdv_run<DQK, DV>(sh, steps, role);
+        dkdv_run<DQK, DV, DS>(sh, steps, role);
         role.store(partial);
     } else {
         DkvSWave<DQK, DV, DS> role(sh, w - C::NR);
-        dkdv_run<DQK, DV>(sh, steps, role);
+        dkdv_run<DQK, DV, DS>(sh, steps, role);
         role.store(partial);
     }
 }
@@ -1540,6 +1560,7 @@ template <int DQK, int DV>
 __global__ __launch_bounds__(256) void k_dkdv_reduce(BwdArgs a) {
     constexpr int W = DQK + DV;
     const int item = blockIdx.x / (kBlock / 8);
+    if (a.ds_flag != nullptr && *a.ds_flag != 0) return;   // SPLIT_DS overflow: the parts computed nothing
     const int parts = a.item_info[3 * item + 1];
     if (parts <= 1) return;
     const int slot = a.item_info[3 * item + 2];

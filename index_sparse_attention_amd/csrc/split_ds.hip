@@ -93,10 +93,26 @@ __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a)
         seq_view(a, b);
         if (m_base >= a.Sq) return;                // a block past the end of the sequence
     }
+    if (a.ds_flag != nullptr && *a.ds_flag != 0) return;   // the dS tiles were not stored (overflow)
 
-    // the key blocks the dK/dV pass visited for this query block
+    // the key blocks the dK/dV pass visited for this query block, and the
+    // slots of their dS tiles: block CSR, R * (K->Q position) + the head's
+    // place among the R query heads of its mask head (the position map read
+    // along with the Q->K list); dense, the head's slot of (qb, kb = 0) + kb
     KeySteps steps;
     init_key_steps(steps, a, b, h, qb, lane);
+    const bool csr = a.mask_kind == 1;
+    int R = 1, rr = 0;
+    int64_t tile0 = 0;
+    if (csr) {
+        R = a.Hq / a.Hm;
+        rr = h - (h * a.Hm / a.Hq) * R;
+        steps.aux = a.ds_map + steps.beg;
+        steps.aux_n = int(min(int64_t(steps.count), max(int64_t(0), a.ds_map_len - steps.beg)));
+    } else {
+        tile0 = (int64_t(b) * a.Hq + h) * int64_t(a.ds_T) +
+                (VL ? int64_t(qb) * a.n_kb : visible_before(qb, a.Sq, a.Sk, a.n_kb, a.causal != 0));
+    }
 
     f32x16_t dq[C::NDT];
 #pragma unroll
@@ -105,7 +121,6 @@ __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a)
     // ---- loads: K part (instruction j = w + NW * kk of the K tile, rows in
     // plain order) and this wave's two dS chunks of the step's key group
     const uint16_t* gk = a.k + b * a.k_sb + hk * a.k_sh;
-    const uint16_t* gds = a.ds + ((int64_t(b) * a.Hq + h) * a.n_qb + qb) * int64_t(a.n_kb) * (kBlock * kBlock);
     const uint32_t lds_base = lds_address(lds);
     auto k_off = [&](int kk, int lim) -> uint32_t {  // tile rows past lim read row lim
         const int e = 512 * (w + C::NW * kk) + 8 * lane;
@@ -130,7 +145,9 @@ __global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a)
         const int kb = n0 / kBlock;
         const int wr = (n0 - kb * kBlock) / C::BN;
         d.sb = lds_base + uint32_t(s * C::STAGE_BYTES);
-        d.ds = gds + int64_t(kb) * (kBlock * kBlock);
+        int64_t tile = csr ? int64_t(R) * steps.aux_at() + rr : tile0 + kb;
+        tile = min(max(tile, int64_t(0)), int64_t(a.ds_cap) - 1);   // in bounds whatever the mask holds
+        d.ds = a.ds + tile * (kBlock * kBlock);
         d.dso = uint32_t((wchunk + 4 * wr) * 1024);
         if (n0 + C::BN <= a.Sk) {
             const uint32_t mk = uint32_t(n0) * uint32_t(a.k_ss * 2);
@@ -245,7 +262,50 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// K->Q position of every Q->K entry of a block CSR (the dS slot of the dQ
+// pass's block): one wave per Q->K row (b, hm, qb), lanes over its entries,
+// each a binary search for qb in the K->Q row (b, hm, kb).  -1 where the
+// two forms disagree.  Thread 0 also sets the overflow flag: the CSR holds
+// more blocks than the map or the dS tiles have room for.
+__global__ __launch_bounds__(256) void k_ds_map(BwdArgs a) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const int64_t rq = int64_t(a.B) * a.Hm * a.n_qb, rk = int64_t(a.B) * a.Hm * a.n_kb;
+        const int64_t nnz = max(int64_t(a.q2k_ptr[rq]), int64_t(a.k2q_ptr[rk]));
+        *a.ds_flag = (nnz > a.ds_map_len || nnz * (a.Hq / a.Hm) > a.ds_cap) ? 1 : 0;
+    }
+    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= int64_t(a.B) * a.Hm * a.n_qb) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t bhm = row / a.n_qb;
+    const int qb = int(row - bhm * a.n_qb);
+    const int end = a.q2k_ptr[row + 1];
+    for (int p = a.q2k_ptr[row] + lane; p < end; p += 64) {
+        if (p < 0 || p >= a.ds_map_len) continue;
+        const int kb = a.q2k_col[p];
+        int pos = -1;
+        if (kb >= 0 && kb < a.n_kb) {
+            const int64_t r = bhm * a.n_kb + kb;
+            const int hi0 = a.k2q_ptr[r + 1];
+            int lo = a.k2q_ptr[r], hi = hi0;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo) / 2;
+                if (a.k2q_col[mid] < qb) lo = mid + 1;
+                else hi = mid;
+            }
+            if (lo < hi0 && a.k2q_col[lo] == qb) pos = lo;
+        }
+        a.ds_map[p] = pos;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ds_map(const BwdArgs& a, hipStream_t s) {
+    const int64_t rows = int64_t(a.B) * a.Hm * a.n_qb;
+    if (a.ds_flag == nullptr) return hipSuccess;  // dense masks: slots from the shape alone
+    hipLaunchKernelGGL(k_ds_map, dim3(unsigned(max(int64_t(1), (rows + 3) / 4))), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s) {
     const bool vl = a.cu_q != nullptr;             // packed sequences

@@ -44,7 +44,8 @@ void copy_view_out(const isattn_tensor_t* t, uint16_t** p, int64_t* sb, int64_t*
 
 }  // namespace
 
-bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
+bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan, const MaskInfo& mask,
+                        bool allow_parts) {
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
         return false;
     if (algo != ISATTN_ALGO_LOOPK && algo != ISATTN_ALGO_LOOPQ && algo != ISATTN_ALGO_SPLIT &&
@@ -80,7 +81,7 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     p.kv_units_bound = 0;
     p.off_units = p.off_info = p.off_partial = off;
     const int64_t n_kv = int64_t(s.batch) * s.heads_k * p.n_kb;
-    if (split && n_kv > 0 && n_kv < kPartModeItems) {
+    if (split && allow_parts && n_kv > 0 && n_kv < kPartModeItems) {
         const int64_t per_item = int64_t(p.G) * p.n_qb;      // query blocks of an item, dense
         const int64_t T = std::max<int64_t>(1, int64_t(std::ceil(std::sqrt(16.0 * double(per_item * n_kv) / 256.0))));
         const int64_t pmax = std::min<int64_t>(kMaxParts, std::max<int64_t>(1, (per_item + T - 1) / T));
@@ -107,10 +108,34 @@ bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan) {
     off = align_up(off + size_t(p.acc0_elems) * sizeof(float), kWsAlign);
     p.off_acc1 = off;
     off = align_up(off + size_t(p.acc1_elems) * sizeof(float), kWsAlign);
-    // SPLIT_DS: a bf16 dS tile for every (b, h, query block, key block)
+    // SPLIT_DS: for a block CSR the K->Q position of every Q->K entry, then a
+    // bf16 dS tile for every kept block of every query head (the slots of
+    // ds_slot in bwd_args.hpp)
+    p.ds_tiles = p.ds_T = p.ds_map_len = 0;
+    if (algo == ISATTN_ALGO_SPLIT_DS) {
+        const int64_t grid = int64_t(p.n_qb) * p.n_kb;
+        const int64_t bh = int64_t(s.batch) * s.heads_q;
+        if (mask.kind == ISATTN_MASK_BLOCK_CSR) {
+            const int64_t hm = mask.heads > 0 ? mask.heads : s.heads_q;
+            p.ds_map_len = mask.nnz >= 0 ? mask.nnz : int64_t(s.batch) * hm * grid;
+            p.ds_tiles = (s.heads_q / hm) * p.ds_map_len;
+        } else if (mask.kind == ISATTN_MASK_DENSE) {
+            p.ds_T = mask.varlen ? grid
+                                 : visible_before(p.n_qb - 1, s.seqlen_q, s.seqlen_k, p.n_kb, mask.causal) +
+                                       visible_kb(p.n_qb - 1, s.seqlen_q, s.seqlen_k, p.n_kb, mask.causal);
+            if (p.n_qb == 0) p.ds_T = 0;
+            p.ds_tiles = bh * p.ds_T;
+        } else {                                     // mask unknown: every block, a map for Hq mask heads
+            p.ds_map_len = bh * grid;
+            p.ds_tiles = bh * grid;
+        }
+    }
+    // the position map and, after it, the int32 overflow flag of a block CSR
+    p.off_dsmap = off;
+    if (algo == ISATTN_ALGO_SPLIT_DS && mask.kind != ISATTN_MASK_DENSE)
+        off = align_up(off + size_t(p.ds_map_len + 1) * sizeof(int32_t), kWsAlign);
     p.off_ds = off;
-    if (algo == ISATTN_ALGO_SPLIT_DS)
-        off = align_up(off + size_t(s.batch) * s.heads_q * p.n_qb * p.n_kb * kBlock * kBlock * 2, kWsAlign);
+    off = align_up(off + size_t(p.ds_tiles) * kBlock * kBlock * 2, kWsAlign);
     p.total = off;
     *plan = p;
     return true;
@@ -123,7 +148,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
                              float softmax_scale, const isattn_tensor_t* dq,
                              const isattn_tensor_t* dk, const isattn_tensor_t* dv, int32_t algo,
                              const void* workspace, size_t workspace_bytes, BwdArgs* args,
-                             BwdPlan* plan, const isattn_varlen_t* varlen) {
+                             BwdPlan* plan, const isattn_varlen_t* varlen, bool allow_parts) {
     if (shape == nullptr) return ISATTN_ERR_NULL;
     const isattn_shape_t s = *shape;
     if (s.batch < 0 || s.seqlen_q < 0 || s.seqlen_k < 0 || s.heads_q < 1 || s.heads_k < 1)
@@ -198,9 +223,25 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
         a.cu_k = varlen->cu_seqlens_k;
     }
 
+    MaskInfo mi;
+    mi.kind = a.mask_kind;
+    mi.heads = a.Hm;
+    mi.nnz = a.mask_kind == ISATTN_MASK_BLOCK_CSR ? mask->nnz : -1;
+    mi.causal = causal != 0;
+    mi.varlen = varlen != nullptr;
     BwdPlan p{};
-    if (!plan_bwd_workspace(s, algo, &p)) return ISATTN_ERR_SHAPE;
-    if (workspace_bytes < p.total) return ISATTN_ERR_WORKSPACE;
+    if (!plan_bwd_workspace(s, algo, &p, mi, allow_parts)) return ISATTN_ERR_SHAPE;
+    if (algo == ISATTN_ALGO_SPLIT_DS) {
+        // the dS tiles: what the workspace holds past the fixed part, at
+        // least what the mask needs
+        if (workspace_bytes < p.off_ds) return ISATTN_ERR_WORKSPACE;
+        const int64_t cap = int64_t((workspace_bytes - p.off_ds) / (size_t(kBlock) * kBlock * 2));
+        if (cap < p.ds_tiles) return ISATTN_ERR_CAPACITY;
+        if (p.ds_tiles >= INT32_MAX) return ISATTN_ERR_UNSUPPORTED;   // tile slots are int32
+        a.ds_cap = int32_t(std::min<int64_t>(cap, INT32_MAX));
+    } else if (workspace_bytes < p.total) {
+        return ISATTN_ERR_WORKSPACE;
+    }
     if (p.total > 0 && workspace == nullptr) return ISATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0) return ISATTN_ERR_WORKSPACE;
 
@@ -230,6 +271,8 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.acc0_elems = p.acc0_elems;
     a.acc1_elems = p.acc1_elems;
+    a.ds_T = int32_t(p.ds_T);
+    a.ds_map_len = p.ds_map_len;
     *args = a;
     *plan = p;
     return ISATTN_OK;

@@ -21,13 +21,30 @@ inline int32_t cdiv(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
 struct BwdPlan {
     int32_t n_qb, n_kb, G, Hm, stat_ld;
-    size_t off_delta, off_lse2, off_order, off_units, off_info, off_partial, off_acc0, off_acc1, off_ds, total;
+    size_t off_delta, off_lse2, off_order, off_units, off_info, off_partial, off_acc0, off_acc1, off_dsmap, off_ds,
+        total;
     int32_t kv_parts_T, kv_units_bound;
     int64_t acc0_elems, acc1_elems;
+    // SPLIT_DS: dS tiles the mask needs (the part from off_ds on), tiles per
+    // (b, h) of a dense mask, length of the Q->K -> K->Q position map
+    int64_t ds_tiles, ds_T, ds_map_len;
+};
+
+// What the workspace plan knows of the mask.  kind < 0: nothing (every
+// block of every head, a position map for heads_q mask heads).
+struct MaskInfo {
+    int32_t kind = -1;      // ISATTN_MASK_DENSE, ISATTN_MASK_BLOCK_CSR, or -1
+    int32_t heads = 0;      // mask heads of a block CSR
+    int64_t nnz = -1;       // blocks of a block CSR, < 0 if unknown
+    bool causal = false;
+    bool varlen = false;
 };
 
 // Workspace layout for isattn_attn_bwd; false if the shape or algo is unusable.
-bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan);
+// allow_parts = false keeps SPLIT's dK/dV pass at one workgroup per item
+// (no fp32 partial slots), whatever the item count.
+bool plan_bwd_workspace(const isattn_shape_t& s, int32_t algo, BwdPlan* plan, const MaskInfo& mask = MaskInfo{},
+                        bool allow_parts = true);
 
 // Full argument check.  On success fills `args` (all but the workspace
 // pointers, which the caller carves from `plan`) and `plan`.
@@ -38,7 +55,7 @@ isattn_status_t validate_bwd(const isattn_shape_t* shape, const isattn_tensor_t*
                              float softmax_scale, const isattn_tensor_t* dq,
                              const isattn_tensor_t* dk, const isattn_tensor_t* dv, int32_t algo,
                              const void* workspace, size_t workspace_bytes, BwdArgs* args,
-                             BwdPlan* plan, const isattn_varlen_t* varlen = nullptr);
+                             BwdPlan* plan, const isattn_varlen_t* varlen = nullptr, bool allow_parts = true);
 
 // Argument check of the forward; on success fills `args`.
 isattn_status_t validate_fwd(const isattn_shape_t* shape, const isattn_tensor_t* q,

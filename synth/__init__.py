@@ -14,5 +14,4 @@ from .gen import (  # noqa: F401
     seed_streams,
     topk_indices,
     make_workload_inputs,
-    stand_in_forward_stats,
 )

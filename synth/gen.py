@@ -192,19 +192,3 @@ def make_workload_inputs(w: Workload, seed: int | None = None, want=("q", "k", "
             out["indices"] = topk_indices(g[5], w.batch, w.seqlen_q, w.seqlen_k,
                                           w.heads_k, w.topk, causal=True)
     return out
-
-
-def stand_in_forward_stats(w: Workload, mean_keys_per_row: float, seed: int | None = None):
-    """Stand-in forward outputs for timing runs that have no forward pass.
-
-    O is bf16 ~ N(0, 1/mean_keys_per_row) and every LSE entry equals
-    ln(mean_keys_per_row) + 1/2, which is the expected log-sum-exp of
-    ``mean_keys_per_row`` unit-variance Gaussian logits.  Backward timing
-    does not depend on these values; they only keep P in a realistic range.
-    """
-    s = (w.seed if seed is None else seed) + 1000003
-    rng = np.random.default_rng(s)
-    n = max(1.0, float(mean_keys_per_row))
-    o = bf16_normal(rng, (w.batch, w.seqlen_q, w.heads_q, w.dim_v), std=1.0 / math.sqrt(n))
-    lse = np.full((w.batch, w.heads_q, w.seqlen_q), math.log(n) + 0.5, dtype=np.float32)
-    return o, lse

@@ -145,7 +145,11 @@ def run_gpu(c: Case, algo: str, mask=None, workspace_fill: int | None = None):
     lse = torch.from_numpy(np.ascontiguousarray(d["lse"])).cuda()
     ws = None
     if workspace_fill is not None:
-        need = isa.attn_bwd_workspace_bytes(c.B, c.Sq, c.Sk, c.Hq, c.Hk, c.Dqk, c.Dv, algo)
+        # sized by the mask's kept blocks: SPLIT_DS gets exactly the dS tiles it needs
+        if mask is not None:
+            mask.nnz()
+        need = isa.attn_bwd_workspace_bytes(c.B, c.Sq, c.Sk, c.Hq, c.Hk, c.Dqk, c.Dv, algo, mask=mask,
+                                            causal=c.causal)
         ws = torch.full((max(need, 1),), workspace_fill, dtype=torch.uint8, device="cuda")
     dq, dk, dv = isa.attn_bwd(q, k, v, o, do, lse, mask=mask, causal=c.causal,
                               softmax_scale=c.scale, algo=algo, workspace=ws)

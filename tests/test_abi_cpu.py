@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
@@ -68,9 +68,10 @@ def test_workspace_sizes(lib):
     # 512 or more dK/dV items: no part mode
     big = shape(B=1, Sq=128, Sk=128 * 256, Hq=2, Hk=2)
     assert ws_bytes(lib, big, 2) == 2 * al(2 * 128 * 4) + al((2 * 256 + 2 * 1) * 4)
-    # SPLIT_DS: SPLIT's parts plus a 128 x 128 bf16 dS tile per (b, h, query block, key block)
-    assert ws_bytes(lib, s, 3) == ws_bytes(lib, s, 2) + al(2 * 4 * 3 * 2 * 128 * 128 * 2)
-    assert ws_bytes(lib, big, 3) == ws_bytes(lib, big, 2) + al(1 * 2 * 1 * 256 * 128 * 128 * 2)
+    # SPLIT_DS sized for any mask: SPLIT's parts, an int32 position map and a 128 x 128 bf16 dS tile
+    # per (b, h, query block, key block)
+    assert ws_bytes(lib, s, 3) == ws_bytes(lib, s, 2) + al(2 * 4 * 3 * 2 * 4 + 4) + al(2 * 4 * 3 * 2 * 128 * 128 * 2)
+    assert ws_bytes(lib, big, 3) == ws_bytes(lib, big, 2) + al(2 * 256 * 4 + 4) + al(1 * 2 * 1 * 256 * 128 * 128 * 2)
     assert ws_bytes(lib, s, 7) == 0
     assert lib.isattn_attn_bwd_workspace_bytes(None, 0) == 0
     # converter: presence B*H*nQB*nKB bytes + row and column counts
@@ -146,7 +147,7 @@ def test_bwd_validation_errors(lib):
     c = Call(lib, algo=2); c.ws_bytes -= 1; assert c() == WS
     c = Call(lib, algo=3); c.views["k"].stride_s = 1 << 22; c.views["k"].stride_b = 256 << 22
     assert c() == STRIDE
-    c = Call(lib, algo=3); c.ws_bytes -= 1; assert c() == WS
+    c = Call(lib, algo=3); c.ws_bytes = ws_bytes(lib, shape(), 2) - 1; assert c() == WS
     c = Call(lib, algo=3); c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, None, None); assert c() == NULL
 
 
@@ -250,3 +251,82 @@ def test_token_bits_validation_errors(lib):
     assert call(cq=FAKE) == NULL
     assert call(B=-1) == SHAPE
     assert call(bits=FAKE + 4) == STRIDE
+
+
+def ws_mask(lib, s, algo, mask=None, causal=0, varlen=0):
+    return lib.isattn_attn_bwd_workspace_bytes_mask(ctypes.byref(s), algo, ctypes.byref(mask) if mask else None,
+                                                    causal, varlen)
+
+
+def brute_visible_blocks(Sq, Sk, causal):
+    """Blocks of one head with a visible pair (bottom-right causal), by enumeration."""
+    n = 0
+    for qb in range(-(-Sq // 128)):
+        for kb in range(-(-Sk // 128)):
+            if not causal:
+                n += 1
+                continue
+            last_row = min(qb * 128 + 127, Sq - 1)
+            n += kb * 128 <= last_row + Sk - Sq
+    return n
+
+
+def test_split_ds_workspace_by_kept_blocks(lib):
+    """SPLIT_DS sizes its dS store by the kept blocks: R * nnz tiles for a
+    block CSR (R query heads per mask head) plus an nnz-entry position map
+    and an overflow flag,
+    B * Hq * (visible blocks of a head) for dense and causal masks, the whole
+    block grid for a dense mask over packed sequences."""
+    al = lambda x: (x + 255) // 256 * 256
+    tile = 128 * 128 * 2
+    for (Sq, Sk) in ((300, 200), (200, 300), (1024, 1024), (1000, 130), (130, 1000), (128, 4096), (257, 129)):
+        s = shape(B=2, Sq=Sq, Sk=Sk, Hq=4, Hk=2)
+        fixed = ws_bytes(lib, s, 2)
+        nq, nk = -(-Sq // 128), -(-Sk // 128)
+        for causal in (0, 1):
+            vis = brute_visible_blocks(Sq, Sk, causal)
+            assert ws_mask(lib, s, 3, None, causal) == fixed + al(2 * 4 * vis * tile), (Sq, Sk, causal)
+            assert ws_mask(lib, s, 3, None, causal, varlen=1) == fixed + al(2 * 4 * nq * nk * tile)
+            for hm in (1, 2, 4):
+                m = _abi.Mask(1, 128, 128, hm, FAKE, FAKE, FAKE, FAKE, None, 5)
+                assert ws_mask(lib, s, 3, m, causal) == fixed + al(5 * 4 + 4) + al((4 // hm) * 5 * tile)
+                unknown = _abi.Mask(1, 128, 128, hm, FAKE, FAKE, FAKE, FAKE)     # nnz not given: every block
+                grid = 2 * hm * nq * nk
+                assert ws_mask(lib, s, 3, unknown, causal) == fixed + al(grid * 4 + 4) + al((4 // hm) * grid * tile)
+        for algo in (0, 1, 2):                     # the other algorithms do not depend on the mask
+            assert ws_mask(lib, s, algo, None, 1) == ws_bytes(lib, s, algo)
+    # the benchmark's block-sparse workload: 34,112 kept blocks of 16 mask heads -> 1.12 GB, not 4.3 GB
+    s = shape(B=2, Sq=8192, Sk=8192, Hq=16, Hk=16)
+    m = _abi.Mask(1, 128, 128, 16, FAKE, FAKE, FAKE, FAKE, None, 34112)
+    assert ws_mask(lib, s, 3, m) - ws_bytes(lib, s, 2) == al(34112 * 4 + 4) + 34112 * tile
+    # the 32K causal d192 workload: 526,336 visible blocks of 16 heads -> 17.2 GB, not 34.4 GB
+    s = shape(B=1, Sq=32768, Sk=32768, Hq=16, Hk=16, Dqk=192, Dv=128)
+    assert ws_mask(lib, s, 3, None, 1) - ws_bytes(lib, s, 2) == 526336 * tile
+    assert ws_mask(lib, s, 3, _abi.Mask(7, 128, 128, 1, None, None, None, None)) == 0
+    assert ws_mask(lib, s, 3, _abi.Mask(1, 128, 128, 3, FAKE, FAKE, FAKE, FAKE)) == 0
+
+
+def test_split_ds_capacity_checked_before_launch(lib):
+    """A workspace holding fewer dS tiles than the mask needs is rejected
+    with ISATTN_ERR_CAPACITY before any launch (no GPU here: a call that
+    passed every check would fail to launch)."""
+    tile = 128 * 128 * 2
+    # block CSR, 2 mask heads, 6 kept blocks given by the caller
+    m = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, FAKE, FAKE, None, 6)
+    c = Call(lib, algo=3, Sq=512, Sk=512)
+    exact = ws_mask(lib, c.shape, 3, m)
+    c.mask = m
+    c.ws_bytes = exact - tile                      # one tile short
+    assert c() == CAP
+    c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, FAKE, FAKE, None, 7)   # more blocks than the workspace holds
+    c.ws_bytes = exact
+    assert c() == CAP
+    c.mask = _abi.Mask(1, 128, 128, 2, FAKE, FAKE, FAKE, FAKE)           # count unknown: needs every block
+    assert c() == CAP
+    # dense causal: every visible block of every head
+    c = Call(lib, algo=3, Sq=512, Sk=512)
+    c.causal = 1
+    c.ws_bytes = ws_mask(lib, c.shape, 3, None, 1) - 1
+    assert c() == CAP
+    c.ws_bytes = ws_bytes(lib, c.shape, 2) - 1     # not even the fixed part
+    assert c() == WS

@@ -150,3 +150,37 @@ def test_split_is_bit_reproducible(name, algo):
         again = run_gpu(c, algo, mask, workspace_fill=fill)
         for n, x, y in zip(("dq", "dk", "dv"), first, again):
             assert np.array_equal(x, y), f"{algo} {name}: {n} differs between calls"
+
+
+def test_split_ds_undercounted_blocks_write_nothing():
+    """A block CSR whose host-side block count is below the true one (the
+    workspace then holds too few dS tiles): the position-map kernel flags it
+    and both SPLIT_DS passes compute nothing, so the outputs keep what they
+    held and nothing lands past the workspace; the same call with the true
+    count is exact again.  (The condition is set from the host; every kernel
+    exits normally.)"""
+    import torch
+    import index_sparse_attention_amd as isa
+    from tests.gpu_helpers import bits_to_dev, dev_to_f64
+    c = get_case("block_h1_gqa_causal")
+    d = c.data
+    mask = gpu_mask(c)
+    true_nnz = mask.nnz()
+    q, k, v = bits_to_dev(d["q"]), bits_to_dev(d["k"]), bits_to_dev(d["v"])
+    o, do = bits_to_dev(d["o"]), bits_to_dev(d["do"])
+    lse = torch.from_numpy(np.ascontiguousarray(d["lse"])).cuda()
+    mask.nnz_host = true_nnz - 1
+    need = isa.attn_bwd_workspace_bytes(c.B, c.Sq, c.Sk, c.Hq, c.Hk, c.Dqk, c.Dv, "split_ds", mask=mask,
+                                        causal=c.causal)
+    # a guard region after the workspace: must stay untouched
+    buf = torch.full((need + (1 << 20),), 0x5A, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.full_like(t, 3.0) for t in (q, k, v))
+    isa.attn_bwd(q, k, v, o, do, lse, mask=mask, causal=c.causal, softmax_scale=c.scale, algo="split_ds",
+                 dq=dq, dk=dk, dv=dv, workspace=buf[:need])
+    torch.cuda.synchronize()
+    assert torch.all(dq == 3.0) and torch.all(dk == 3.0) and torch.all(dv == 3.0)
+    assert torch.all(buf[need:] == 0x5A), "a write landed past the workspace"
+    mask.nnz_host = true_nnz
+    got = run_gpu(c, "split_ds", mask, workspace_fill=0xFF)
+    for n, g, r in zip(("dq", "dk", "dv"), got, oracle_grads(c)):
+        assert_close(n, g, r)

@@ -54,10 +54,24 @@ def test_sink_mask_grouped_order(algo):
     log(f"sink mask {algo}")
     mask = isa.block_mask_to_csr(torch.from_numpy(d["presence"]).cuda())
     assert_csr_equal(csr_to_host(mask), d["csr"])
-    dq, dk, dv = isa.attn_bwd(bits_to_dev(d["q"]), bits_to_dev(d["k"]), bits_to_dev(d["v"]), bits_to_dev(d["o"]),
-                              bits_to_dev(d["do"]), torch.from_numpy(d["lse"]).cuda(), mask=mask, causal=False,
-                              softmax_scale=d["scale"], algo=algo)
+    q, k, v = bits_to_dev(d["q"]), bits_to_dev(d["k"]), bits_to_dev(d["v"])
+    # outputs and workspace start as NaN: a block no work item writes stays NaN
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    ws = torch.full((isa.attn_bwd_workspace_bytes(B, S, S, H, H, D, D, algo),), 0xFF, dtype=torch.uint8,
+                    device=q.device)
+    isa.attn_bwd(q, k, v, bits_to_dev(d["o"]), bits_to_dev(d["do"]), torch.from_numpy(d["lse"]).cuda(), mask=mask,
+                 causal=False, softmax_scale=d["scale"], algo=algo, dq=dq, dk=dk, dv=dv, workspace=ws)
     torch.cuda.synchronize()
+    # the work order: each XCD's slice of each pass is a permutation of its item range
+    n_items = B * H * (S // 128)
+    stat_bytes = B * H * S * 4                          # delta, then lse * log2(e); 256-byte multiples here
+    order = ws[2 * stat_bytes:2 * stat_bytes + 8 * n_items].view(torch.int32).cpu().numpy()
+    per = -(-n_items // 8)
+    for pass_, base in (("dK/dV", 0), ("dQ", n_items)):
+        for x in range(8):
+            lo, hi = min(n_items, x * per), min(n_items, (x + 1) * per)
+            got = np.sort(order[base + lo:base + hi])
+            assert np.array_equal(got, np.arange(lo, hi)), f"{pass_} order of XCD {x} is not a permutation"
     dq, dk, dv = dev_to_f64(dq), dev_to_f64(dk), dev_to_f64(dv)
     rq, rk, rv = d["ref"]
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):

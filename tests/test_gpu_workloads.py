@@ -23,8 +23,8 @@ CHECKED = {
     "dense_mha_s256_d64": None,
     "causal_gqa_s2k_d128": None,
     "blocksparse_mha_s8k_d128": [0, 13],
-    "indexsparse_gqa_s16k_d128": [0, 1],
-    "causal_mha_s32k_d192": [5],
+    "indexsparse_gqa_s16k_d128": [0, 1, 8],        # KV heads 0 and 1
+    "causal_mha_s32k_d192": [5, 15],
 }
 
 _cache = {}
@@ -77,6 +77,7 @@ def test_workload_full_size(name, algo):
     mask = gpu_mask(w, d)
     if mask is not None:
         assert_csr_equal(csr_to_host(mask), d["csr"])
+    # the workspace is sized by the kept blocks (SPLIT_DS: exactly the dS tiles the mask needs)
     dq, dk, dv = isa.attn_bwd(bits_to_dev(d["q"]), bits_to_dev(d["k"]), bits_to_dev(d["v"]),
                               bits_to_dev(d["o"]), bits_to_dev(d["do"]),
                               torch.from_numpy(d["lse"]).cuda(), mask=mask, causal=w.causal,
