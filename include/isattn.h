@@ -35,7 +35,8 @@ typedef enum isattn_status {
     ISATTN_ERR_MASK = 5,          /* malformed mask descriptor                          */
     ISATTN_ERR_WORKSPACE = 6,     /* workspace missing, too small or misaligned         */
     ISATTN_ERR_CAPACITY = 7,      /* CSR column or dS tile capacity below what is needed */
-    ISATTN_ERR_HIP = 8            /* a HIP runtime call or kernel launch failed         */
+    ISATTN_ERR_HIP = 8,           /* a HIP runtime call or kernel launch failed         */
+    ISATTN_ERR_SCRATCH = 9        /* needs more than the static scratch of _noalloc     */
 } isattn_status_t;
 
 /* Problem sizes.  Token-major layout (row = token), as the (total_q, NHK, topk)
@@ -170,6 +171,33 @@ isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape,
                                 const isattn_tensor_t* dv,
                                 int32_t algo, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * isattn_attn_bwd with algo ISATTN_ALGO_SPLIT and no workspace argument.  Its
+ * workspace is a static device array of ISATTN_NOALLOC_SCRATCH_BYTES (64
+ * MiB) inside the library; each GPU holds its own copy from its first call
+ * until the process ends, and nothing is allocated or freed per call (no
+ * hipMalloc, no hipFree).  The dK/dV pass runs one workgroup per (b, KV head,
+ * key block) item (no part mode, so no fp32 partials), which bounds the
+ * scratch to delta and lse * log2(e), fp32 [B,Hq,ceil(Sq/128)*128] each, and
+ * the int32 work order: B*Hq*ceil(Sq/128)*128*8 + 4*(B*Hk*ceil(Sk/128) +
+ * B*Hq*ceil(Sq/128)) bytes, 256-byte aligned parts.  A problem needing more
+ * returns ISATTN_ERR_SCRATCH before anything is enqueued.  Every call on a
+ * GPU uses that GPU's one scratch array, whose contents (left over from the
+ * previous call) need no clearing; calls that overlap in time on one GPU --
+ * on different streams or from different threads without ordering -- race
+ * on it and give undefined results.  Other arguments, errors and results as
+ * isattn_attn_bwd with ISATTN_ALGO_SPLIT. */
+#define ISATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+isattn_status_t isattn_attn_bwd_noalloc(const isattn_shape_t* shape,
+                                        const isattn_tensor_t* q, const isattn_tensor_t* k,
+                                        const isattn_tensor_t* v, const isattn_tensor_t* o,
+                                        const isattn_tensor_t* dO, const float* lse,
+                                        const isattn_mask_t* mask_desc, int32_t causal,
+                                        float softmax_scale,
+                                        const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                                        const isattn_tensor_t* dv, void* stream);
 
 /* Attention forward on the same mask descriptor: the outputs the backward
  * consumes ([P1] Summary: the backward recomputes P from the forward's LSE;

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     BlockMask,
     Timer,
     attn_bwd,
+    attn_bwd_noalloc,
     attn_fwd,
     attn_bwd_workspace_bytes,
     choose_algo,

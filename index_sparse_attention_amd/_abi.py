@@ -10,8 +10,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisattn.s
 STATUS = {
     0: "ISATTN_OK", 1: "ISATTN_ERR_NULL", 2: "ISATTN_ERR_SHAPE", 3: "ISATTN_ERR_STRIDE_ALIGN",
     4: "ISATTN_ERR_UNSUPPORTED", 5: "ISATTN_ERR_MASK", 6: "ISATTN_ERR_WORKSPACE",
-    7: "ISATTN_ERR_CAPACITY", 8: "ISATTN_ERR_HIP",
+    7: "ISATTN_ERR_CAPACITY", 8: "ISATTN_ERR_HIP", 9: "ISATTN_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MASK_DENSE, MASK_BLOCK_CSR = 0, 1
 ALGO_LOOPK, ALGO_LOOPQ, ALGO_SPLIT, ALGO_SPLIT_DS = 0, 1, 2, 3
 
@@ -51,6 +52,7 @@ SIGNATURES = {
     "isattn_attn_bwd_workspace_bytes_mask": (c_size_t, [POINTER(Shape), c_int32, POINTER(Mask), c_int32, c_int32]),
     "isattn_attn_bwd": (c_int32, _BWD_ARGS),
     "isattn_attn_bwd_timed": (c_int32, _BWD_ARGS + [c_void_p]),
+    "isattn_attn_bwd_noalloc": (c_int32, _BWD_ARGS[:13] + [c_void_p]),
     "isattn_attn_fwd": (c_int32, [POINTER(Shape), _T, _T, _T, POINTER(Mask), c_int32, c_float, _T, c_void_p,
                                   c_void_p]),
     "isattn_attn_bwd_varlen": (c_int32, [POINTER(Shape), POINTER(Varlen)] + _BWD_ARGS[1:]),

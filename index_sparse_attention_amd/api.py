@@ -234,6 +234,30 @@ def attn_bwd(q, k, v, o, do, lse, mask: BlockMask | None = None, causal: bool = 
     return dq, dk, dv
 
 
+def attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, mask: BlockMask | None = None, causal: bool = False,
+                     softmax_scale: float | None = None, stream=None):
+    """``attn_bwd`` with algo "split" through isattn_attn_bwd_noalloc: the
+    library allocates nothing (its workspace is a static 64 MiB device array
+    per GPU) and this wrapper allocates nothing either -- the caller passes
+    dq, dk, dv.  Calls that overlap on one GPU race on the shared scratch.
+    Returns (dq, dk, dv)."""
+    lib = _abi.load()
+    B, Sq, Sk, Hq, Hk, Dqk, Dv = _dims(q, k, v, None)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    shape = _abi.Shape(B, Sq, Sk, Hq, Hk, Dqk, Dv)
+    views = [_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
+                                      (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    m = mask._abi() if mask is not None else _DENSE()
+    args = [ctypes.byref(x) for x in views[:5]] + [
+        lse.data_ptr(), ctypes.byref(m), int(bool(causal)), float(softmax_scale)] + [
+        ctypes.byref(x) for x in views[5:]] + [_stream_ptr(stream)]
+    _abi.check(lib.isattn_attn_bwd_noalloc(ctypes.byref(shape), *args), "isattn_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
 def attn_fwd(q, k, v, mask: BlockMask | None = None, causal: bool = False, softmax_scale: float | None = None,
              o=None, lse=None, stream=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
              max_seqlen_k=None):

@@ -3,12 +3,21 @@
 // enqueues the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "../../include/isattn.h"
 #include "kernels.hpp"
 #include "validate.hpp"
+
+// Scratch of isattn_attn_bwd_noalloc: the workspace of its SPLIT call, a
+// static device array of ISATTN_NOALLOC_SCRATCH_BYTES that every GPU the
+// library runs on holds from the first such call until the process ends.
+// Host code never uses its name as an address: each device's copy is looked
+// up once with hipGetSymbolAddress (scratch_address below) and that pointer
+// is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[ISATTN_NOALLOC_SCRATCH_BYTES];
 
 struct isattn_timer {
     int32_t capacity = 0;
@@ -29,6 +38,25 @@ isattn_status_t record(isattn_timer_t* t, int slot, int k, hipStream_t s) {
     return hipEventRecord(t->ev[size_t(slot) * kTimerEvents + k], s) == hipSuccess ? ISATTN_OK : ISATTN_ERR_HIP;
 }
 
+// Address of the current device's copy of `scratch`, looked up on the
+// device's first call (with that device current) and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+isattn_status_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ISATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ISATTN_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return ISATTN_OK;
+}
+
 isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t* q,
                               const isattn_tensor_t* k, const isattn_tensor_t* v,
                               const isattn_tensor_t* o, const isattn_tensor_t* dO, const float* lse,
@@ -36,11 +64,11 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
                               const isattn_tensor_t* dq, const isattn_tensor_t* dk,
                               const isattn_tensor_t* dv, int32_t algo, void* workspace,
                               size_t workspace_bytes, void* stream, isattn_timer_t* timer,
-                              const isattn_varlen_t* varlen = nullptr) {
+                              const isattn_varlen_t* varlen = nullptr, bool allow_parts = true) {
     BwdArgs a{};
     BwdPlan plan{};
     isattn_status_t st = validate_bwd(shape, q, k, v, o, dO, lse, mask, causal, softmax_scale, dq, dk,
-                                      dv, algo, workspace, workspace_bytes, &a, &plan, varlen);
+                                      dv, algo, workspace, workspace_bytes, &a, &plan, varlen, allow_parts);
     if (st != ISATTN_OK) return st;
     if (a.B == 0) return ISATTN_OK;
     a.delta = reinterpret_cast<float*>(ws_at(workspace, plan.off_delta));
@@ -127,6 +155,27 @@ isattn_status_t isattn_attn_bwd(const isattn_shape_t* shape, const isattn_tensor
                                 size_t workspace_bytes, void* stream) {
     return attn_bwd_impl(shape, q, k, v, o, dO, lse, mask_desc, causal, softmax_scale, dq, dk, dv, algo,
                          workspace, workspace_bytes, stream, nullptr);
+}
+
+isattn_status_t isattn_attn_bwd_noalloc(const isattn_shape_t* shape, const isattn_tensor_t* q,
+                                        const isattn_tensor_t* k, const isattn_tensor_t* v,
+                                        const isattn_tensor_t* o, const isattn_tensor_t* dO, const float* lse,
+                                        const isattn_mask_t* mask_desc, int32_t causal, float softmax_scale,
+                                        const isattn_tensor_t* dq, const isattn_tensor_t* dk,
+                                        const isattn_tensor_t* dv, void* stream) {
+    // the size check needs no device: SPLIT's workspace without part mode
+    if (shape != nullptr) {
+        BwdPlan p{};
+        if (plan_bwd_workspace(*shape, ISATTN_ALGO_SPLIT, &p, MaskInfo{}, false) &&
+            p.total > size_t(ISATTN_NOALLOC_SCRATCH_BYTES))
+            return ISATTN_ERR_SCRATCH;
+    }
+    void* ws = nullptr;
+    isattn_status_t st = scratch_address(&ws);
+    if (st != ISATTN_OK) return st;
+    st = attn_bwd_impl(shape, q, k, v, o, dO, lse, mask_desc, causal, softmax_scale, dq, dk, dv, ISATTN_ALGO_SPLIT,
+                       ws, ISATTN_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, false);
+    return st == ISATTN_ERR_WORKSPACE ? ISATTN_ERR_SCRATCH : st;
 }
 
 isattn_status_t isattn_attn_bwd_varlen(const isattn_shape_t* shape, const isattn_varlen_t* varlen,
@@ -316,6 +365,7 @@ const char* isattn_status_string(isattn_status_t status) {
         case ISATTN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case ISATTN_ERR_CAPACITY: return "CSR column or dS tile capacity too small";
         case ISATTN_ERR_HIP: return "HIP runtime error";
+        case ISATTN_ERR_SCRATCH: return "problem needs more than the static no-allocation scratch";
     }
     return "unknown status";
 }

@@ -12,7 +12,7 @@ from index_sparse_attention_amd import _abi
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "isattn.h")
 
-OK, NULL, SHAPE, STRIDE, UNSUP, MASK, WS, CAP = 0, 1, 2, 3, 4, 5, 6, 7
+OK, NULL, SHAPE, STRIDE, UNSUP, MASK, WS, CAP, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7, 9
 FAKE = 0x7F0000000000          # aligned dummy device address: never dereferenced on a failed check
 
 
@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
         assert n in _abi.SIGNATURES, f"{n} missing from the Python declarations"
@@ -38,8 +38,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.isattn_version().decode().count(".") == 2
-    for code in range(9):
-        assert lib.isattn_status_string(code)
+    for code in range(10):
+        assert lib.isattn_status_string(code) != b"unknown status"
     assert lib.isattn_status_string(99) == b"unknown status"
 
 
@@ -330,3 +330,20 @@ def test_split_ds_capacity_checked_before_launch(lib):
     assert c() == CAP
     c.ws_bytes = ws_bytes(lib, c.shape, 2) - 1     # not even the fixed part
     assert c() == WS
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """isattn_attn_bwd_noalloc checks the size against its static scratch
+    before touching a device: past 64 MiB it returns ISATTN_ERR_SCRATCH."""
+    def call(**kw):
+        c = Call(lib, algo=2, **kw)
+        v = c.views
+        return lib.isattn_attn_bwd_noalloc(ctypes.byref(c.shape), ctypes.byref(v["q"]), ctypes.byref(v["k"]),
+                                           ctypes.byref(v["v"]), ctypes.byref(v["o"]), ctypes.byref(v["do"]),
+                                           c.lse, None, 0, 0.125, ctypes.byref(v["dq"]), ctypes.byref(v["dk"]),
+                                           ctypes.byref(v["dv"]), None)
+    # delta + lse2 = 8 bytes per padded query row: 8 Mi rows need 64 MiB plus the work order
+    assert call(B=1, Sq=1 << 20, Sk=128, Hq=8, Hk=8) == SCRATCH
+    assert call(B=4, Sq=1 << 18, Sk=256, Hq=8, Hk=1) == SCRATCH
+    # 32K tokens x 16 heads (4.3 MiB) fits; the call then needs a GPU, which this host lacks
+    assert call(B=1, Sq=32768, Sk=32768, Hq=16, Hk=16) != SCRATCH
