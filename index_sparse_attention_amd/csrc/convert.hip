@@ -9,7 +9,8 @@
 //
 // Kernels:
 //   k_index_presence : one workgroup per (qb, hk, b); streams the block's
-//                      block_q x topk indices with 16-byte loads, sets bits of
+//                      block_q x topk indices with 16-byte loads (the next
+//                      batch in flight while one is marked), sets bits of
 //                      an LDS bitmap (test-then-set keeps LDS atomics rare once
 //                      a block is marked), writes the uint8 presence row and
 //                      its popcount.  HBM-bound on the index read.
@@ -27,7 +28,8 @@
 namespace isattn {
 namespace {
 
-constexpr int kPresThreads = 512;
+constexpr int kPresThreads = 1024;
+constexpr int kPresBatch = 4;                      // 16-byte index loads per thread per batch
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 4;
 
@@ -72,34 +74,45 @@ __global__ __launch_bounds__(kPresThreads) void k_index_presence(
     const int64_t row_stride = int64_t(nhk) * topk;
     const int32_t* base = idx + (first + r0) * row_stride + int64_t(hk) * topk;
     if (vec4) {
+        // 16-byte loads in batches of kPresBatch per thread, the next batch in
+        // flight while the current one is marked (two register buffers);
+        // slots past the block's indices read as -1 (nothing selected)
         const int per_row = topk >> 2;
         const int total = rows * per_row;
-        int u = tid;
-        for (; u + 3 * kPresThreads < total; u += 4 * kPresThreads) {
-            int4 x[4];
+        const int pr_shift = (per_row & (per_row - 1)) == 0 ? __builtin_ctz(unsigned(per_row)) : -1;
+        auto fetch = [&](int u0, int4 (&x)[kPresBatch]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int uu = u + j * kPresThreads;
-                const int rr = uu / per_row;
-                const int c = uu - rr * per_row;
-                x[j] = *reinterpret_cast<const int4*>(base + rr * row_stride + 4 * c);
+            for (int j = 0; j < kPresBatch; ++j) {
+                const int uu = u0 + j * kPresThreads;
+                x[j] = int4{-1, -1, -1, -1};
+                if (uu < total) {
+                    const int rr = pr_shift >= 0 ? uu >> pr_shift : uu / per_row;
+                    const int c = uu - rr * per_row;
+                    x[j] = *reinterpret_cast<const int4*>(base + rr * row_stride + 4 * c);
+                }
             }
+        };
+        auto mark = [&](const int4 (&x)[kPresBatch]) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kPresBatch; ++j) {
                 mark_key(bits, x[j].x, Sk, bk, bk_shift);
                 mark_key(bits, x[j].y, Sk, bk, bk_shift);
                 mark_key(bits, x[j].z, Sk, bk, bk_shift);
                 mark_key(bits, x[j].w, Sk, bk, bk_shift);
             }
-        }
-        for (; u < total; u += kPresThreads) {
-            const int rr = u / per_row;
-            const int c = u - rr * per_row;
-            const int4 x = *reinterpret_cast<const int4*>(base + rr * row_stride + 4 * c);
-            mark_key(bits, x.x, Sk, bk, bk_shift);
-            mark_key(bits, x.y, Sk, bk, bk_shift);
-            mark_key(bits, x.z, Sk, bk, bk_shift);
-            mark_key(bits, x.w, Sk, bk, bk_shift);
+        };
+        constexpr int kStep = kPresBatch * kPresThreads;
+        int4 xa[kPresBatch], xb[kPresBatch];
+        int u = tid;
+        fetch(u, xa);
+        while (u < total) {
+            fetch(u + kStep, xb);
+            mark(xa);
+            u += kStep;
+            if (u >= total) break;
+            fetch(u + kStep, xa);
+            mark(xb);
+            u += kStep;
         }
     } else {
         const int total = rows * topk;
