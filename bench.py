@@ -167,6 +167,24 @@ def cpu_baseline(w, data, budget_s=20.0, max_slices=64):
     }
 
 
+def cpu_converter(w, data):
+    """The oracle's mask conversion on the host (NumPy), for the GPU
+    converter's comparison: presence -> CSR (block masks) or indices ->
+    presence -> CSR (index masks), whole workload, one run."""
+    import oracle
+    if w.mask == "block":
+        t0 = time.perf_counter()
+        oracle.presence_to_csr(data["presence"])
+        what = "presence -> CSR"
+    elif w.mask == "index":
+        t0 = time.perf_counter()
+        oracle.presence_to_csr(oracle.indices_to_presence(data["indices"], w.batch, w.seqlen_q, w.seqlen_k))
+        what = "indices -> presence -> CSR"
+    else:
+        return None
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 2), "what": what, "kind": "oracle"}
+
+
 def _head_flop(omask, w, h):
     """FLOP of one (batch, query head) slice over its computed blocks, with the
     convention of the GPU figure (whole 128x128 blocks, ragged edges cut)."""
@@ -348,6 +366,27 @@ def main():
                                                    w.dim_v, mask=m0, causal=w.causal, device=dev) != "split_ds":
         log("split_ds: the dS store does not fit the free device memory; timing split instead")
         args.algo = "split"
+    def time_atomic_ceiling(n_add=1 << 27, n_dst=1 << 24, reps=5):
+        """fp32 global atomic adds per second of a plain library kernel (torch
+        index_add_: one atomic add per source element, consecutive elements to
+        consecutive destinations), the reference rate for the atomic
+        reductions of LoopK (dK/dV) and LoopQ (dQ)."""
+        dst = torch.zeros(n_dst, dtype=torch.float32, device=dev)
+        src = torch.ones(n_add, dtype=torch.float32, device=dev)
+        idx = torch.arange(n_add, dtype=torch.int64, device=dev) % n_dst
+        dst.index_add_(0, idx, src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.index_add_(0, idx, src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        del dst, src, idx
+        return {"g_atomics_per_s": round(n_add / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4),
+                "adds": n_add, "dst_elems": n_dst, "what": "torch index_add_ fp32"}
+
     log(f"timing {args.algo}: {args.warmup} warmup + {args.steps} steps")
     r = run(args.algo, args.steps, args.warmup)
     pairs = kept * 128 * 128
@@ -360,6 +399,9 @@ def main():
                      "executed_mfma_tflops": round(pairs * exe_pp / (ms * 1e-3) / 1e12, 3)})
         if name == "k_bwd_dq_ds":                  # streams 2 bytes of stored dS per pair
             kern[-1]["ds_read_gbs"] = round(pairs * 2 / (ms * 1e-3) / 1e9, 1)
+        if name in ("k_bwd_loopk", "k_bwd_loopq"):  # fp32 atomic adds: dK+dV per key (LoopK), dQ per query (LoopQ)
+            per_pair = (w.dim_qk + w.dim_v) / 128 if name == "k_bwd_loopk" else w.dim_qk / 128
+            kern[-1]["g_atomics_per_s"] = round(pairs * per_pair / (ms * 1e-3) / 1e9, 1)
     dom = max(kern, key=lambda k: k["avg_launch_ms"])
     traffic = load_traffic(f"{dom['kernel']}:{args.algo}:{w.name}")
     out = {
@@ -391,6 +433,7 @@ def main():
         "converter": time_converter(),
         "forward": time_forward(),
         "indexer_topk": time_topk(),
+        "atomic_ceiling": time_atomic_ceiling(),
     }
     rows_q = w.batch * w.seqlen_q * w.heads_q
     rows_k = w.batch * w.seqlen_k * w.heads_k
@@ -412,14 +455,20 @@ def main():
         out["compare"] = []
         for other in [a for a in ("split", "split_ds", "loopk", "loopq") if a != args.algo]:
             log(f"timing {other} for comparison")
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()                # the previous run's workspace back to the device first
             r2 = run(other, max(10, args.steps // 2), 3)
             out["compare"].append({"algo": other, "ms_per_step": round(r2["ms_per_step"], 4),
                                    "value": round(flop / (r2["ms_per_step"] * 1e-3) / 1e12, 3),
                                    "stages_ms": [round(x, 4) for x in r2["stage_ms"]],
                                    "step_ms": {k: round(v, 4) for k, v in r2["step_ms"].items()}})
+            if other in ("loopk", "loopq"):           # fp32 atomic adds per second of the main kernel
+                n_at = pairs * ((w.dim_qk + w.dim_v) if other == "loopk" else w.dim_qk) / 128
+                out["compare"][-1]["g_atomics_per_s"] = round(n_at / (r2["stage_ms"][1] * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, data)
+        out["converter_cpu"] = cpu_converter(w, data)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
