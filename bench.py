@@ -446,7 +446,7 @@ def main():
         pre_bytes += rows_q * w.dim_qk * 4
         post_bytes = rows_q * w.dim_qk * (4 + 2)
     elif args.algo == "split_ds":
-        pre_bytes += rows_q * 4                    # lse * log2(e)
+        pre_bytes += rows_q * 4 * 2                # lse read, lse * log2(e) written
     out["prepost_gbs"] = {"pre": round(pre_bytes / (r["stage_ms"][0] * 1e-3) / 1e9, 1),
                           "post": (round(post_bytes / (r["stage_ms"][3] * 1e-3) / 1e9, 1)
                                    if post_bytes else None),

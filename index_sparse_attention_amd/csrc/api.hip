@@ -92,11 +92,12 @@ isattn_status_t attn_bwd_impl(const isattn_shape_t* shape, const isattn_tensor_t
     if (timer != nullptr) slot = timer->recorded % timer->capacity;
 
     if ((st = record(timer, slot, 0, s)) != ISATTN_OK) return st;
-    // SPLIT needs no preprocess launch: its dQ pass, which runs first,
-    // computes delta and lse2 for the dK/dV pass
-    if (algo != ISATTN_ALGO_SPLIT && launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
-    if (split && launch_split_schedule(a, s) != hipSuccess) return ISATTN_ERR_HIP;
-    if (algo == ISATTN_ALGO_SPLIT_DS && launch_ds_map(a, s) != hipSuccess) return ISATTN_ERR_HIP;
+    // LoopK / LoopQ: delta rows and zeroed accumulators.  SPLIT and SPLIT_DS:
+    // one set-up launch (work order; for SPLIT_DS also the delta and lse2
+    // rows and, with a block CSR, the dS position map).  SPLIT computes delta
+    // and lse2 in its dQ pass, which runs first.
+    if (!split && launch_preprocess(a, algo, s) != hipSuccess) return ISATTN_ERR_HIP;
+    if (split && launch_split_setup(a, algo == ISATTN_ALGO_SPLIT_DS, s) != hipSuccess) return ISATTN_ERR_HIP;
     if ((st = record(timer, slot, 1, s)) != ISATTN_OK) return st;
     hipError_t e;
     if (algo == ISATTN_ALGO_LOOPK) e = launch_loopk(a, s);

@@ -7,7 +7,7 @@
 
 namespace isattn {
 
-// delta = rowsum(dO * O) and zeroing of the fp32 accumulators of `algo`.
+// LoopK / LoopQ: delta = rowsum(dO * O) and zeroing of the fp32 accumulators of `algo`.
 hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s);
 // fp32 accumulators -> bf16 outputs (x softmax_scale for dK / dQ).
 hipError_t launch_postprocess(const BwdArgs& a, int algo, hipStream_t s);
@@ -17,14 +17,15 @@ hipError_t launch_loopq(const BwdArgs& a, hipStream_t s);
 // Atomic-free two-pass backward: dK/dV pass (key-outer), dQ pass (query-outer).
 // Attention forward: O and LSE.
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
-// Work order of the two passes (into a.order); runs before either.
-hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s);
+// Set-up of the two-pass backward, before either pass: the work order of
+// both (into a.order); for SPLIT_DS with a block CSR the K->Q position of
+// every Q->K entry (a.ds_map) and the overflow flag; with `delta` the delta
+// and lse2 rows.  One launch.
+hipError_t launch_split_setup(const BwdArgs& a, bool delta, hipStream_t s);
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);
 // SPLIT_DS second pass: dQ from the dS tiles the dK/dV pass stored.
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s);
-// SPLIT_DS with a block CSR: the K->Q position of every Q->K entry (a.ds_map).
-hipError_t launch_ds_map(const BwdArgs& a, hipStream_t s);
 
 // Token indices -> presence rows [B, nhk, n_qb, n_kb] (+ per-row counts).
 // Top-k positions per score row within [starts[r], ends[r]) (full rows when

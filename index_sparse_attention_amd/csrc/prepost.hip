@@ -1,13 +1,12 @@
 // Preprocess and postprocess of the attention backward.
 //
-// Preprocess of LoopK, LoopQ and SPLIT_DS: delta[b, h, i] = sum_d
-// dO[b,i,h,d] * O[b,i,h,d] (fp32 sum of exact bf16 products); for SPLIT_DS
-// also lse2 = lse * log2(e), the form its dK/dV pass copies straight into
-// LDS, both padded to whole 128-row blocks (delta = 0, lse2 = +inf); plus
-// zeroing of the fp32 accumulators the main loop reduces into (dK/dV for
-// LoopK, dQ for LoopQ).  The zeroing is a plain fill kernel, not a memset
-// node, so the whole call can be graph-captured.  (SPLIT computes delta in
-// its dQ pass instead.)
+// Preprocess of LoopK and LoopQ: the delta rows (delta[b, h, i] = sum_d
+// dO[b,i,h,d] * O[b,i,h,d], fp32 sum of exact bf16 products, padded to
+// whole 128-row blocks with 0; delta_rows in pre_rows.hpp) plus zeroing of
+// the fp32 accumulators the main loop reduces into (dK/dV for LoopK, dQ for
+// LoopQ).  The zeroing is a plain fill kernel, not a memset node, so the
+// whole call can be graph-captured.  (SPLIT_DS runs the same delta rows, with
+// lse2, inside its set-up launch; SPLIT computes delta in its dQ pass.)
 //
 // Postprocess: fp32 accumulator -> bf16 output (round to nearest even), times
 // softmax_scale for dK and dQ.  MagiAttention PR #334, Core changes item 3:
@@ -18,78 +17,18 @@
 // segment per lane group, rows in memory order.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "pre_rows.hpp"
 
 namespace isattn {
 namespace {
 
 constexpr int kThreads = 256;
 
-// Delta blocks: RPB rows per pass, R passes per block, every thread issuing
-// the 2R 16-byte loads of its R rows before any arithmetic.
-constexpr int kPreRows = 4;
-
 template <int DV>
 __global__ __launch_bounds__(kThreads) void k_preprocess(BwdArgs a, int32_t nblk_delta, int64_t n4_0,
                                                          int64_t n4_1) {
-    constexpr int L = DV / 8;          // lanes per row, 8 bf16 each
-    constexpr int RPB = kThreads / L;  // rows per pass
-    constexpr int R = kPreRows;
     if (int32_t(blockIdx.x) < nblk_delta) {
-        // rows taken in (b, i, h) order, h fastest: the token-major memory
-        // order of O and dO, so a block reads whole token rows; they are
-        // written to the statistics array at (b, h, i)
-        const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
-        const int sub = threadIdx.x % L;
-        int64_t row[R], stat[R], i[R];
-        bool in[R];
-        u32x4_t o[R], g[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            row[r] = (int64_t(blockIdx.x) * R + r) * RPB + threadIdx.x / L;
-            const int64_t h = row[r] % a.Hq;
-            const int64_t bi = row[r] / a.Hq;
-            i[r] = bi % a.stat_ld;
-            const int64_t b = bi / a.stat_ld;
-            stat[r] = (b * a.Hq + h) * a.stat_ld + i[r];
-            o[r] = u32x4_t{0u, 0u, 0u, 0u};
-            g[r] = u32x4_t{0u, 0u, 0u, 0u};
-            in[r] = false;
-            if (row[r] < rows) {
-                // token row of (b, i): b * stride_b + i * stride_s, or for packed
-                // sequences cu_q[b] + i (rows past the sequence's length are padding)
-                int64_t ob = b * a.o_sb + i[r] * a.o_ss, db = b * a.do_sb + i[r] * a.do_ss;
-                int sq = a.Sq;
-                if (a.cu_q != nullptr) {
-                    const int64_t t = a.cu_q[b] + i[r];
-                    sq = seq_len(a.cu_q, int(b), a.Sq);
-                    ob = t * a.o_ss;
-                    db = t * a.do_ss;
-                }
-                in[r] = i[r] < sq;
-                if (in[r]) {
-                    o[r] = gload128(a.o + ob + h * a.o_sh + 8 * sub);
-                    g[r] = gload128(a.dO + db + h * a.do_sh + 8 * sub);
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc = fmaf(bf16_lo(o[r][j]), bf16_lo(g[r][j]), acc);
-                acc = fmaf(bf16_hi(o[r][j]), bf16_hi(g[r][j]), acc);
-            }
-#pragma unroll
-            for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-            if (row[r] < rows && sub == 0) {
-                a.delta[stat[r]] = acc;
-                if (a.lse2 != nullptr) {
-                    const int64_t bh = stat[r] / a.stat_ld;
-                    a.lse2[stat[r]] = in[r] ? a.lse[bh * a.lse_ld + i[r]] * kLog2e : __builtin_inff();
-                }
-            }
-        }
+        delta_rows<DV, kThreads>(a, blockIdx.x);
     } else {
         const int64_t n4 = n4_0 + n4_1;
         const int64_t stride = int64_t(gridDim.x - nblk_delta) * kThreads;
@@ -153,8 +92,7 @@ hipError_t post_dispatch(int D, const float* acc, uint16_t* out, int64_t sb, int
 hipError_t launch_preprocess(const BwdArgs& a, int algo, hipStream_t s) {
     (void)algo;
     const int64_t rows = int64_t(a.B) * a.Hq * a.stat_ld;
-    const int L = a.Dv / 8;
-    const int rpb = kThreads / L * kPreRows;
+    const int rpb = a.Dv == 64 ? delta_rows_per_block<64, kThreads>() : delta_rows_per_block<128, kThreads>();
     const int32_t nblk_delta = int32_t((rows + rpb - 1) / rpb);
     const int64_t n4_0 = a.acc0_elems / 4;
     const int64_t n4_1 = a.acc1_elems / 4;

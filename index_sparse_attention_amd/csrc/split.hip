@@ -33,6 +33,7 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "key_steps.hpp"
+#include "pre_rows.hpp"
 
 namespace isattn {
 namespace {
@@ -164,12 +165,10 @@ __device__ void schedule_parts(const BwdArgs& a, int* cnt, int* wsum) {
     }
 }
 
-// workgroup (pass, XCD range): counting sort of the range into a.order
-__global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
-    __shared__ int cnt[kSchedKeys];
-    __shared__ int wsum[kSchedThreads / 64];
-    const int pass = blockIdx.x / kXcds;
-    const int x = blockIdx.x - pass * kXcds;
+// workgroup blk = (pass, XCD range): counting sort of the range into a.order
+__device__ __forceinline__ void schedule_range(const BwdArgs& a, int blk, int* cnt, int* wsum, int* s_total_p) {
+    const int pass = blk / kXcds;
+    const int x = blk - pass * kXcds;
     if (pass == 0 && a.kv_parts_T > 0) {            // part mode: one workgroup schedules the dK/dV units
         if (x == 0) schedule_parts(a, cnt, wsum);
         return;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
         wc[j] = i < hi ? work_of(i) : 0;
     }
     const int i_rest = lo + tid + kCache * kSchedThreads;
-    __shared__ int s_total;
+    int& s_total = *s_total_p;
     for (int k = tid; k < kSchedKeys; k += kSchedThreads) cnt[k] = 0;
     if (tid == 0) s_total = 0;
     __syncthreads();
@@ -262,6 +261,27 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_schedule(BwdArgs a) {
         if (i < hi) out[lo + atomicAdd(&cnt[key(i, wc[j])], 1)] = i;
     }
     for (int i = i_rest; i < hi; i += kSchedThreads) out[lo + atomicAdd(&cnt[key(i, work_of(i))], 1)] = i;
+}
+
+// Set-up of the two-pass backward, one launch: workgroups [0, n_sched) sort
+// the work order (schedule_range), the next n_map build the dS position map
+// of SPLIT_DS with a block CSR, the rest compute the delta and lse2 rows of
+// SPLIT_DS (DV = 0: none).  The three read disjoint inputs and write disjoint
+// outputs, so they run side by side; the passes that use them start after
+// this kernel ends.
+template <int DV>
+__global__ __launch_bounds__(kSchedThreads) void k_split_setup(BwdArgs a, int32_t n_sched, int32_t n_map) {
+    __shared__ int cnt[kSchedKeys];
+    __shared__ int wsum[kSchedThreads / 64];
+    __shared__ int s_total;
+    const int blk = blockIdx.x;
+    if (blk < n_sched) {
+        schedule_range(a, blk, cnt, wsum, &s_total);
+    } else if (blk < n_sched + n_map) {
+        ds_map_rows<kSchedThreads>(a, blk - n_sched);
+    } else if constexpr (DV > 0) {
+        delta_rows<DV, kSchedThreads>(a, blk - n_sched - n_map);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1629,9 +1649,27 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_split_schedule(const BwdArgs& a, hipStream_t s) {
-    if (int64_t(a.B) * (int64_t(a.Hk) * a.n_kb + int64_t(a.Hq) * a.n_qb) == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_split_schedule, dim3(2 * kXcds), dim3(kSchedThreads), 0, s, a);
+hipError_t launch_split_setup(const BwdArgs& a, bool delta, hipStream_t s) {
+    const bool sched = int64_t(a.B) * (int64_t(a.Hk) * a.n_kb + int64_t(a.Hq) * a.n_qb) != 0;
+    const int32_t n_sched = sched ? 2 * kXcds : 0;
+    // the map (and its overflow flag) whenever SPLIT_DS has a block CSR, even an empty one
+    const int64_t map_rows = int64_t(a.B) * a.Hm * a.n_qb;
+    constexpr int kMapRows = kSchedThreads / 64;
+    const int32_t n_map = a.ds_flag != nullptr ? int32_t(max(int64_t(1), (map_rows + kMapRows - 1) / kMapRows)) : 0;
+    const int64_t rows = delta ? int64_t(a.B) * a.Hq * a.stat_ld : 0;
+    int64_t grid = n_sched + n_map;
+    if (rows == 0 || a.Dv == 0) {
+        if (grid == 0) return hipSuccess;
+        hipLaunchKernelGGL(k_split_setup<0>, dim3(unsigned(grid)), dim3(kSchedThreads), 0, s, a, n_sched, n_map);
+    } else if (a.Dv == 64) {
+        grid += (rows + delta_rows_per_block<64, kSchedThreads>() - 1) / delta_rows_per_block<64, kSchedThreads>();
+        hipLaunchKernelGGL(k_split_setup<64>, dim3(unsigned(grid)), dim3(kSchedThreads), 0, s, a, n_sched, n_map);
+    } else if (a.Dv == 128) {
+        grid += (rows + delta_rows_per_block<128, kSchedThreads>() - 1) / delta_rows_per_block<128, kSchedThreads>();
+        hipLaunchKernelGGL(k_split_setup<128>, dim3(unsigned(grid)), dim3(kSchedThreads), 0, s, a, n_sched, n_map);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -45,7 +45,11 @@ struct DsqCfg {
     static constexpr int K_BYTES = BN * DQK * 2;
     static constexpr int S_BYTES = 2 * 1024;       // one wave's dS of a step: 2 chunks
     static constexpr int STAGE_BYTES = K_BYTES + NW * S_BYTES;
-    static constexpr int NS = 3;                   // ring stages
+    // ring stages: four make 64 KiB of LDS per workgroup at Dqk = 128, so
+    // two workgroups share a CU; that measured 5 % faster than three
+    // workgroups of a 3-stage ring (48 KiB each), and deeper rings or one
+    // workgroup per CU were slower
+    static constexpr int NS = 4;
     static constexpr int AHEAD = 2;                // loads run this many steps ahead
     static_assert(NS >= AHEAD + 1, "a stage is reloaded only after the step that last read it");
     static constexpr int LDS_BYTES = NS * STAGE_BYTES;
@@ -71,7 +75,7 @@ __device__ __forceinline__ uint32_t ds_lds_off(int l, int cc, int j, int hf) {
 }
 
 template <int DQK, bool VL>
-__global__ __launch_bounds__(256, DQK > 128 ? 2 : 3) void k_bwd_dq_ds(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_dq_ds(BwdArgs a) {
     using C = DsqCfg<DQK>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int tid = threadIdx.x;
@@ -262,50 +266,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// K->Q position of every Q->K entry of a block CSR (the dS slot of the dQ
-// pass's block): one wave per Q->K row (b, hm, qb), lanes over its entries,
-// each a binary search for qb in the K->Q row (b, hm, kb).  -1 where the
-// two forms disagree.  Thread 0 also sets the overflow flag: the CSR holds
-// more blocks than the map or the dS tiles have room for.
-__global__ __launch_bounds__(256) void k_ds_map(BwdArgs a) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        const int64_t rq = int64_t(a.B) * a.Hm * a.n_qb, rk = int64_t(a.B) * a.Hm * a.n_kb;
-        const int64_t nnz = max(int64_t(a.q2k_ptr[rq]), int64_t(a.k2q_ptr[rk]));
-        *a.ds_flag = (nnz > a.ds_map_len || nnz * (a.Hq / a.Hm) > a.ds_cap) ? 1 : 0;
-    }
-    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= int64_t(a.B) * a.Hm * a.n_qb) return;
-    const int lane = threadIdx.x & 63;
-    const int64_t bhm = row / a.n_qb;
-    const int qb = int(row - bhm * a.n_qb);
-    const int end = a.q2k_ptr[row + 1];
-    for (int p = a.q2k_ptr[row] + lane; p < end; p += 64) {
-        if (p < 0 || p >= a.ds_map_len) continue;
-        const int kb = a.q2k_col[p];
-        int pos = -1;
-        if (kb >= 0 && kb < a.n_kb) {
-            const int64_t r = bhm * a.n_kb + kb;
-            const int hi0 = a.k2q_ptr[r + 1];
-            int lo = a.k2q_ptr[r], hi = hi0;
-            while (lo < hi) {
-                const int mid = lo + (hi - lo) / 2;
-                if (a.k2q_col[mid] < qb) lo = mid + 1;
-                else hi = mid;
-            }
-            if (lo < hi0 && a.k2q_col[lo] == qb) pos = lo;
-        }
-        a.ds_map[p] = pos;
-    }
-}
-
 }  // namespace
-
-hipError_t launch_ds_map(const BwdArgs& a, hipStream_t s) {
-    const int64_t rows = int64_t(a.B) * a.Hm * a.n_qb;
-    if (a.ds_flag == nullptr) return hipSuccess;  // dense masks: slots from the shape alone
-    hipLaunchKernelGGL(k_ds_map, dim3(unsigned(max(int64_t(1), (rows + 3) / 4))), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
 
 hipError_t launch_split_ds_dq(const BwdArgs& a, hipStream_t s) {
     const bool vl = a.cu_q != nullptr;             // packed sequences
