@@ -20,6 +20,12 @@
 //   k_scan2          : two exclusive scans (rows, columns) -> row_ptr arrays.
 //   k_fill           : one wave per CSR row of either form, ballot + prefix
 //                      popcount writes the ascending column list; one launch.
+//   k_csr_small      : masks of at most kCsrTotalBytes presence bytes (slices
+//                      of at most kCsrSideMax x kCsrSideMax, kCsrSliceBytes):
+//                      the whole presence -> CSR in one launch, one workgroup
+//                      per (b, h) slice with the slice in LDS; its offset in
+//                      the CSRs (the kept blocks of the slices before it) is
+//                      counted by the workgroup itself, so none waits on another.
 // The conversion is latency-bound at the benchmark's sizes, so launches are
 // fused wherever no result crosses workgroups.
 #include "device_common.hpp"
@@ -32,6 +38,10 @@ constexpr int kPresThreads = 1024;
 constexpr int kPresBatch = 4;                      // 16-byte index loads per thread per batch
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 4;
+constexpr int kCsrThreads = 1024;
+constexpr int kCsrSliceBytes = 16384;
+constexpr int kCsrSideMax = 1024;
+constexpr int64_t kCsrTotalBytes = 256 * 1024;
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -266,6 +276,137 @@ __global__ __launch_bounds__(256) void k_fill(const uint8_t* __restrict__ presen
     }
 }
 
+// Kept (nonzero) bytes of a 32-bit word.
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+    uint32_t x = w | (w >> 4);
+    x |= x >> 2;
+    x |= x >> 1;
+    return __popc(x & 0x01010101u);
+}
+
+// Exclusive scan over the kCsrThreads threads of a workgroup (one value
+// each); *total gets the sum.  wsum holds kCsrThreads / 64 ints.
+__device__ int csr_block_scan(int v, int* wsum, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    int pre = x - v, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kCsrThreads / 64; ++w) {
+        pre += w < wid ? wsum[w] : 0;
+        tot += wsum[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return pre;
+}
+
+// One workgroup per slice bh = (b, h) of a presence [BH, n_qb, n_kb]
+// (n_qb, n_kb <= kCsrSideMax, n_qb * n_kb <= kCsrSliceBytes): counts the
+// kept blocks of the slices before it (its offset in both CSRs), stages its
+// slice in LDS, counts rows (ballot per wave) and columns (LDS atomics),
+// scans both, writes its row_ptr entries and fills both column lists in
+// ascending order.
+__global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __restrict__ presence, int32_t n_qb,
+                                                           int32_t n_kb, int32_t* __restrict__ q2k_ptr,
+                                                           int32_t* __restrict__ q2k_col,
+                                                           int32_t* __restrict__ k2q_ptr,
+                                                           int32_t* __restrict__ k2q_col) {
+    __shared__ __attribute__((aligned(16))) uint8_t pres[kCsrSliceBytes];
+    __shared__ int rcnt[kCsrSideMax];
+    __shared__ int ccnt[kCsrSideMax];
+    __shared__ int wsum[kCsrThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    constexpr int NW = kCsrThreads / 64;
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    const int bh = blockIdx.x;
+    const int S = n_qb * n_kb;
+    const int64_t before = int64_t(bh) * S;
+    const uint8_t* slice = presence + before;
+    const bool vec = (reinterpret_cast<uintptr_t>(presence) & 15) == 0 && (S & 15) == 0;
+
+    // offset: kept blocks of the slices before this one
+    int c = 0;
+    if (vec) {
+        const u32x4_t* p4 = reinterpret_cast<const u32x4_t*>(presence);
+        for (int64_t i = tid; i < before / 16; i += kCsrThreads) {
+            const u32x4_t w = p4[i];
+            c += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+        }
+    } else {
+        for (int64_t i = tid; i < before; i += kCsrThreads) c += presence[i] != 0;
+    }
+    // the slice into LDS; column counts cleared
+    if (vec) {
+        for (int i = tid; i < S / 16; i += kCsrThreads)
+            reinterpret_cast<u32x4_t*>(pres)[i] = reinterpret_cast<const u32x4_t*>(slice)[i];
+    } else {
+        for (int i = tid; i < S; i += kCsrThreads) pres[i] = slice[i];
+    }
+    for (int i = tid; i < n_kb; i += kCsrThreads) ccnt[i] = 0;
+    int off = 0;
+    csr_block_scan(c, wsum, &off);                 // (the scan's barriers also publish pres and ccnt)
+
+    // row counts (one wave per row) and column counts
+    for (int r = wid; r < n_qb; r += NW) {
+        int n = 0;
+        for (int c0 = 0; c0 < n_kb; c0 += 64) {
+            const int kb = c0 + lane;
+            const bool on = kb < n_kb && pres[r * n_kb + kb] != 0;
+            if (on) atomicAdd(&ccnt[kb], 1);
+            n += __popcll(__ballot(on));
+        }
+        if (lane == 0) rcnt[r] = n;
+    }
+    __syncthreads();
+    const int rc = tid < n_qb ? rcnt[tid] : 0;
+    const int cc = tid < n_kb ? ccnt[tid] : 0;
+    int rtot = 0, ctot = 0;
+    const int rx = csr_block_scan(rc, wsum, &rtot);
+    const int cx = csr_block_scan(cc, wsum, &ctot);
+    if (tid < n_qb) {
+        rcnt[tid] = off + rx;                      // start of row tid's list
+        q2k_ptr[int64_t(bh) * n_qb + tid + 1] = off + rx + rc;
+    }
+    if (tid < n_kb) {
+        ccnt[tid] = off + cx;
+        k2q_ptr[int64_t(bh) * n_kb + tid + 1] = off + cx + cc;
+    }
+    if (bh == 0 && tid == 0) {
+        q2k_ptr[0] = 0;
+        k2q_ptr[0] = 0;
+    }
+    __syncthreads();
+
+    // column lists: ballot + prefix popcount place each kept block
+    for (int r = wid; r < n_qb; r += NW) {
+        int base = rcnt[r];
+        for (int c0 = 0; c0 < n_kb; c0 += 64) {
+            const int kb = c0 + lane;
+            const bool on = kb < n_kb && pres[r * n_kb + kb] != 0;
+            const uint64_t m = __ballot(on);
+            if (on) q2k_col[base + __popcll(m & below)] = kb;
+            base += __popcll(m);
+        }
+    }
+    for (int k = wid; k < n_kb; k += NW) {
+        int base = ccnt[k];
+        for (int q0 = 0; q0 < n_qb; q0 += 64) {
+            const int qb = q0 + lane;
+            const bool on = qb < n_qb && pres[qb * n_kb + k] != 0;
+            const uint64_t m = __ballot(on);
+            if (on) k2q_col[base + __popcll(m & below)] = qb;
+            base += __popcll(m);
+        }
+    }
+}
+
 // Token bits: every slot cleared, then one workgroup per (qb, hk, b) sets the
 // bits of its rows' selected keys in both layouts (row-major and key-major)
 // with relaxed 32-bit atomic ORs (rows of one block hit the same words).
@@ -345,6 +486,13 @@ hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n
                                   int32_t* k2q_ptr, int32_t* k2q_col, hipStream_t s) {
     const int32_t rows = BH * n_qb;
     const int32_t cols = BH * n_kb;
+    const int64_t slice = int64_t(n_qb) * n_kb;
+    if (BH > 0 && slice > 0 && n_qb <= kCsrSideMax && n_kb <= kCsrSideMax && slice <= kCsrSliceBytes &&
+        int64_t(BH) * slice <= kCsrTotalBytes) {
+        hipLaunchKernelGGL(k_csr_small, dim3(BH), dim3(kCsrThreads), 0, s, presence, n_qb, n_kb, q2k_ptr, q2k_col,
+                           k2q_ptr, k2q_col);
+        return hipGetLastError();
+    }
     const int32_t row_blocks = rows > 0 && !have_row_counts ? (rows + 3) / 4 : 0;
     const int32_t tiles = (n_kb + 63) / 64;
     const int32_t col_blocks = cols > 0 ? BH * tiles : 0;

@@ -99,8 +99,11 @@ def test_index_converter_full_workload():
     assert int(got[0][-1]) == 2 * 128 * 129 // 2      # the full lower block triangle per KV head
 
 
+# the first seven fit the single-launch path (slices of at most 1024 x 1024 and
+# 16 KiB, 256 KiB in all); the rest take the count / scan / fill launches
 @pytest.mark.parametrize("shape", [(2, 16, 64, 64), (1, 3, 5, 9), (3, 1, 70, 1), (1, 2, 1, 130), (1, 4, 128, 128),
-                                   (4, 16, 64, 64), (2, 3, 100, 77), (1, 1, 129, 2)])
+                                   (4, 16, 64, 64), (2, 3, 100, 77), (1, 1, 129, 2),
+                                   (8, 16, 64, 64), (1, 1, 2000, 3), (1, 1, 3, 2000), (1, 2, 128, 200)])
 def test_block_mask_to_csr(shape):
     import index_sparse_attention_amd as isa
     rng = np.random.default_rng(sum(shape))
@@ -109,3 +112,29 @@ def test_block_mask_to_csr(shape):
     m = isa.block_mask_to_csr(torch.from_numpy(pres).cuda())
     torch.cuda.synchronize()
     assert_csr_equal(csr_to_host(m), oracle.presence_to_csr(pres))
+
+
+@pytest.mark.parametrize("offset", [1, 16])
+def test_block_mask_to_csr_unaligned(offset):
+    """A presence view that starts off a 16-byte boundary takes the byte loads."""
+    import index_sparse_attention_amd as isa
+    shape = (3, 4, 32, 32)
+    rng = np.random.default_rng(offset)
+    pres = (rng.random(shape) < 0.4).astype(np.uint8)
+    flat = torch.zeros(offset + pres.size, dtype=torch.uint8, device="cuda")
+    flat[offset:] = torch.from_numpy(pres.reshape(-1)).cuda()
+    view = flat[offset:].view(shape)
+    log(f"block mask csr unaligned offset {offset}")
+    m = isa.block_mask_to_csr(view)
+    torch.cuda.synchronize()
+    assert_csr_equal(csr_to_host(m), oracle.presence_to_csr(pres))
+
+
+def test_index_converter_large_path():
+    """More than 1024 key blocks: the index path's count / scan / fill launches
+    (with the row counts the presence kernel already produced)."""
+    rng = np.random.default_rng(21)
+    B, Sq, Sk, nhk, topk = 2, 200, 2100, 2, 9
+    idx = synth.topk_indices(rng, B, Sq, Sk, nhk, topk)
+    log("converter large path")
+    assert_csr_equal(_gpu_index(idx, B, Sq, Sk, 64, 2), _oracle_index(idx, B, Sq, Sk, 64, 2))
