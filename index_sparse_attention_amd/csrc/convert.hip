@@ -334,10 +334,20 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __rest
     // offset: kept blocks of the slices before this one
     int c = 0;
     if (vec) {
+        // eight 16-byte loads in flight per thread (the latest slice reads up to
+        // kCsrTotalBytes, 16 per thread)
         const u32x4_t* p4 = reinterpret_cast<const u32x4_t*>(presence);
-        for (int64_t i = tid; i < before / 16; i += kCsrThreads) {
-            const u32x4_t w = p4[i];
-            c += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+        const int64_t n16 = before / 16;
+        for (int64_t i0 = 0; i0 < n16; i0 += 8 * kCsrThreads) {
+            u32x4_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t i = i0 + j * kCsrThreads + tid;
+                w[j] = i < n16 ? p4[i] : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c += nonzero_bytes(w[j][0]) + nonzero_bytes(w[j][1]) + nonzero_bytes(w[j][2]) + nonzero_bytes(w[j][3]);
         }
     } else {
         for (int64_t i = tid; i < before; i += kCsrThreads) c += presence[i] != 0;
