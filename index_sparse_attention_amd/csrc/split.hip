@@ -707,17 +707,28 @@ struct DkvCfg {
 // block of every head of the GQA group.  Every wave walks it identically.
 // Visibility (causal) is decided per block; parts of a visible block that no
 // row of sees, or that lie past Sq, are still stepped through: their P is
-// masked to zero or their rows' lse2 is +inf.  The kept query blocks of a
-// head are read 64 at a time into a register (one per lane).
+// masked to zero or their rows' lse2 is +inf.
+//
+// The kept query blocks of a head are taken 64 list entries at a time, one
+// per lane: each lane decides its entry (in the item's [lo, hi) range, a
+// valid block index, some row of it sees the key block) and computes its dS
+// tile slot, and the valid entries are packed to the low lanes in list
+// order (ballot, prefix popcount, ds_permute).  A step then reads its block
+// and slot with two lane reads; the per-entry tests run once per 64 entries,
+// lane-parallel, instead of serially at every step.
 template <int BM, bool DS>
 struct DkvSteps {
     static constexpr int PARTS = kBlock / BM;
     const BwdArgs& a;
     int b, hk, kb, n_base, shift, lane;
-    int gi = 0, it = -1, part = 0, count = 0, first = 0;
+    int gi = 0, part = 0, count = 0, first = 0;
     int m = 0;                                      // first row of the current step
     int cum = 0;                                    // blocks in the group's earlier heads
     int lo = 0, hi = INT_MAX;                       // range of the group's concatenated block lists
+    int scan = 0;                                   // next list entry of the current head to take
+    int pos = 0, nval = 0;                          // current / number of packed entries
+    int e_qb = 0;                                   // packed entries (one per lane): block, dS slot
+    int e_tile = 0;
     const int32_t* list = nullptr;
     // DS (SPLIT_DS): the dS tile slot (dS tile slots in bwd_args.hpp) of the
     // current block, and the current head's slot of its first list entry
@@ -725,7 +736,6 @@ struct DkvSteps {
     // heads of its mask head; the next entry is R slots on) or of (qb = 0,
     // kb) (dense)
     int tile = 0, tile0 = 0;
-    int chunk = 0, chunk_base = -1;
     // the current head's Q, dO and statistics rows
     const uint16_t* qh = nullptr;
     const uint16_t* oh = nullptr;
@@ -750,7 +760,6 @@ struct DkvSteps {
         dh = a.delta + srow;
         list = nullptr;
         first = 0;
-        chunk_base = -1;
         if (a.mask_kind == 1) {
             const int hm = h * a.Hm / a.Hq;
             const int r = (b * a.Hm + hm) * a.n_kb + kb;
@@ -770,38 +779,49 @@ struct DkvSteps {
             if constexpr (DS) tile0 = (b * a.Hq + h) * a.ds_T + kb;
         }
     }
-    __device__ int qb_at() {
-        if (list == nullptr) return first + it;
-        const int base = it & ~63;
-        if (base != chunk_base) {
-            chunk_base = base;
-            chunk = base + lane < count ? list[base + lane] : -1;
+    // pack the current head's entries scan .. scan + 63 (see above)
+    __device__ void refill() {
+        const int e = scan + lane;
+        bool v = e < count && cum + e < hi;
+        int qb = -1;
+        if (v) qb = list != nullptr ? list[e] : first + e;
+        v = v && qb >= 0 && qb < a.n_qb && qb * kBlock < a.Sq &&                  // a malformed entry: nothing to do
+            !(a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base);   // no row sees the key block
+        int tl = 0;
+        if constexpr (DS) {
+            if (v) {
+                if (list != nullptr) tl = tile0 + (a.Hq / a.Hm) * e;
+                else tl = tile0 + (a.cu_q != nullptr ? qb * a.n_kb
+                                                      : int(visible_before(qb, a.Sq, a.Sk, a.n_kb, a.causal != 0)));
+            }
         }
-        return __builtin_amdgcn_readlane(chunk, it & 63);
+        const uint64_t mask = __ballot(v);
+        const int dst = v ? __popcll(mask & ((uint64_t(1) << lane) - 1)) : 63;   // unused lanes: slot 63, past nval
+        e_qb = __builtin_amdgcn_ds_permute(dst * 4, qb);
+        if constexpr (DS) e_tile = __builtin_amdgcn_ds_permute(dst * 4, tl);
+        nval = __popcll(mask);
+        pos = -1;
+        scan += 64;
     }
     // next kept block some row of which sees the key block; false at the end
     // (of the item, or of its [lo, hi) range)
     __device__ bool next_block() {
         for (;;) {
-            ++it;
-            while (it >= count) {
+            if (++pos < nval) {
+                const int qb = __builtin_amdgcn_readlane(e_qb, pos);
+                if constexpr (DS) tile = __builtin_amdgcn_readlane(e_tile, pos);
+                part = 0;
+                m = qb * kBlock;
+                return true;
+            }
+            while (scan >= count) {                 // the head's list is done
                 if (++gi >= a.G) return false;
                 cum += count;
                 load_head();
-                it = 0;
+                scan = 0;
             }
-            if (cum + it >= hi) return false;
-            const int qb = qb_at();
-            if (qb < 0 || qb >= a.n_qb || qb * kBlock >= a.Sq) continue;  // malformed entry: nothing to do
-            if (a.causal && min(qb * kBlock + kBlock - 1, a.Sq - 1) + shift < n_base) continue;
-            part = 0;
-            m = qb * kBlock;
-            if constexpr (DS) {
-                if (list != nullptr) tile = tile0 + (a.Hq / a.Hm) * it;
-                else tile = tile0 + (a.cu_q != nullptr ? qb * a.n_kb
-                                                       : int(visible_before(qb, a.Sq, a.Sk, a.n_kb, a.causal != 0)));
-            }
-            return true;
+            if (cum + scan >= hi) return false;
+            refill();
         }
     }
     __device__ bool start() {
@@ -811,7 +831,9 @@ struct DkvSteps {
             cum += count;
             load_head();
         }
-        it = lo - cum - 1;
+        scan = lo - cum;
+        pos = 0;
+        nval = 0;
         return next_block();
     }
     __device__ bool next() {
