@@ -11,38 +11,50 @@ namespace isattn {
 
 // Every 32-key part of every kept key block that holds a key some row of the
 // query block sees (key <= last, the last key visible to the block's last
-// row).  The kept key blocks are read 64 at a time into a register (one per
-// lane).
+// row).  The kept key blocks are taken 64 list entries at a time, one per
+// lane, tested lane-parallel and packed, so a step reads its block with one
+// lane read.
 struct KeySteps {
-    int it = -1, sub = 0, count = 0, n0 = 0, n_kb = 0, last = 0, lane = 0;
+    int sub = 0, count = 0, n0 = 0, n_kb = 0, last = 0, lane = 0;
     const int32_t* list = nullptr;
-    int chunk = 0, chunk_base = -1;
     int beg = 0;                                    // Q->K position of the row's first entry
     // optional per-entry values read along with the list (aux[i] for entry
     // i, i < aux_n; -1 past it): aux_at() gives the current entry's
     const int32_t* aux = nullptr;
-    int aux_n = 0, achunk = -1;
+    int aux_n = 0;
+    int scan = 0, pos = 0, nval = 0;                // next entry to take; current / number of packed
+    int e_kb = 0, e_aux = -1;                       // packed entries, one per lane
 
-    __device__ int kb_at() {
-        if (list == nullptr) return it;
-        const int base = it & ~63;
-        if (base != chunk_base) {
-            chunk_base = base;
-            chunk = base + lane < count ? list[base + lane] : -1;
-            if (aux != nullptr) achunk = base + lane < aux_n ? aux[base + lane] : -1;
+    // take entries scan .. scan + 63: each lane tests its own (a valid block
+    // index that holds a key some row sees) and the valid ones are packed to
+    // the low lanes in list order
+    __device__ void refill() {
+        const int e = scan + lane;
+        int kb = -1, x = -1;
+        if (e < count) {
+            kb = list != nullptr ? list[e] : e;
+            if (aux != nullptr && e < aux_n) x = aux[e];
         }
-        return __builtin_amdgcn_readlane(chunk, it & 63);
+        const bool v = kb >= 0 && kb < n_kb && kb * kBlock <= last;
+        const uint64_t mask = __ballot(v);
+        const int dst = v ? __popcll(mask & ((uint64_t(1) << lane) - 1)) : 63;
+        e_kb = __builtin_amdgcn_ds_permute(dst * 4, kb);
+        if (aux != nullptr) e_aux = __builtin_amdgcn_ds_permute(dst * 4, x);
+        nval = __popcll(mask);
+        pos = -1;
+        scan += 64;
     }
-    __device__ int aux_at() const { return __builtin_amdgcn_readlane(achunk, it & 63); }
+    __device__ int aux_at() const { return __builtin_amdgcn_readlane(e_aux, pos); }
     __device__ bool next_block() {
         for (;;) {
-            if (++it >= count) return false;
-            const int kb = kb_at();
-            if (kb < 0 || kb >= n_kb) continue;     // malformed entry: nothing to do
-            if (kb * kBlock > last) continue;
-            sub = 0;
-            n0 = kb * kBlock;
-            return true;
+            if (++pos < nval) {
+                const int kb = __builtin_amdgcn_readlane(e_kb, pos);
+                sub = 0;
+                n0 = kb * kBlock;
+                return true;
+            }
+            if (scan >= count) return false;
+            refill();
         }
     }
     __device__ bool next() {
