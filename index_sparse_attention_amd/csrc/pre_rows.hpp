@@ -57,8 +57,9 @@ __device__ __forceinline__ void delta_rows(const BwdArgs& a, int64_t blk) {
             }
             in[r] = i < sq;
             if (in[r]) {
-                o[r] = gload128(a.o + ob + h * a.o_sh + 8 * sub);
-                g[r] = gload128(a.dO + db + h * a.do_sh + 8 * sub);
+                // read once: non-temporal, so they do not displace cached lines
+                o[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.o + ob + h * a.o_sh + 8 * sub));
+                g[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.dO + db + h * a.do_sh + 8 * sub));
                 if (a.lse2 != nullptr) l2[r] = a.lse[(b * a.Hq + h) * a.lse_ld + i] * kLog2e;
             }
         }
