@@ -21,7 +21,8 @@
 //   k_fill           : one wave per CSR row of either form, ballot + prefix
 //                      popcount writes the ascending column list; one launch.
 //   k_csr_small      : masks of at most kCsrTotalBytes presence bytes (slices
-//                      of at most kCsrSideMax x kCsrSideMax, kCsrSliceBytes):
+//                      of at most kCsrSideMax x kCsrSideMax, kCsrSliceBytes;
+//                      the offset counts re-read at most kCsrPrefixBytes):
 //                      the whole presence -> CSR in one launch, one workgroup
 //                      per (b, h) slice with the slice in LDS; its offset in
 //                      the CSRs (the kept blocks of the slices before it) is
@@ -42,6 +43,7 @@ constexpr int kCsrThreads = 1024;
 constexpr int kCsrSliceBytes = 16384;
 constexpr int kCsrSideMax = 1024;
 constexpr int64_t kCsrTotalBytes = 256 * 1024;
+constexpr int64_t kCsrPrefixBytes = 16 << 20;
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -497,8 +499,11 @@ hipError_t launch_presence_to_csr(const uint8_t* presence, int32_t BH, int32_t n
     const int32_t rows = BH * n_qb;
     const int32_t cols = BH * n_kb;
     const int64_t slice = int64_t(n_qb) * n_kb;
+    // the single launch while each workgroup's offset count stays small: the
+    // slices before it hold at most kCsrTotalBytes, and all workgroups
+    // together re-read at most kCsrPrefixBytes of presence
     if (BH > 0 && slice > 0 && n_qb <= kCsrSideMax && n_kb <= kCsrSideMax && slice <= kCsrSliceBytes &&
-        int64_t(BH) * slice <= kCsrTotalBytes) {
+        int64_t(BH) * slice <= kCsrTotalBytes && int64_t(BH) * (BH - 1) / 2 * slice <= kCsrPrefixBytes) {
         hipLaunchKernelGGL(k_csr_small, dim3(BH), dim3(kCsrThreads), 0, s, presence, n_qb, n_kb, q2k_ptr, q2k_col,
                            k2q_ptr, k2q_col);
         return hipGetLastError();
