@@ -1231,11 +1231,6 @@ struct DkvSWave {
         const uint16_t* vr = a.v + sh.b * a.v_sb + sh.hk * a.v_sh + int64_t(in ? key : 0) * a.v_ss + 8 * sh.h2;
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) vB[c] = in ? gload_operand(vr + 16 * c) : bf16x8_t{};
-        // the V rows land before the step loop: a wave that issues no loads in
-        // the loop (but may store dS) then never waits on the memory counter
-        // inside it (the compiler would otherwise guard the first use of vB in
-        // the loop body, and that wait would also cover the dS stores)
-        wait_vmcnt<0>();
 #pragma unroll
         for (int j = 0; j < C::NDK; ++j) dk[j] = f32x16_t{};
         const lds_char* o0 = sh.lp + C::O_OFF + (C::NS - 1) * C::O_BYTES;
@@ -1415,6 +1410,11 @@ struct DkvSWave {
     __device__ void first(int m, bool mask, const Dma& d, int64_t dso) {
         (void)m;
         (void)mask;
+        // the V rows land before the step loop: a wave that issues no loads in
+        // the loop (but may store dS) then never waits on the memory counter
+        // inside it (the compiler would otherwise guard the first use of vB in
+        // the loop body, and that wait would also cover the dS stores)
+        wait_vmcnt<0>();
         ds_prev = dso;
         fire_all(d);
     }
@@ -1560,21 +1560,28 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dkdv(BwdArgs a) {
         if (kb * C::BN >= a.Sk) return;            // a key block past the end of the sequence
     }
     const DkvShared<DQK, DV> sh(a, lds, w, lane, b, hk, kb * C::BN);
-    if constexpr (DS) {
-        // a block CSR whose true block count needs more dS tiles than the
-        // workspace holds (flagged by the position-map kernel): nothing is
-        // computed rather than anything written past the workspace
-        if (a.ds_flag != nullptr && *a.ds_flag != 0) return;
-    }
     DkvSteps<C::BM, DS> steps(a, b, hk, kb, lane);
     steps.lo = lo;
     steps.hi = hi;
+    // a block CSR whose true block count needs more dS tiles than the
+    // workspace holds (flagged by the set-up launch): nothing is computed or
+    // stored rather than anything written past the workspace (read once the
+    // K / V rows are on their way)
+    const bool overflow = DS && a.ds_flag != nullptr && *a.ds_flag != 0;
     if (w < C::NR) {
         DkvPWave<DQK, DV, TOK> role(sh, w);
+        if (overflow) {
+            wait_vmcnt<0>();
+            return;
+        }
         dkdv_run<DQK, DV, DS>(sh, steps, role);
         role.store(partial);
     } else {
         DkvSWave<DQK, DV, DS> role(sh, w - C::NR);
+        if (overflow) {
+            wait_vmcnt<0>();
+            return;
+        }
         dkdv_run<DQK, DV, DS>(sh, steps, role);
         role.store(partial);
     }
