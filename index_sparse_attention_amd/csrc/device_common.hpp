@@ -98,6 +98,8 @@ namespace isattn {
 // and store() can be split around other work to prefetch the next tile.
 // Rows at or past `limit` read as zeros.  With PERM, tile row r lands at LDS
 // row swap23(r).
+__device__ __forceinline__ int chunk_swz(int r, int D);   // below: the chunk swizzle of a tile row
+
 template <int D, int PITCH, int ROWS, int NT, bool PERM>
 struct TileStager {
     static constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -125,6 +127,19 @@ struct TileStager {
             const int c = u - r * CH;
             const int lr = PERM ? swap23(r) : r;
             *reinterpret_cast<u32x4_t*>(dst + lr * PITCH + 8 * c) = v[i];
+        }
+    }
+    // Row-major copy into a swizzled tile without padding (PITCH == D): tile
+    // row r at LDS row swap23(r) when PERM, chunk c at c ^ chunk_swz(row, D).
+    __device__ __forceinline__ void store_swz(uint16_t* dst, int tid) const {
+        static_assert(PITCH == D, "swizzled tiles have no padding");
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            const int r = u / CH;
+            const int c = u - r * CH;
+            const int lr = PERM ? swap23(r) : r;
+            *reinterpret_cast<u32x4_t*>(dst + lr * D + 8 * (c ^ chunk_swz(lr, D))) = v[i];
         }
     }
     // Transposed copy: element (r, d) to dstT[d * PT + r].

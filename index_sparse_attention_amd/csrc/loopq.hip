@@ -8,13 +8,16 @@
 //
 // One workgroup = 4 waves = one 128-key tile of one (batch, KV head); wave w
 // owns keys 32w..32w+31.  Each inner step stages 64 query rows of Q and dO
-// (row-major and transposed), their LSE*log2e and delta.  Per step and wave:
+// (rows swap23-staged and chunk-swizzled, so the dV / dK B operands come from
+// transposing reads), their LSE*log2e and delta; the next step's rows are
+// loaded into registers while the current one computes.  Per step and wave:
 //
 //   S  = Q K^T        [64 q x 32 keys]  32x32x16 MFMA, A = Q (LDS), B = K (regs)
 //   dP = dO V^T       [64 q x 32 keys]  B = V (regs)
 //   P  = exp2(S*scale*log2e - LSE*log2e),  dS = P * (dP - delta)
 //   dV += P^T dO      [32 keys x Dv]    A = P^T from the S accumulator registers
-//   dK += dS^T Q      [32 keys x Dqk]   A = dS^T from registers, B = Q^T (LDS)
+//   dK += dS^T Q      [32 keys x Dqk]   A = dS^T from registers, B = Q^T (LDS,
+//                                       transposing reads)
 //   dS -> LDS, then dQ_part = dS K [64 q x Dqk/4] per wave (16x16x32 MFMA,
 //   B = K (regs)), fp32 atomic add into the dQ accumulator.
 #include "device_common.hpp"
@@ -29,16 +32,12 @@ struct LoopQCfg {
     static constexpr int BN = 128;                 // keys per workgroup
     static constexpr int BM = 64;                  // query rows per inner step
     static constexpr int NT = 256;
-    static constexpr int PQ = DQK + 8;
-    static constexpr int PQT = BM + 4;
-    static constexpr int PDO = DV + 8;
-    static constexpr int PDOT = BM + 4;
     static constexpr int PDS = BN + 8;             // sdS[m][key]
+    // Q and dO tiles: rows swap23-staged, 16-byte chunks swizzled, no padding
+    // (the layout the transposing operand reads expect)
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_QT = OFF_Q + BM * PQ;
-    static constexpr int OFF_DO = OFF_QT + DQK * PQT;
-    static constexpr int OFF_DOT = OFF_DO + BM * PDO;
-    static constexpr int OFF_DS = OFF_DOT + DV * PDOT;
+    static constexpr int OFF_DO = OFF_Q + BM * DQK;
+    static constexpr int OFF_DS = OFF_DO + BM * DV;
     static constexpr int OFF_STAT = OFF_DS + BM * PDS;  // float lse2[BM], delta[BM]
     static constexpr int END_LOOP = OFF_STAT + 4 * BM;
     static constexpr int PK = DQK + 8;             // prologue staging
@@ -136,9 +135,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
     for (int t = 0; t < C::NDV; ++t) dv[t] = f32x16_t{};
 
     uint16_t* sQ = lds + C::OFF_Q;
-    uint16_t* sQt = lds + C::OFF_QT;
     uint16_t* sdO = lds + C::OFF_DO;
-    uint16_t* sdOt = lds + C::OFF_DOT;
     uint16_t* sdS = lds + C::OFF_DS;
     float* sL = reinterpret_cast<float*>(lds + C::OFF_STAT);
     float* sD = sL + C::BM;
@@ -146,54 +143,117 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
     const bool key_in = key < a.Sk;
     const bool tile_ragged = n_base + C::BN > a.Sk;
 
-    for (int gi = 0; gi < a.G; ++gi) {
+    // ---- steps: every 64-row half of every kept query block (of every query
+    // head of the GQA group) that some row of sees the key tile, in order.
+    // The next step's Q and dO rows and statistics are loaded into registers
+    // while the current step computes and issues its dQ atomics, and staged
+    // into LDS once the step is done.
+    struct Step {
+        int gi, it, half, m0;
+    };
+    int cnt = 0, first = 0, chunk = -1, chunk_base = -1;
+    const int32_t* list = nullptr;
+    auto head_list = [&](int gi) {
         const int h = hk * a.G + gi;
-        int qb_count, qb_first = 0;
-        const int32_t* qb_list = nullptr;
+        list = nullptr;
+        first = 0;
+        chunk_base = -1;
         if (a.mask_kind == 1) {
             const int hm = h * a.Hm / a.Hq;
             const int r = (b * a.Hm + hm) * a.n_kb + kb;
             const int beg = a.k2q_ptr[r];
-            qb_count = a.k2q_ptr[r + 1] - beg;
-            qb_list = a.k2q_col + beg;
+            cnt = a.k2q_ptr[r + 1] - beg;
+            list = a.k2q_col + beg;
         } else {
-            qb_first = 0;
             if (a.causal) {
                 const int first_row = n_base - shift;           // first row that sees key n_base
-                qb_first = first_row <= 0 ? 0 : first_row / kBlock;
+                first = first_row <= 0 ? 0 : first_row / kBlock;
             }
-            qb_count = a.n_qb - qb_first;
+            cnt = a.n_qb - first;
         }
-        const uint16_t* gq = a.q + b * a.q_sb + h * a.q_sh;
-        const uint16_t* gdo = a.dO + b * a.do_sb + h * a.do_sh;
-        const int64_t srow = (int64_t(b) * a.Hq + h) * a.Sq;
+    };
+    auto qb_at = [&](int it) {
+        if (list == nullptr) return first + it;
+        const int base = it & ~63;
+        if (base != chunk_base) {
+            chunk_base = base;
+            chunk = base + lane < cnt ? list[base + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(chunk, it & 63);
+    };
+    // the step after st (st.gi < 0: before the first); gi == G: none left
+    constexpr int PARTS = kBlock / C::BM;
+    auto advance = [&](Step st) {
+        if (st.gi < 0) {
+            st.gi = 0;
+            head_list(0);
+            st.it = 0;
+            st.half = -1;
+        }
+        for (;;) {
+            if (++st.half >= PARTS) {
+                st.half = 0;
+                ++st.it;
+            }
+            while (st.it >= cnt) {                  // the head's list is done
+                if (++st.gi >= a.G) return st;
+                head_list(st.gi);
+                st.it = 0;
+                st.half = 0;
+            }
+            const int qb = qb_at(st.it);
+            if (qb < 0 || qb >= a.n_qb) {           // ignore malformed CSR entries
+                st.half = PARTS - 1;
+                continue;
+            }
+            st.m0 = qb * kBlock + st.half * C::BM;
+            if (st.m0 >= a.Sq) {                    // the block's remaining rows are past Sq
+                st.half = PARTS - 1;
+                continue;
+            }
+            const int mlast = min(st.m0 + C::BM - 1, a.Sq - 1);
+            if (a.causal && mlast + shift < n_base) continue;  // every row of the step precedes the tile
+            return st;
+        }
+    };
+    TileStager<DQK, DQK, C::BM, C::NT, true> tq;
+    TileStager<DV, DV, C::BM, C::NT, true> tdo;
+    float nl = __builtin_inff(), nd = 0.f;
+    auto issue = [&](const Step& st) {              // loads of step st into registers
+        const int h = hk * a.G + st.gi;
+        tq.load(a.q + b * a.q_sb + h * a.q_sh, a.q_ss, st.m0, a.Sq, tid);
+        tdo.load(a.dO + b * a.do_sb + h * a.do_sh, a.do_ss, st.m0, a.Sq, tid);
+        if (tid < C::BM) {
+            const int64_t srow = (int64_t(b) * a.Hq + h) * a.Sq;
+            const int row = st.m0 + tid;
+            nl = row < a.Sq ? a.lse[srow + row] * kLog2e : __builtin_inff();
+            nd = row < a.Sq ? a.delta[srow + row] : 0.f;
+        }
+    };
+
+    Step cur = advance(Step{-1, 0, 0, 0});
+    if (cur.gi < a.G) issue(cur);
+    while (cur.gi < a.G) {
+        const int m0 = cur.m0;
+        const int h = hk * a.G + cur.gi;
         float* gdq = a.acc0 + (int64_t(b) * a.Hq + h) * a.Sq * DQK;   // head-major [B, Hq, Sq, Dqk]
-
-        for (int it = 0; it < qb_count; ++it) {
-            const int qb = qb_list ? qb_list[it] : qb_first + it;
-            if (qb < 0 || qb >= a.n_qb) continue;   // ignore malformed CSR entries
-#pragma unroll 1
-            for (int half = 0; half < kBlock / C::BM; ++half) {
-                const int m0 = qb * kBlock + half * C::BM;
-                if (m0 >= a.Sq) break;
-                const int mlast = min(m0 + C::BM - 1, a.Sq - 1);
-                if (a.causal && mlast + shift < n_base) continue;  // every row of the step precedes the tile
-                stage_both<DQK, C::PQ, C::PQT, C::BM, C::NT>(sQ, sQt, gq, a.q_ss, m0, a.Sq, tid);
-                stage_both<DV, C::PDO, C::PDOT, C::BM, C::NT>(sdO, sdOt, gdo, a.do_ss, m0, a.Sq, tid);
-                if (tid < C::BM) {
-                    const int row = m0 + tid;
-                    sL[tid] = row < a.Sq ? a.lse[srow + row] * kLog2e : __builtin_inff();
-                    sD[tid] = row < a.Sq ? a.delta[srow + row] : 0.f;
-                }
-                __syncthreads();
-
+        tq.store_swz(sQ, tid);
+        tdo.store_swz(sdO, tid);
+        if (tid < C::BM) {
+            sL[tid] = nl;
+            sD[tid] = nd;
+        }
+        __syncthreads();
+        const Step nxt = advance(cur);
+        if (nxt.gi < a.G) issue(nxt);
+        {
                 f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
                 f32x16_t dp[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
                 for (int c = 0; c < C::NCQ; ++c) {
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) {
-                        const bf16x8_t qa = as_bf16x8(lds_read128(sQ + (32 * mt + l32) * C::PQ + 16 * c + 8 * h2));
+                        const bf16x8_t qa = as_bf16x8(lds_read128(sQ + 32 * mt * DQK + swz_off<DQK>(l32, 16 * c + 8 * h2)));
                         s[mt] = mfma32(qa, kS[c], s[mt]);
                     }
                 }
@@ -201,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
                 for (int c = 0; c < C::NCV; ++c) {
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) {
-                        const bf16x8_t oa = as_bf16x8(lds_read128(sdO + (32 * mt + l32) * C::PDO + 16 * c + 8 * h2));
+                        const bf16x8_t oa = as_bf16x8(lds_read128(sdO + 32 * mt * DV + swz_off<DV>(l32, 16 * c + 8 * h2)));
                         dp[mt] = mfma32(oa, vS[c], dp[mt]);
                     }
                 }
@@ -211,7 +271,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
                 for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int ml = 32 * mt + 8 * (i >> 2) + 4 * h2 + (i & 3);
+                        // LDS row 32 mt + 8 (i / 4) + 4 h2 + i % 4 holds logical row swap23 of it
+                        const int ml = 32 * mt + swap23(8 * (i >> 2) + 4 * h2 + (i & 3));
                         float p = fast_exp2(s[mt][i] * a.scale_log2 - sL[ml]);
                         if (need_mask) {
                             const bool ok = key_in && (!a.causal || key <= m0 + ml + shift);
@@ -235,20 +296,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
                             pp[j] = pack_bf16x2(s[mt][8 * c + 2 * j], s[mt][8 * c + 2 * j + 1]);
                             pd[j] = pack_bf16x2(dp[mt][8 * c + 2 * j], dp[mt][8 * c + 2 * j + 1]);
                         }
-                        const int moff = 32 * mt + 16 * c + 4 * h2;
+                        // k = logical rows 32 mt + 16 c + 8 h2 + 0..7: the partner
+                        // columns by transposing reads of the swizzled tiles
+                        const int roff = 32 * mt + 16 * c;
 #pragma unroll
                         for (int dt = 0; dt < C::NDV; ++dt) {
-                            const uint16_t* src = sdOt + (32 * dt + l32) * C::PDOT + moff;
-                            const u32x2_t lo = lds_read64(src);
-                            const u32x2_t hi = lds_read64(src + 8);
+                            const u32x2_t lo = lds_read_tr16(sdO + roff * DV + tr_read_off<DV>(lane, dt, 0) / 2);
+                            const u32x2_t hi = lds_read_tr16(sdO + roff * DV + tr_read_off<DV>(lane, dt, 1) / 2);
                             const u32x4_t bv = {lo[0], lo[1], hi[0], hi[1]};
                             dv[dt] = mfma32(as_bf16x8(pp), as_bf16x8(bv), dv[dt]);
                         }
 #pragma unroll
                         for (int dt = 0; dt < C::NDK; ++dt) {
-                            const uint16_t* src = sQt + (32 * dt + l32) * C::PQT + moff;
-                            const u32x2_t lo = lds_read64(src);
-                            const u32x2_t hi = lds_read64(src + 8);
+                            const u32x2_t lo = lds_read_tr16(sQ + roff * DQK + tr_read_off<DQK>(lane, dt, 0) / 2);
+                            const u32x2_t hi = lds_read_tr16(sQ + roff * DQK + tr_read_off<DQK>(lane, dt, 1) / 2);
                             const u32x4_t bq = {lo[0], lo[1], hi[0], hi[1]};
                             dk[dt] = mfma32(as_bf16x8(pd), as_bf16x8(bq), dk[dt]);
                         }
@@ -277,8 +338,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
                     }
                 }
                 __syncthreads();
-            }
         }
+        cur = nxt;
     }
 
     // ---- epilogue: dK = scale * acc, dV = acc -> bf16, stored directly
