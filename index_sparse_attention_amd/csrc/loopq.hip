@@ -218,7 +218,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
     };
     TileStager<DQK, DQK, C::BM, C::NT, true> tq;
     TileStager<DV, DV, C::BM, C::NT, true> tdo;
-    float nl = __builtin_inff(), nd = 0.f;
+    // raw statistics of the next step's row tid; scaled and masked when staged,
+    // so nothing waits on these loads before the step's work is issued
+    float nl = 0.f, nd = 0.f;
+    bool nin = false;
     auto issue = [&](const Step& st) {              // loads of step st into registers
         const int h = hk * a.G + st.gi;
         tq.load(a.q + b * a.q_sb + h * a.q_sh, a.q_ss, st.m0, a.Sq, tid);
@@ -226,8 +229,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
         if (tid < C::BM) {
             const int64_t srow = (int64_t(b) * a.Hq + h) * a.Sq;
             const int row = st.m0 + tid;
-            nl = row < a.Sq ? a.lse[srow + row] * kLog2e : __builtin_inff();
-            nd = row < a.Sq ? a.delta[srow + row] : 0.f;
+            nin = row < a.Sq;
+            if (nin) {
+                nl = a.lse[srow + row];
+                nd = a.delta[srow + row];
+            }
         }
     };
 
@@ -240,8 +246,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_loopq(BwdArgs a) {
         tq.store_swz(sQ, tid);
         tdo.store_swz(sdO, tid);
         if (tid < C::BM) {
-            sL[tid] = nl;
-            sD[tid] = nd;
+            sL[tid] = nin ? nl * kLog2e : __builtin_inff();
+            sD[tid] = nin ? nd : 0.f;
         }
         __syncthreads();
         const Step nxt = advance(cur);
