@@ -286,19 +286,19 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
     return __popc(x & 0x01010101u);
 }
 
-// Exclusive scan over the kCsrThreads threads of a workgroup (one value
-// each); *total gets the sum.  wsum holds kCsrThreads / 64 ints.
-__device__ int csr_block_scan(int v, int* wsum, int* total) {
+// Exclusive scan over the kCsrThreads threads of a workgroup (one 64-bit
+// value each); *total gets the sum.  wsum holds kCsrThreads / 64 values.
+__device__ int64_t csr_block_scan(int64_t v, int64_t* wsum, int64_t* total) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    int x = v;
+    int64_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
+        const int64_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
     if (lane == 63) wsum[wid] = x;
     __syncthreads();
-    int pre = x - v, tot = 0;
+    int64_t pre = x - v, tot = 0;
 #pragma unroll
     for (int w = 0; w < kCsrThreads / 64; ++w) {
         pre += w < wid ? wsum[w] : 0;
@@ -313,7 +313,7 @@ __device__ int csr_block_scan(int v, int* wsum, int* total) {
 // (n_qb, n_kb <= kCsrSideMax, n_qb * n_kb <= kCsrSliceBytes): counts the
 // kept blocks of the slices before it (its offset in both CSRs), stages its
 // slice in LDS, counts rows (ballot per wave) and columns (LDS atomics),
-// scans both, writes its row_ptr entries and fills both column lists in
+// scans the three counts packed in one 64-bit value, writes its row_ptr entries and fills both column lists in
 // ascending order.
 __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __restrict__ presence, int32_t n_qb,
                                                            int32_t n_kb, int32_t* __restrict__ q2k_ptr,
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __rest
     __shared__ __attribute__((aligned(16))) uint8_t pres[kCsrSliceBytes];
     __shared__ int rcnt[kCsrSideMax];
     __shared__ int ccnt[kCsrSideMax];
-    __shared__ int wsum[kCsrThreads / 64];
+    __shared__ int64_t wsum[kCsrThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     constexpr int NW = kCsrThreads / 64;
     const uint64_t below = (uint64_t(1) << lane) - 1;
@@ -333,7 +333,10 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __rest
     const uint8_t* slice = presence + before;
     const bool vec = (reinterpret_cast<uintptr_t>(presence) & 15) == 0 && (S & 15) == 0;
 
-    // offset: kept blocks of the slices before this one
+    // the slice's own bytes requested first (at most one 16-byte piece per
+    // thread), then the offset: kept blocks of the slices before this one
+    u32x4_t own = {0u, 0u, 0u, 0u};
+    if (vec && tid < S / 16) own = reinterpret_cast<const u32x4_t*>(slice)[tid];
     int c = 0;
     if (vec) {
         // eight 16-byte loads in flight per thread (the latest slice reads up to
@@ -351,19 +354,13 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __rest
             for (int j = 0; j < 8; ++j)
                 c += nonzero_bytes(w[j][0]) + nonzero_bytes(w[j][1]) + nonzero_bytes(w[j][2]) + nonzero_bytes(w[j][3]);
         }
+        if (tid < S / 16) reinterpret_cast<u32x4_t*>(pres)[tid] = own;
     } else {
         for (int64_t i = tid; i < before; i += kCsrThreads) c += presence[i] != 0;
-    }
-    // the slice into LDS; column counts cleared
-    if (vec) {
-        for (int i = tid; i < S / 16; i += kCsrThreads)
-            reinterpret_cast<u32x4_t*>(pres)[i] = reinterpret_cast<const u32x4_t*>(slice)[i];
-    } else {
         for (int i = tid; i < S; i += kCsrThreads) pres[i] = slice[i];
     }
     for (int i = tid; i < n_kb; i += kCsrThreads) ccnt[i] = 0;
-    int off = 0;
-    csr_block_scan(c, wsum, &off);                 // (the scan's barriers also publish pres and ccnt)
+    __syncthreads();
 
     // row counts (one wave per row) and column counts
     for (int r = wid; r < n_qb; r += NW) {
@@ -377,11 +374,15 @@ __global__ __launch_bounds__(kCsrThreads) void k_csr_small(const uint8_t* __rest
         if (lane == 0) rcnt[r] = n;
     }
     __syncthreads();
+    // one scan for all three: row counts (bits 0-15), column counts (bits
+    // 16-31; both at most 16384 in all) and the offset count (bits 32-; only
+    // its total is used)
     const int rc = tid < n_qb ? rcnt[tid] : 0;
     const int cc = tid < n_kb ? ccnt[tid] : 0;
-    int rtot = 0, ctot = 0;
-    const int rx = csr_block_scan(rc, wsum, &rtot);
-    const int cx = csr_block_scan(cc, wsum, &ctot);
+    int64_t tot = 0;
+    const int64_t x = csr_block_scan((int64_t(c) << 32) | (int64_t(cc) << 16) | int64_t(rc), wsum, &tot);
+    const int off = int(tot >> 32);
+    const int rx = int(x & 0xffff), cx = int((x >> 16) & 0xffff);
     if (tid < n_qb) {
         rcnt[tid] = off + rx;                      // start of row tid's list
         q2k_ptr[int64_t(bh) * n_qb + tid + 1] = off + rx + rc;
