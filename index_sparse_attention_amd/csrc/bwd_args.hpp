@@ -24,7 +24,7 @@ struct BwdArgs {
     uint16_t* dk; int64_t dk_sb, dk_ss, dk_sh;
     uint16_t* dv; int64_t dv_sb, dv_ss, dv_sh;
     const float* lse;     // [B, Hq, lse_ld] natural-log LSE
-    float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O)
+    float* delta;         // [B, Hq, stat_ld] workspace: rowsum(dO * O); SPLIT / SPLIT_DS store its negation
     float* lse2;          // [B, Hq, stat_ld] workspace (SPLIT only): lse * log2(e); else null
     int32_t* order;       // SPLIT work order: B*Hk*n_kb dK/dV items, then B*Hq*n_qb dQ items; else null
     // SPLIT part mode (kv_parts_T > 0): target blocks per part, the units

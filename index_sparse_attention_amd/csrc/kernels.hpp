@@ -20,7 +20,7 @@ hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
 // Set-up of the two-pass backward, before either pass: the work order of
 // both (into a.order); for SPLIT_DS with a block CSR the K->Q position of
 // every Q->K entry (a.ds_map) and the overflow flag; with `delta` the delta
-// and lse2 rows.  One launch.
+// rows (negated, as the dK/dV pass reads them) and the lse2 rows.  One launch.
 hipError_t launch_split_setup(const BwdArgs& a, bool delta, hipStream_t s);
 hipError_t launch_split_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_split_dq(const BwdArgs& a, hipStream_t s);

@@ -10,7 +10,8 @@ namespace isattn {
 
 // Delta rows: delta[b, h, i] = sum over d of dO[b,i,h,d] * O[b,i,h,d], the
 // fp32 sum of exact bf16 products (it equals the row sum of P * dP, the
-// term dS = P (dP - delta) subtracts), and where a.lse2 is set also
+// term dS = P (dP - delta) subtracts; with NEG the row gets -delta, the value
+// the two-pass dK/dV kernel starts its dP accumulators at), and where a.lse2 is set also
 // lse2 = lse * log2(e); rows past a sequence's length get delta 0 and
 // lse2 = +inf.  Rows are taken in (b, i, h) order, h fastest: the token-major
 // memory order of O and dO, so a block reads whole token rows; they are
@@ -20,7 +21,7 @@ namespace isattn {
 // (and their lse) before any arithmetic.
 constexpr int kPreRows = 4;
 
-template <int DV, int NT>
+template <int DV, int NT, bool NEG = false>
 __device__ __forceinline__ void delta_rows(const BwdArgs& a, int64_t blk) {
     constexpr int L = DV / 8;
     constexpr int RPB = NT / L;        // rows per pass
@@ -75,7 +76,7 @@ __device__ __forceinline__ void delta_rows(const BwdArgs& a, int64_t blk) {
 #pragma unroll
         for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
         if (row[r] < rows && sub == 0) {
-            a.delta[stat[r]] = acc;
+            a.delta[stat[r]] = NEG ? -acc : acc;
             if (a.lse2 != nullptr) a.lse2[stat[r]] = l2[r];
         }
     }

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kSchedThreads) void k_split_setup(BwdArgs a, int32_
     } else if (blk < n_sched + n_map) {
         ds_map_rows<kSchedThreads>(a, blk - n_sched);
     } else if constexpr (DV > 0) {
-        delta_rows<DV, kSchedThreads>(a, blk - n_sched - n_map);
+        delta_rows<DV, kSchedThreads, true>(a, blk - n_sched - n_map);
     }
 }
 
@@ -355,8 +355,8 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
     // rows' statistics, computed here and stored for the dK/dV pass (which
     // runs after this one): delta = rowsum(dO * O) over the lane's half of the
     // O row at the same positions as its dO operands plus the partner lane's
-    // half, and lse2 = lse * log2(e).  Padding rows past Sq get lse2 = +inf
-    // (P = 0) and delta = 0.
+    // half (stored as -delta), and lse2 = lse * log2(e).  Padding rows past
+    // Sq get lse2 = +inf (P = 0) and delta = 0.
     const int wrow = w * WR;
     bf16x8_t qB[C::QT][C::NCQ], doB[C::QT][C::NCV];
     float lse2[C::QT], dlt[C::QT];
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * (128 / WR), DQK > 128 ? 1 : 2) void k_bwd_dq(B
         if (h2 == 0) {
             const int64_t si = (int64_t(b) * a.Hq + h) * a.stat_ld + qrow;
             a.lse2[si] = lse2[qt];
-            a.delta[si] = dlt[qt];
+            a.delta[si] = -dlt[qt];             // negated: the dK/dV pass starts dP there
         }
     }
 
@@ -666,7 +666,7 @@ struct DkvCfg {
     static constexpr int NS = 3;                            // LDS ring stages (loads run one step ahead)
     static constexpr int Q_BYTES = BM * DQK * 2;
     static constexpr int O_BYTES = BM * DV * 2;
-    static constexpr int ST_BYTES = 2 * BM * 4;             // float lse2[64], delta[64]
+    static constexpr int ST_BYTES = 2 * BM * 4;             // float lse2[64], -delta[64]
     static constexpr int XBUF_BYTES = NR * NH * 2 * 1024;   // P of all P waves for one step, (wave, half, cc)
     // LDS regions: the NS Q tiles, the NS dO tiles, the NS statistics slots,
     // two P buffers
@@ -1268,16 +1268,26 @@ struct DkvSWave {
         return as_bf16x8(v);
     }
 
-    // dS pair (cc, jj): packed bf16 of P * (dP - delta)
-    __device__ uint32_t ds_pair(const f32x16_t& dpt, const f32x4_t (&d4)[4], uint32_t pw, int cc, int jj) const {
+    // Initial dP accumulators of a half: the rows' -delta (the statistics
+    // slot holds the negated value, four rows per 16-byte read in accumulator
+    // order), so the MFMAs leave dP - delta and dS needs one multiply.
+    static __device__ f32x16_t neg_delta(const f32x4_t (&d4)[4]) {
+        f32x16_t r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const f32x4_t v = d4[i >> 2];
+            r[i] = (i & 3) == 0 ? v.x : (i & 3) == 1 ? v.y : (i & 3) == 2 ? v.z : v.w;
+        }
+        return r;
+    }
+    // dS pair (cc, jj): packed bf16 of P * (dP - delta), dpt holding dP - delta
+    __device__ uint32_t ds_pair(const f32x16_t& dpt, uint32_t pw, int cc, int jj) const {
         float r[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int i = 8 * cc + 2 * jj + e;
-            const f32x4_t dv4 = d4[i >> 2];
-            const float dl = (i & 3) == 0 ? dv4.x : (i & 3) == 1 ? dv4.y : (i & 3) == 2 ? dv4.z : dv4.w;
             const float p = e == 0 ? bf16_lo(pw) : bf16_hi(pw);
-            r[e] = p * (dpt[i] - dl);
+            r[e] = p * dpt[i];
         }
         return pack_bf16x2(r[0], r[1]);
     }
@@ -1306,14 +1316,14 @@ struct DkvSWave {
             for (int cc = 0; cc < 2; ++cc) pw[hh][cc] = lds_ld128(x_at + (hh * 2 + cc) * 1024);
         };
         auto ds_q = [&](int hh, int q) {
-            sa[hh][q >> 2][q & 3] = ds_pair(dp[hh], d4[hh], pw[hh][q >> 2][q & 3], q >> 2, q & 3);
+            sa[hh][q >> 2][q & 3] = ds_pair(dp[hh], pw[hh][q >> 2][q & 3], q >> 2, q & 3);
         };
         bf16x8_t oa[PFO];
         // dP(0)
 #pragma unroll
         for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = o_row(0, c);
         load_stats(0);
-        dp[0] = f32x16_t{};
+        dp[0] = neg_delta(d4[0]);
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
             dp[0] = mfma32(oa[c % PFO], vB[c], dp[0]);
@@ -1324,7 +1334,7 @@ struct DkvSWave {
 #pragma unroll
         for (int c = 0; c < PFO && c < C::NCV; ++c) oa[c] = o_row(1, c);
         load_stats(1);
-        dp[1] = f32x16_t{};
+        dp[1] = neg_delta(d4[1]);
 #pragma unroll
         for (int c = 0; c < C::NCV; ++c) {
             dp[1] = mfma32(oa[c % PFO], vB[c], dp[1]);
@@ -1379,7 +1389,7 @@ struct DkvSWave {
             for (int cc = 0; cc < 2; ++cc) pw[cc] = lds_ld128(x_at + (hh * 2 + cc) * 1024);
             constexpr int NQF = 2 * C::NDK;        // Q^T fragments (cc, j)
             bf16x8_t qf[NQF];
-            f32x16_t dp = f32x16_t{};
+            f32x16_t dp = neg_delta(d4);
 #pragma unroll
             for (int c = 0; c < C::NCV; ++c) {
                 dp = mfma32(oa[c % PFO], vB[c], dp);
@@ -1390,7 +1400,7 @@ struct DkvSWave {
             }
             u32x4_t sa[2];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, d4, pw[q >> 2][q & 3], q >> 2, q & 3);
+            for (int q = 0; q < 8; ++q) sa[q >> 2][q & 3] = ds_pair(dp, pw[q >> 2][q & 3], q >> 2, q & 3);
             store_ds(hh, sa);
 #pragma unroll
             for (int f = 0; f < NQF; ++f) dk[f % C::NDK] = mfma32(as_bf16x8(sa[f / C::NDK]), qf[f], dk[f % C::NDK]);
