@@ -99,12 +99,13 @@ def test_index_converter_full_workload():
     assert int(got[0][-1]) == 2 * 128 * 129 // 2      # the full lower block triangle per KV head
 
 
-# up to (1, 1, 16, 1024) the shapes fit the single-launch path (slices of at
-# most 1024 x 1024 and 16 KiB, 256 KiB in all, the first two at its row and
-# column limits); the rest take the count / scan / fill launches
-@pytest.mark.parametrize("shape", [(2, 16, 64, 64), (1, 3, 5, 9), (3, 1, 70, 1), (1, 2, 1, 130), (1, 4, 128, 128),
-                                   (4, 16, 64, 64), (2, 3, 100, 77), (1, 1, 129, 2), (1, 1, 1024, 16),
-                                   (1, 1, 16, 1024),
+# up to (1, 1, 4, 1024) the shapes fit the single-launch path (slices of at
+# most 1024 x 1024 and 4 KiB, 256 KiB in all; (4, 16, 64, 64) at the total
+# and the last two at the row and column limits); the rest take the count /
+# scan / fill launches
+@pytest.mark.parametrize("shape", [(2, 16, 64, 64), (1, 3, 5, 9), (3, 1, 70, 1), (1, 2, 1, 130), (1, 1, 129, 2),
+                                   (4, 16, 64, 64), (1, 1, 1024, 4), (1, 1, 4, 1024),
+                                   (1, 4, 128, 128), (2, 3, 100, 77), (1, 1, 1024, 16), (1, 1, 16, 1024),
                                    (8, 16, 64, 64), (1, 1, 2000, 3), (1, 1, 3, 2000), (1, 2, 128, 200)])
 def test_block_mask_to_csr(shape):
     import index_sparse_attention_amd as isa
